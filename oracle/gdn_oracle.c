@@ -1,0 +1,284 @@
+/*
+ * gdn_oracle.c -- plain, slow, fp64 CPU oracle for draft-tree verification
+ * through Gated DeltaNet (GDN) layers.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the HIP library; the two meet only in the seeded input
+ * generator, which holds none of the method's arithmetic.
+ *
+ * What it computes (page "Trees from Marginals: Autoregressive drafting with
+ * factorized priors", section 3 "rollback-free tree verification for GDN",
+ * state-update equation of the "challenge" item): every tree node's state is
+ * the state reached by running the gated delta rule sequentially along that
+ * node's own root-to-node path, starting from the prefix state S0.  We store S
+ * as d_v x d_k (row r = value coordinate, column c = key coordinate); the
+ * page's d_k x d_v form  S_t = a_t (I - b_t k k^T) S_{t-1} + b_t k v^T  is its
+ * exact transpose, with a_t the gate g:
+ *
+ *     S <- g * S * (I - beta k k^T) + beta v k^T ,     o_i = S_i q_i .
+ *
+ * The decay multiplies the whole transition but not the new write, and the
+ * output of node i is read from the state after node i's own update.
+ *
+ * Tree conventions (same section, "the tree is topologically sorted" item):
+ * parent[i] = -1 means node i follows the prefix state S0 directly, otherwise
+ * parent[i] must lie in [0, i).  The first node violating this makes the whole
+ * tree invalid: status = i + 1, outputs NaN, nothing committed.
+ *
+ * Deferred commit (same section, "state commitment is deferred" item): the
+ * state to commit is the state of the accepted node, or S0 when the accepted
+ * index is -1 (nothing accepted); path lists the accepted node's root-to-node
+ * path, root first.  An accepted index outside [-1, N) gives path_len = -1 and
+ * S0 as the committed state.
+ *
+ * Auxiliary outputs, also straight from the recurrence:
+ *   u_i = beta_i (v_i - g_i S_{parent(i)} k_i)   the rank-one write of node i's
+ *         step, i.e. S_i = g_i S_{parent(i)} + u_i k_i^T;
+ *   log_gamma_i = sum of ln g_j over node i's root-to-node path (inclusive).
+ *
+ * Evaluation order is fixed: w = S k with the sum over c ascending, then
+ * S[r][c] = g * (S[r][c] - beta * w[r] * k[c]) + beta * v[r] * k[c].
+ * Build with -ffp-contract=off so every machine rounds the same way.
+ *
+ * Two modes give bit-identical results: mode 0 walks each node's whole path
+ * from S0; mode 1 (memo) applies the same single step to the stored parent
+ * state, which is the same sequence of fp64 operations.
+ *
+ * Parity pins: the single step against a gradient step of the online
+ * regression loss (autograd), closed forms (beta = 0 pure decay; beta = 1 with
+ * q = k of unit norm returns v), a chain against the product form of the
+ * linear recurrence, ancestor masks against a boolean transitive closure,
+ * whole trees against a dense linear solve, and tree invariants (siblings,
+ * non-ancestors, relabelling).  See the tests that load this library.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ trees */
+
+/* Validate one tree and return 0, or i+1 for the first node with a bad parent. */
+static int tree_check(int n, const int32_t* par)
+{
+    for (int i = 0; i < n; ++i)
+        if (par[i] < -1 || par[i] >= i) return i + 1;
+    return 0;
+}
+
+/* Root-to-node path of node i (root first) into out; returns its length. */
+static int tree_path(const int32_t* par, int i, int32_t* out)
+{
+    int len = 0;
+    for (int j = i; j >= 0; j = par[j]) out[len++] = j;
+    for (int a = 0, b = len - 1; a < b; ++a, --b) {
+        int32_t t = out[a]; out[a] = out[b]; out[b] = t;
+    }
+    return len;
+}
+
+/*
+ * Per sequence b: status[b], depth[b][i] (= path length - 1, so a node under
+ * the prefix has depth 0) and strict-ancestor bit rows
+ * mask[b][i][w] (bit j%32 of word j/32 set <=> j is a strict ancestor of i;
+ * unused high bits zero).  Rows of an invalid tree are left zero, depth -1.
+ */
+int oracle_tree(int B, int N, const int32_t* parent, uint32_t* mask,
+                int32_t* depth, int32_t* status)
+{
+    if (B < 0 || N < 1) return -1;
+    const int W = (N + 31) / 32;
+    int32_t* path = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+    if (!path) return -2;
+    for (int b = 0; b < B; ++b) {
+        const int32_t* par = parent + (size_t)b * N;
+        uint32_t* mb = mask + (size_t)b * N * W;
+        memset(mb, 0, sizeof(uint32_t) * (size_t)N * W);
+        status[b] = tree_check(N, par);
+        for (int i = 0; i < N; ++i) {
+            if (status[b]) { depth[(size_t)b * N + i] = -1; continue; }
+            int len = tree_path(par, i, path);
+            depth[(size_t)b * N + i] = len - 1;
+            for (int m = 0; m + 1 < len; ++m)
+                mb[(size_t)i * W + path[m] / 32] |= 1u << (path[m] % 32);
+        }
+    }
+    free(path);
+    return 0;
+}
+
+/* ------------------------------------------------------------ recurrence */
+
+/* One gated delta step on S (dv x dk, row-major), in the fixed order above. */
+static void gdn_step(int dv, int dk, double* S, const double* k, const double* v,
+                     double beta, double g, double* w)
+{
+    for (int r = 0; r < dv; ++r) {
+        double acc = 0.0;
+        for (int c = 0; c < dk; ++c) acc += S[(size_t)r * dk + c] * k[c];
+        w[r] = acc;
+    }
+    for (int r = 0; r < dv; ++r) {
+        for (int c = 0; c < dk; ++c) {
+            double s = S[(size_t)r * dk + c];
+            S[(size_t)r * dk + c] = g * (s - beta * w[r] * k[c]) + beta * v[r] * k[c];
+        }
+    }
+}
+
+/* o = S q, sum over c ascending. */
+static void state_times(int dv, int dk, const double* S, const double* q, double* o)
+{
+    for (int r = 0; r < dv; ++r) {
+        double acc = 0.0;
+        for (int c = 0; c < dk; ++c) acc += S[(size_t)r * dk + c] * q[c];
+        o[r] = acc;
+    }
+}
+
+typedef struct {
+    int B, N, Hk, Hv, dk, dv;
+    const double *S0, *q, *k, *v, *beta, *g;
+    const int32_t *parent, *accepted;
+} problem;
+
+/* index helpers for the documented layouts */
+static size_t ix_qk(const problem* P, int b, int i, int h) /* [B][N][Hk][dk] */
+{ return (((size_t)b * P->N + i) * P->Hk + h) * P->dk; }
+static size_t ix_v(const problem* P, int b, int i, int h)  /* [B][N][Hv][dv] */
+{ return (((size_t)b * P->N + i) * P->Hv + h) * P->dv; }
+static size_t ix_bg(const problem* P, int b, int i, int h) /* [B][N][Hv] */
+{ return ((size_t)b * P->N + i) * P->Hv + h; }
+static size_t ix_S(const problem* P, int b, int h)          /* [B][Hv][dv][dk] */
+{ return ((size_t)b * P->Hv + h) * (size_t)P->dv * P->dk; }
+static size_t ix_u(const problem* P, int b, int h, int i)   /* [B][Hv][N][dv] */
+{ return (((size_t)b * P->Hv + h) * P->N + i) * P->dv; }
+
+/*
+ * One (sequence b, value head h) unit.  Value head h reads key head
+ * h / (Hv / Hk).  Writes o, u, log_gamma and the committed state.
+ */
+static void run_unit(const problem* P, int b, int h, int memo, int status,
+                     double* o, double* u, double* lg, double* S_commit)
+{
+    const int N = P->N, dv = P->dv, dk = P->dk;
+    const int hk = h / (P->Hv / P->Hk);
+    const size_t SS = (size_t)dv * dk;
+    const int32_t* par = P->parent + (size_t)b * N;
+    const double* S0 = P->S0 + ix_S(P, b, h);
+    const int acc = P->accepted[b];
+    double* Sc = S_commit + ix_S(P, b, h);
+
+    memcpy(Sc, S0, sizeof(double) * SS);   /* default commit: nothing accepted */
+    if (status) {
+        for (int i = 0; i < N; ++i) {
+            for (int r = 0; r < dv; ++r) o[ix_v(P, b, i, h) + r] = NAN;
+            for (int r = 0; r < dv; ++r) u[ix_u(P, b, h, i) + r] = NAN;
+            lg[((size_t)b * P->Hv + h) * N + i] = NAN;
+        }
+        return;
+    }
+
+    double* w = (double*)malloc(sizeof(double) * (size_t)dv);
+    int32_t* path = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+    /* memo keeps every node's state; the path walk keeps one working state */
+    double* S = (double*)malloc(sizeof(double) * SS * (memo ? (size_t)N : 1));
+
+    for (int i = 0; i < N; ++i) {
+        double* Si = memo ? S + (size_t)i * SS : S;
+        const double* kb = P->k + ix_qk(P, b, i, hk);
+        const double* vb = P->v + ix_v(P, b, i, h);
+        const double bi = P->beta[ix_bg(P, b, i, h)];
+        const double gi = P->g[ix_bg(P, b, i, h)];
+        double lgi;
+        if (memo) {
+            const double* Sp = par[i] < 0 ? S0 : S + (size_t)par[i] * SS;
+            memcpy(Si, Sp, sizeof(double) * SS);
+            lgi = (par[i] < 0 ? 0.0 : lg[((size_t)b * P->Hv + h) * N + par[i]]) + log(gi);
+        } else {
+            int len = tree_path(par, i, path);
+            memcpy(Si, S0, sizeof(double) * SS);
+            lgi = 0.0;
+            for (int m = 0; m + 1 < len; ++m) {
+                int j = path[m];
+                gdn_step(dv, dk, Si, P->k + ix_qk(P, b, j, hk), P->v + ix_v(P, b, j, h),
+                         P->beta[ix_bg(P, b, j, h)], P->g[ix_bg(P, b, j, h)], w);
+                lgi += log(P->g[ix_bg(P, b, j, h)]);
+            }
+            lgi += log(gi);
+        }
+        /* Si now holds the parent's state: record the write vector u_i. */
+        state_times(dv, dk, Si, kb, w);
+        for (int r = 0; r < dv; ++r)
+            u[ix_u(P, b, h, i) + r] = bi * (vb[r] - gi * w[r]);
+        gdn_step(dv, dk, Si, kb, vb, bi, gi, w);
+        lg[((size_t)b * P->Hv + h) * N + i] = lgi;
+        state_times(dv, dk, Si, P->q + ix_qk(P, b, i, hk), o + ix_v(P, b, i, h));
+        if (i == acc) memcpy(Sc, Si, sizeof(double) * SS);
+    }
+    free(S);
+    free(path);
+    free(w);
+}
+
+/*
+ * Verify every node of every tree and produce the state to commit.
+ *
+ * Inputs (float64, the exact values the GPU library reads, widened):
+ *   S0 [B][Hv][dv][dk], q, k [B][N][Hk][dk], v [B][N][Hv][dv],
+ *   beta, g [B][N][Hv], parent [B][N], accepted [B].
+ * Outputs: o [B][N][Hv][dv], u [B][Hv][N][dv], log_gamma [B][Hv][N],
+ *   S_commit [B][Hv][dv][dk], path [B][N] (root first, -1 padded),
+ *   path_len [B], status [B].
+ * memo: 0 = walk every path from S0, 1 = reuse the parent's stored state.
+ * nthreads: OpenMP threads over (b, h) units, 0 = runtime default.
+ * Returns 0, or a negative value for bad sizes / allocation failure.
+ */
+int oracle_verify(int B, int N, int Hk, int Hv, int dk, int dv,
+                  const double* S0, const double* q, const double* k,
+                  const double* v, const double* beta, const double* g,
+                  const int32_t* parent, const int32_t* accepted, int memo,
+                  int nthreads, double* o, double* u, double* log_gamma,
+                  double* S_commit, int32_t* path, int32_t* path_len,
+                  int32_t* status)
+{
+    if (B < 0 || N < 1 || Hk < 1 || Hv < 1 || Hv % Hk || dk < 1 || dv < 1) return -1;
+    problem P = {B, N, Hk, Hv, dk, dv, S0, q, k, v, beta, g, parent, accepted};
+
+    for (int b = 0; b < B; ++b) {
+        const int32_t* par = parent + (size_t)b * N;
+        int32_t* pb = path + (size_t)b * N;
+        for (int i = 0; i < N; ++i) pb[i] = -1;
+        status[b] = tree_check(N, par);
+        const int a = accepted[b];
+        if (status[b] || a < -1 || a >= N) path_len[b] = -1;
+        else if (a == -1) path_len[b] = 0;
+        else path_len[b] = tree_path(par, a, pb);
+    }
+
+    const long units = (long)B * Hv;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (long t = 0; t < units; ++t) {
+        int b = (int)(t / Hv), h = (int)(t % Hv);
+        run_unit(&P, b, h, memo, status[b], o, u, log_gamma, S_commit);
+    }
+    /* an accepted index outside [-1, N) matches no node: run_unit left S0 */
+    return 0;
+}
+
+/* Threads the OpenMP runtime would use (for reporting). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
