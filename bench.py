@@ -1,0 +1,262 @@
+"""Benchmark: tree nodes verified per second per GDN layer on one MI355X.
+
+A step is one decode iteration of the 36-layer stack: for every layer, verify
+all 64 draft trees (128 nodes, M = 8 wide, 16 deep; 16 key / 32 value heads,
+d = 128, bf16 q/k/v, fp32 state) and commit each sequence's accepted node.
+The committed states of step t are the prefix states of step t + 1, as in a
+decode loop.  All inputs are synthetic (workloads.py) and resident in HBM
+before the timed region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.  value = B * N * layers * K / elapsed, i.e. nodes per
+second per layer (each layer call verifies B * N nodes).  The roofline block
+reports the dominant kernel (verification): algorithmic bytes per launch over
+its average launch time, measured here with HIP events on the launch stream.
+The cpu_baseline block times the fp64 oracle (path-walk mode) on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- byte model
+
+def verify_bytes(s, e):
+    """Algorithmic HBM bytes of one verify launch: S0 read once, q/k read once
+    per key head, v read, beta/g/parent read, o written, the cache written
+    (u, Gamma, ancestor rows, depth, status)."""
+    B, N, Hk, Hv, d = s.batch, s.n_nodes, s.h_k, s.h_v, s.d
+    Wd = (N + 31) // 32
+    per_seq = (4 * Hv * d * d + 2 * N * Hk * d * e + N * Hv * d * e + 8 * N * Hv + 4 * N
+               + N * Hv * d * e + 4 * N * Hv * d + 4 * N * Hv + 4 * N * Wd + 4 * N + 4)
+    return B * per_seq
+
+
+def commit_bytes(s, e, path_lens):
+    """Algorithmic bytes of one commit launch: S in + out, and per path node its
+    u row, k row and Gamma, plus the accepted row of the ancestor mask, the
+    path written and the small per-sequence scalars."""
+    Hk, Hv, d, N = s.h_k, s.h_v, s.d, s.n_nodes
+    Wd = (N + 31) // 32
+    tot = 0
+    for P in path_lens:
+        P = max(int(P), 0)
+        tot += (8 * Hv * d * d + P * (4 * Hv * d + Hk * d * e + 4 * Hv) + 4 * Hv
+                + 4 * Wd + 4 * N + 12)
+    return tot
+
+
+# ---------------------------------------------------------------- GPU run
+
+def run_gpu(args, s):
+    import torch
+    import tree_masked_gated_amd as T
+
+    dev = torch.device("cuda:0")
+    e = 2 if s.io == "bf16" else 4
+    parent, accepted = W.make_trees(s)
+    L = s.layers
+    log(f"generating {L} layers of {s.name} on the host")
+    t0 = time.time()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, L)) as ex:
+        futs = [ex.submit(W.make_layer, s, l) for l in range(L)]
+        layers = []
+        for l, f in enumerate(futs):
+            lay = f.result()
+            layers.append({
+                "q": W.to_device(lay["q"], s.io, dev), "k": W.to_device(lay["k"], s.io, dev),
+                "v": W.to_device(lay["v"], s.io, dev),
+                "beta": W.to_device(lay["beta"], device=dev),
+                "g": W.to_device(lay["g"], device=dev),
+                "S": [W.to_device(lay["S0"], device=dev), None],
+            })
+            layers[-1]["S"][1] = torch.empty_like(layers[-1]["S"][0])
+            del lay
+    log(f"generated and uploaded in {time.time() - t0:.1f} s")
+    dims = T.dims(s.batch, s.n_nodes, s.h_k, s.h_v, s.d, s.d, s.io)
+    par = W.to_device(parent, device=dev)
+    acc = W.to_device(accepted, device=dev)
+    caches = [T.TreeCache(dims, dev) for _ in range(L)]
+    o = [torch.empty((s.batch, s.n_nodes, s.h_v, s.d), dtype=layers[0]["q"].dtype,
+                     device=dev) for _ in range(L)]
+    path = torch.empty((s.batch, s.n_nodes), dtype=torch.int32, device=dev)
+    plen = torch.empty((s.batch,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    phase = [0]
+
+    def verify(l):
+        x = layers[l]
+        T.gdn_tree_verify(dims, x["S"][phase[0]], x["q"], x["k"], x["v"], x["beta"], x["g"],
+                          par, o[l], caches[l], sptr)
+
+    def commit(l):
+        x = layers[l]
+        T.gdn_tree_commit(dims, x["S"][phase[0]], x["S"][1 - phase[0]], x["k"], caches[l],
+                          acc, path, plen, sptr)
+
+    def step():
+        for l in range(L):
+            verify(l)
+            commit(l)
+        phase[0] ^= 1
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    log(f"timed {args.steps} steps: {total_ms:.3f} ms")
+
+    # per-kernel averages, same stream, same launch configuration
+    reps = max(1, args.steps)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            for l in range(L):
+                fn(l)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * L)
+
+    verify_ms = timed(verify)
+    commit_ms = timed(commit)
+    log(f"verify {verify_ms * 1e3:.1f} us/launch, commit {commit_ms * 1e3:.1f} us/launch")
+    path_lens = plen.cpu().numpy()
+    return {
+        "total_ms": total_ms, "verify_ms": verify_ms, "commit_ms": commit_ms,
+        "verify_bytes": verify_bytes(s, e), "commit_bytes": commit_bytes(s, e, path_lens),
+        "path_lens": path_lens, "parent": parent, "accepted": accepted,
+    }
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(s, budget_s):
+    """The fp64 oracle, path-walk mode, on the first sequences of layer 0 (all
+    value heads), growing the sample until it took about budget_s seconds."""
+    import oracle
+    lib = oracle.load()
+    parent, accepted = W.make_trees(s)
+    lay = W.make_layer(s, 0)
+    f = lambda a: W.io_to_f64(a, s.io)
+    nb, spent, done_nodes = 1, 0.0, 0
+    t_all = 0.0
+    while True:
+        sl = slice(0, nb)
+        args = (lay["S0"][sl].astype(np.float64), f(lay["q"][sl]), f(lay["k"][sl]),
+                f(lay["v"][sl]), lay["beta"][sl].astype(np.float64),
+                lay["g"][sl].astype(np.float64), parent[sl], accepted[sl])
+        t0 = time.perf_counter()
+        oracle.verify(*args, memo=False, lib=lib)
+        dt = time.perf_counter() - t0
+        t_all += dt
+        if dt >= budget_s / 4 or nb >= s.batch:
+            break
+        nb = min(s.batch, nb * 2)
+    # nodes/s/layer: a full layer has s.batch sequences; the sample had nb
+    value = (nb * s.n_nodes) / dt
+    return {"value": value, "unit": "nodes/s/layer", "cores": oracle.max_threads(lib),
+            "kind": "oracle",
+            "sample": f"layer 0, sequences 0..{nb - 1} (all {s.h_v} value heads, "
+                      f"{nb * s.n_nodes} nodes), fp64 path walk, {dt:.2f} s"}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mary128_b64_l36")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: every (sequence, value head) unit is "
+              "independent, so the path shards across GPUs without exchange; run it "
+              "with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    s = W.spec(args.workload)
+    r = run_gpu(args, s)
+    L = s.layers
+    nodes = s.batch * s.n_nodes
+    value = nodes * L * args.steps / (r["total_ms"] * 1e-3)
+    vb = r["verify_bytes"]
+    achieved = vb / (r["verify_ms"] * 1e-3) / 1e9
+    base = None
+    if args.cpu_budget > 0:
+        log("timing the oracle on the host")
+        base = cpu_baseline(s, args.cpu_budget)
+
+    out = {
+        "metric": "tree nodes verified/sec per GDN layer",
+        "value": value,
+        "unit": "nodes/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["total_ms"] / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-io/f32-state" if s.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": s.name, "batch": s.batch, "n_nodes": s.n_nodes, "layers": L,
+            "tree": f"{s.width}-ary x depth {s.depth}" if s.tree == "mary" else s.tree,
+            "h_k": s.h_k, "h_v": s.h_v, "d_k": s.d, "d_v": s.d, "io": s.io,
+            "state": "f32",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "verify", "achieved": achieved,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None, "alg_bytes_per_launch": vb,
+            "launch_us": r["verify_ms"] * 1e3,
+        },
+        "commit": {
+            "launch_us": r["commit_ms"] * 1e3, "alg_bytes_per_launch": r["commit_bytes"],
+            "achieved_GBs": r["commit_bytes"] / (r["commit_ms"] * 1e-3) / 1e9,
+        },
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * gdn_tree.h -- C ABI of the MI355X (gfx950) library for rollback-free
+ * verification of a speculative draft tree through Gated DeltaNet layers.
+ *
+ * Source of the operation: page "Trees from Marginals: Autoregressive drafting
+ * with factorized priors" (gist.science summary of arXiv 2607.06763), section 3
+ * "rollback-free tree verification for GDN".  A GDN layer updates its state with
+ * the gated delta rule (the state-update equation of that section's "challenge"
+ * item).  The section's "solution" items state the method: the tree is
+ * topologically sorted, interaction matrices X and Y encode ancestor
+ * relations, a linear system (I + X) U = beta V yields every node's output
+ * without speculatively updating the recurrent state, and the state is
+ * committed only once the accepted branch is known, at the next decoding
+ * iteration.  Hence two calls: gdn_tree_verify reads the prefix state and
+ * never writes it; gdn_tree_commit writes the accepted node's state.
+ *
+ * What the calls compute.  Per (sequence b, value head h) unit, with the state
+ * S stored d_v x d_k (the page's d_k x d_v state transposed) and value head h
+ * reading key head h / (h_v / h_k):
+ *
+ *     S_i = g_i * S_p(i) * (I - beta_i k_i k_i^T) + beta_i v_i k_i^T,
+ *     S_p(i) = S0 when parent[i] = -1,        o_i = S_i q_i,
+ *
+ * i.e. node i's state is the state reached by running the rule along its own
+ * root-to-node path.  The library realises this with the unrolled tree form
+ * (Gamma_i = sum of ln g over the path, u_i = S_i - g_i S_p(i) as a rank-one
+ * write u_i k_i^T):
+ *
+ *     (I + X) U = R,  X_ij = beta_i e^(Gamma_i-Gamma_j) k_i.k_j  (j strict ancestor)
+ *                     R = diag(beta) (V - diag(e^Gamma) K S0^T)
+ *     O = diag(e^Gamma) Q S0^T + Y U,  Y_ij = e^(Gamma_i-Gamma_j) q_i.k_j  (j ancestor or i)
+ *     commit:  S_a = e^(Gamma_a) S0 + sum_{j on path(a)} e^(Gamma_a-Gamma_j) u_j k_j^T
+ *
+ * (the page's right-hand side beta V is the S0 = 0, undecayed special case).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major arrays
+ *    owned by the caller, 16-byte aligned.  The library allocates nothing,
+ *    never synchronises the device or stream, keeps no global state, and
+ *    enqueues its kernels on `stream` (0 = the null stream).  Calls are
+ *    asynchronous; every output is valid once the stream reaches them.
+ *  - Return value: GDN_OK (0), or a negative gdn_status for an error found on
+ *    the host, in which case nothing was launched.  GDN_ERR_LAUNCH means a
+ *    kernel launch failed (hipGetLastError after the launch).
+ *  - Tree errors are found on the device without a host sync: see
+ *    gdn_tree_cache.tree_status.
+ *  - The library applies no L2 normalisation and no 1/sqrt(d_k) scale to q or
+ *    k; the caller does both.
+ *  - batch = 0 is valid and launches nothing.
+ *  - Supported sizes: 1 <= n_nodes <= 1024; 1 <= d_k, d_v <= 256; h_k >= 1;
+ *    h_v a multiple of h_k.  The fastest kernels cover d_k = d_v = 128.
+ */
+#ifndef GDN_TREE_H
+#define GDN_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o.  bf16 is stored as its 16-bit pattern; the
+ * library rounds o to bf16 with round-to-nearest-even. */
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,    /* a required pointer is NULL                          */
+    GDN_ERR_DIMS = -2,    /* sizes outside the supported range                   */
+    GDN_ERR_DTYPE = -3,   /* io_dtype not a gdn_dtype                            */
+    GDN_ERR_LAUNCH = -4,  /* a kernel launch failed                              */
+    GDN_ERR_ALIGN = -5    /* a device pointer is not 16-byte aligned             */
+} gdn_status;
+
+/* Problem sizes: B sequences (one draft tree each), N nodes per tree, h_k key
+ * heads, h_v value heads, head sizes d_k and d_v, io_dtype a gdn_dtype. */
+typedef struct {
+    int32_t batch, n_nodes, h_k, h_v, d_k, d_v, io_dtype;
+} gdn_tree_dims;
+
+/* Per-call state written by gdn_tree_verify and read by gdn_tree_commit.
+ * Caller-allocated device buffers, sizes from gdn_tree_cache_bytes. */
+typedef struct {
+    /* [B][N][ceil(N/32)]: bit (j % 32) of word j / 32 of row i is set iff node
+     * j is a strict ancestor of node i; padding bits are zero.  Rows of an
+     * invalid tree are zero. */
+    uint32_t* anc_mask;
+    /* [B][N]: number of strict ancestors of each node (depth; 0 under S0),
+     * -1 for every node of an invalid tree. */
+    int32_t* depth;
+    /* [B][H_v][N][d_v] fp32: the rank-one write u_i of every node. */
+    float* u;
+    /* [B][H_v][N] fp32: Gamma_i, the sum of ln g over node i's path. */
+    float* log_gamma;
+    /* [B]: 0 when the tree is valid, else i + 1 for the first node i whose
+     * parent is outside [-1, i).  The o rows of an invalid tree are NaN. */
+    int32_t* tree_status;
+} gdn_tree_cache;
+
+/* Byte sizes of the five cache buffers for `dims` (any pointer may be NULL to
+ * skip it).  Returns GDN_OK, GDN_ERR_NULL (dims NULL) or the size errors of
+ * gdn_tree_verify. */
+int gdn_tree_cache_bytes(const gdn_tree_dims* dims, size_t* anc_mask, size_t* depth,
+                         size_t* u, size_t* log_gamma, size_t* tree_status);
+
+/*
+ * Verify every node of every tree in one pass (section 3, the masked triangular
+ * solve and the single-pass output stage).
+ *
+ *   S0      [B][H_v][d_v][d_k] fp32    prefix state; read only, never written
+ *   q, k    [B][N][H_k][d_k]   io      queries and keys per key head
+ *   v       [B][N][H_v][d_v]   io      values per value head
+ *   beta, g [B][N][H_v]        fp32    write strength and gate, g in (0, 1]
+ *   parent  [B][N]             int32   -1 = follows S0, else an index < i
+ *   o       [B][N][H_v][d_v]   io      out: o_i = S_i q_i
+ *   cache                               out: see gdn_tree_cache
+ *
+ * The tree must list parents before children (a topological order); the
+ * library validates this on the device and does not reorder nodes.
+ */
+int gdn_tree_verify(const gdn_tree_dims* dims, const float* S0, const void* q,
+                    const void* k, const void* v, const float* beta, const float* g,
+                    const int32_t* parent, void* o, const gdn_tree_cache* cache,
+                    hipStream_t stream);
+
+/*
+ * Commit the accepted node's state (section 3, deferred state commitment):
+ * S_out = S_a for a = accepted[b], from the cached u and Gamma, without
+ * replaying the recurrence.
+ *
+ *   S_in     [B][H_v][d_v][d_k] fp32  the S0 that gdn_tree_verify read
+ *   S_out    [B][H_v][d_v][d_k] fp32  out; may alias S_in (in-place commit)
+ *   k        [B][N][H_k][d_k]   io    the keys given to gdn_tree_verify
+ *   cache                              as written by gdn_tree_verify
+ *   accepted [B]                int32 accepted node, or -1 for none
+ *   path     [B][N]             int32 out: root..accepted, -1 padded
+ *   path_len [B]                int32 out: path length; 0 when accepted = -1;
+ *                                     -1 when the tree is invalid or accepted
+ *                                     is outside [-1, N) -- then S_out = S_in
+ *
+ * k and the cache must be unchanged since gdn_tree_verify, with the same dims.
+ */
+int gdn_tree_commit(const gdn_tree_dims* dims, const float* S_in, float* S_out,
+                    const void* k, const gdn_tree_cache* cache, const int32_t* accepted,
+                    int32_t* path, int32_t* path_len, hipStream_t stream);
+
+/* Static description of a gdn_status value. */
+const char* gdn_tree_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_TREE_H */

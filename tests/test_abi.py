@@ -1,0 +1,98 @@
+"""The C-ABI library loads and exports every declared symbol, and its host-side
+argument checks return the documented codes before anything is launched.
+CPU only: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_tree.h")
+
+T = pytest.importorskip("tree_masked_gated_amd")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_tree_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == ["gdn_tree_cache_bytes", "gdn_tree_commit", "gdn_tree_strerror",
+                     "gdn_tree_verify"]
+    out = subprocess.run(["nm", "-D", "--defined-only", T.lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(T._lib, n)
+
+
+def test_header_compiles_as_c():
+    """The header is plain C: a C compiler accepts it on its own."""
+    src = '#include "gdn_tree.h"\nint main(void){gdn_tree_dims d={0};(void)d;return 0;}\n'
+    p = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only", "-I",
+                        os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                        "-D__HIP_PLATFORM_AMD__", "-"], input=src, text=True,
+                       capture_output=True)
+    assert p.returncode == 0, p.stderr
+
+
+def V(d, ptrs, cache=None):
+    return T._lib.gdn_tree_verify(ctypes.byref(d) if d is not None else None, *ptrs,
+                                  ctypes.byref(cache) if cache is not None else None, None)
+
+
+def C(d, ptrs, cache=None, tail=(None, None, None)):
+    return T._lib.gdn_tree_commit(ctypes.byref(d) if d is not None else None, *ptrs,
+                                  ctypes.byref(cache) if cache is not None else None,
+                                  *tail, None)
+
+
+FAKE = 0x10000          # a 16-byte-aligned pointer value, never dereferenced here
+ODD = 0x10004
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="fake device pointers are only passed where no GPU exists")
+def test_error_codes():
+    good = T.dims(2, 7, 1, 2, 16, 16, "f32")
+    ok8 = [FAKE] * 8
+    cache = T.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert V(None, ok8, cache) == -1
+    assert V(good, [None] + ok8[1:], cache) == -1
+    assert V(good, ok8, None) == -1
+    assert V(good, ok8, T.Cache(FAKE, None, FAKE, FAKE, FAKE)) == -1
+    assert V(good, ok8, T.Cache(FAKE, FAKE, ODD, FAKE, FAKE)) == -5
+    assert V(good, ok8[:3] + [ODD] + ok8[4:], cache) == -5
+    assert V(T.dims(2, 7, 1, 2, 16, 16, 5), ok8, cache) == -3
+    for bad in [T.dims(-1, 7, 1, 2, 16, 16, 0), T.dims(2, 0, 1, 2, 16, 16, 0),
+                T.dims(2, 1025, 1, 2, 16, 16, 0), T.dims(2, 7, 0, 2, 16, 16, 0),
+                T.dims(2, 7, 2, 3, 16, 16, 0), T.dims(2, 7, 1, 2, 0, 16, 0),
+                T.dims(2, 7, 1, 2, 16, 257, 0)]:
+        assert V(bad, ok8, cache) == -2
+    # batch 0 launches nothing and succeeds, whatever the pointers
+    assert V(T.dims(0, 7, 1, 2, 16, 16, 0), [None] * 8, None) == 0
+    ok3 = [FAKE] * 3
+    assert C(None, ok3, cache, (FAKE,) * 3) == -1
+    assert C(good, ok3, cache, (FAKE, None, FAKE)) == -1
+    assert C(good, ok3, cache, (FAKE, FAKE, ODD)) == -5
+    assert C(good, [FAKE, ODD, FAKE], cache, (FAKE,) * 3) == -5
+    assert C(T.dims(0, 7, 1, 2, 16, 16, 0), [None] * 3, None) == 0
+    assert C(T.dims(2, 7, 1, 2, 16, 16, 9), ok3, cache, (FAKE,) * 3) == -3
+
+
+def test_strerror_and_cache_bytes():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert T.gdn_tree_strerror(code) and T.gdn_tree_strerror(code) != "unknown gdn_status"
+    assert T.gdn_tree_strerror(-99) == "unknown gdn_status"
+    d = T.dims(3, 70, 2, 4, 32, 64, "bf16")
+    b = T.gdn_tree_cache_bytes(d)
+    assert b == {"anc_mask": 3 * 70 * 3 * 4, "depth": 3 * 70 * 4, "u": 3 * 4 * 70 * 64 * 4,
+                 "log_gamma": 3 * 4 * 70 * 4, "tree_status": 3 * 4}
+    with pytest.raises(T.GdnError):
+        T.gdn_tree_cache_bytes(T.dims(1, 2000, 1, 1, 16, 16, 0))

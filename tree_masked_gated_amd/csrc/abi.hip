@@ -1,0 +1,107 @@
+// abi.hip -- the library's C ABI: argument checks, kernel selection, launches.
+// Every check runs on the host before anything is enqueued; a failed check
+// returns a negative gdn_status and launches nothing.
+#include <stdint.h>
+
+#include "gdn_common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+using namespace gdn;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_dims(const gdn_tree_dims* d) {
+    if (!d) return GDN_ERR_NULL;
+    if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (d->batch < 0 || d->n_nodes < 1 || d->n_nodes > kMaxNodes) return GDN_ERR_DIMS;
+    if (d->h_k < 1 || d->h_v < 1 || d->h_v % d->h_k != 0) return GDN_ERR_DIMS;
+    if (d->d_k < 1 || d->d_k > kMaxHead || d->d_v < 1 || d->d_v > kMaxHead)
+        return GDN_ERR_DIMS;
+    // the grid's x extent is batch * h_v workgroups
+    if ((int64_t)d->batch * d->h_v > 0x7fffffffLL) return GDN_ERR_DIMS;
+    return GDN_OK;
+}
+
+int check_cache(const gdn_tree_cache* c) {
+    if (!c || !c->anc_mask || !c->depth || !c->u || !c->log_gamma || !c->tree_status)
+        return GDN_ERR_NULL;
+    if (misaligned(c->anc_mask) || misaligned(c->depth) || misaligned(c->u) ||
+        misaligned(c->log_gamma) || misaligned(c->tree_status))
+        return GDN_ERR_ALIGN;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_tree_cache_bytes(const gdn_tree_dims* dims, size_t* anc_mask, size_t* depth,
+                         size_t* u, size_t* log_gamma, size_t* tree_status) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const size_t B = dims->batch, N = dims->n_nodes, W = (N + 31) / 32;
+    if (anc_mask) *anc_mask = B * N * W * sizeof(uint32_t);
+    if (depth) *depth = B * N * sizeof(int32_t);
+    if (u) *u = B * (size_t)dims->h_v * N * (size_t)dims->d_v * sizeof(float);
+    if (log_gamma) *log_gamma = B * (size_t)dims->h_v * N * sizeof(float);
+    if (tree_status) *tree_status = B * sizeof(int32_t);
+    return GDN_OK;
+}
+
+int gdn_tree_verify(const gdn_tree_dims* dims, const float* S0, const void* q,
+                    const void* k, const void* v, const float* beta, const float* g,
+                    const int32_t* parent, void* o, const gdn_tree_cache* cache,
+                    hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->batch == 0) return GDN_OK;
+    if (!S0 || !q || !k || !v || !beta || !g || !parent || !o) return GDN_ERR_NULL;
+    rc = check_cache(cache);
+    if (rc) return rc;
+    if (misaligned(S0) || misaligned(q) || misaligned(k) || misaligned(v) ||
+        misaligned(beta) || misaligned(g) || misaligned(parent) || misaligned(o))
+        return GDN_ERR_ALIGN;
+
+    VerifyArgs a{dims->batch, dims->n_nodes, dims->h_k, dims->h_v, dims->d_k, dims->d_v,
+                 S0, q, k, v, beta, g, parent, o,
+                 cache->anc_mask, cache->depth, cache->u, cache->log_gamma,
+                 cache->tree_status};
+    hipError_t e = launch_verify_generic(a, dims->io_dtype, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+int gdn_tree_commit(const gdn_tree_dims* dims, const float* S_in, float* S_out,
+                    const void* k, const gdn_tree_cache* cache, const int32_t* accepted,
+                    int32_t* path, int32_t* path_len, hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->batch == 0) return GDN_OK;
+    if (!S_in || !S_out || !k || !accepted || !path || !path_len) return GDN_ERR_NULL;
+    rc = check_cache(cache);
+    if (rc) return rc;
+    if (misaligned(S_in) || misaligned(S_out) || misaligned(k) || misaligned(accepted) ||
+        misaligned(path) || misaligned(path_len))
+        return GDN_ERR_ALIGN;
+
+    CommitArgs a{dims->batch, dims->n_nodes, dims->h_k, dims->h_v, dims->d_k, dims->d_v,
+                 S_in, S_out, k, cache->anc_mask, cache->u, cache->log_gamma,
+                 cache->tree_status, accepted, path, path_len};
+    hipError_t e = launch_commit(a, dims->io_dtype, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+const char* gdn_tree_strerror(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_DIMS: return "sizes outside the supported range";
+        case GDN_ERR_DTYPE: return "io_dtype is not GDN_F32 or GDN_BF16";
+        case GDN_ERR_LAUNCH: return "a kernel launch failed";
+        case GDN_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+        default: return "unknown gdn_status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,17 @@
+// launch.hpp -- host-side launchers of the library's kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gdn_common.hpp"
+
+namespace gdn {
+
+// General-shape verification: any valid size, fp32 vector arithmetic.
+size_t verify_generic_lds_bytes(int n_nodes);
+hipError_t launch_verify_generic(const VerifyArgs& a, int io, hipStream_t stream);
+
+// Deferred commit of the accepted node's state.
+hipError_t launch_commit(const CommitArgs& a, int io, hipStream_t stream);
+
+}  // namespace gdn

@@ -242,3 +242,23 @@ def unit_slice(s: Spec, lay: dict, parent: np.ndarray, accepted: np.ndarray,
         "parent": parent[b:b + 1],
         "accepted": accepted[b:b + 1],
     }
+
+
+# ---------------------------------------------------------------- upload
+
+def to_device(arr: np.ndarray, io: str = "", device="cuda"):
+    """numpy -> torch device tensor.  io="bf16" reinterprets uint16 bit
+    patterns as torch.bfloat16; everything else keeps its dtype."""
+    import torch
+    a = np.ascontiguousarray(arr)
+    if io == "bf16":
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def from_device_f64(t, io: str = "") -> np.ndarray:
+    """torch tensor -> float64 numpy (bf16 widened exactly)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
