@@ -11,6 +11,10 @@ namespace gdn {
 size_t verify_generic_lds_bytes(int n_nodes);
 hipError_t launch_verify_generic(const VerifyArgs& a, int io, hipStream_t stream);
 
+// MFMA verification: d_k = d_v = 128, bf16 io, up to 128 nodes.
+bool verify_tiled_supported(const VerifyArgs& a, int io);
+hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream);
+
 // Deferred commit of the accepted node's state.
 hipError_t launch_commit(const CommitArgs& a, int io, hipStream_t stream);
 

@@ -1,0 +1,459 @@
+// verify_tiled.hip -- MFMA tree verification for d_k = d_v = 128, bf16 q/k/v/o
+// and trees of up to 16 * NB nodes (NB = 4 or 8 blocks of 16 nodes).
+//
+// Method (page "Trees from Marginals: Autoregressive drafting with factorized
+// priors", section 3, rollback-free tree verification for GDN): with G_i the
+// path sum of ln g and the ancestor relation of the topologically sorted tree,
+//     X_ij = beta_i e^(G_i-G_j) k_i.k_j  (j strict ancestor of i), else 0
+//     Y_ij = e^(G_i-G_j) q_i.k_j         (j ancestor of i, or j = i), else 0
+//     (I + X) U = R,  R = diag(beta) (V - diag(e^G) K S0^T)
+//     O = diag(e^G) Q S0^T + Y U.
+// The section names the three fused stages this kernel runs in one pass: the
+// Gram matrix, a tiled forward substitution, and the output stage.
+//
+// One workgroup per (sequence, key head, group of HPW value heads), four waves
+// per value head.  Every global load is issued at entry (parent, g, beta; the
+// tree's k and q rows; each wave's S0 rows and v columns), so that after the
+// tree is built nothing waits on global memory except the output stores:
+//  1. the tree's strict-ancestor bit rows go to LDS (in-place pointer
+//     jumping), then k / q rows (bf16, XOR-swizzled 16-byte chunks) and, per
+//     value head, G and beta;
+//  2. Gram tiles K_t K_s^T and Q_t K_s^T (16 x 16, s <= t) on
+//     v_mfma_f32_16x16x32_bf16, shared by the HPW heads, masked and decayed
+//     per head into bf16 X / Y tiles (X negated) and fp32 diagonal X blocks;
+//  3. each diagonal block (I + X_tt) is inverted in fp32 (16 x 16 unit lower
+//     triangular, forward substitution per column) and stored as bf16;
+//  4. each wave owns 32 of its head's 128 value columns and runs, block by
+//     block, with no barrier: P_K = K_t S0^T and P_Q^T = S0 Q_t^T (S0 held in
+//     registers as bf16), R_t, the blocked substitution
+//     R_t += sum_{s<t} (-X_ts) U_s, U_t = (I + X_tt)^-1 R_t and
+//     O_t = e^G P_Q + sum_{s<=t} Y_ts U_s on the 16x16x16 MFMA.  The
+//     accumulator layout (lane l: rows 4(l/16)..+3 of column l%16) is also
+//     the B-operand layout of that MFMA, and, read transposed, its A-operand
+//     layout, so U stays in registers as a bf16 hi + lo pair (about 16
+//     mantissa bits) and the outputs come out transposed, four consecutive
+//     columns per lane, for 8- and 16-byte row stores.
+//
+// HBM traffic is the algorithm's own: S0 once (fp32, rounded to bf16 on
+// chip), k / q once per workgroup, v once, o (bf16) and the u / G cache (fp32)
+// written once.  Nothing writes S0.
+#include "gdn_common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ float bf16_val(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// 4 fp32 accumulator values -> bf16 hi part and bf16 lo part (x - hi).
+__device__ __forceinline__ void split4(f32x4 x, s16x4& hi, s16x4& lo) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        uint16_t h = bf16_rne(x[m]);
+        hi[m] = (short)h;
+        lo[m] = (short)bf16_rne(x[m] - bf16_val(h));
+    }
+}
+
+// 8 fp32 -> bf16x8 (RNE).
+__device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
+    bf16x8 r;
+    r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
+    r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
+    return r;
+}
+
+// Map a workgroup id to (sequence b, key head hk, head group hg).  Workgroups
+// are handed to the eight XCDs round robin, so ids x and x + 8 share an XCD and
+// its L2; when a key head has several head groups (GG > 1) they get ids 8
+// apart, so all but the first find that pair's q and k in L2.
+__device__ __forceinline__ void group_of(int x, int B, int Hk, int GG, int& b, int& hk,
+                                         int& hg) {
+    const int P = B * Hk;
+    const int full = (P / 8) * 8 * GG;
+    int pair;
+    if (x < full) {
+        const int q = x / (8 * GG), rem = x % (8 * GG);
+        hg = rem / 8;
+        pair = q * 8 + rem % 8;
+    } else {
+        const int y = x - full;
+        pair = (P / 8) * 8 + y / GG;
+        hg = y % GG;
+    }
+    b = pair / Hk;
+    hk = pair % Hk;
+}
+
+// 16-byte chunk (row, chunk) of a k / q row in LDS; chunks are XOR-swizzled by
+// the row's low bits so the 16 rows of a fragment read hit distinct banks.
+__device__ __forceinline__ int kq_off(int row, int chunk) {
+    return row * kD + ((chunk ^ (row & 15)) << 3);
+}
+
+// A/B fragment of a 16-node block for the 16x16x32 MFMA from LDS: lane l gets
+// row 16*blk + l%16, columns 32*cs + 8*(l/16) .. +7.
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* m, int blk, int cs, int lane) {
+    const int row = 16 * blk + (lane & 15);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                          m + kq_off(row, 4 * cs + (lane >> 4))));
+}
+
+// Position of element (row, col) of a 16x16 tile stored in A-operand fragment
+// order of the 16x16x16 MFMA (lane L holds row L%16, columns 4(L/16)..+3).
+__device__ __forceinline__ int frag_pos(int row, int col) {
+    return (row + 16 * (col >> 2)) * 4 + (col & 3);
+}
+
+template <int NB, int HPW>
+__global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a) {
+    constexpr int NT = 256 * HPW;               // threads
+    constexpr int NP = 16 * NB;                 // padded node count
+    constexpr int NX = NB * (NB - 1) / 2;       // strictly-lower X tiles
+    constexpr int NPAIR = NB * (NB + 1) / 2;    // Gram tiles (s <= t)
+    constexpr int MW = NP / 32 > 0 ? NP / 32 : 1;
+    constexpr int CH = 2 * NP * 16 / NT;        // 16-byte k/q chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[NP * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[NP * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t s_tiles[HPW][NB * NB * 256];  // -X (s < t) then Y (s <= t)
+    __shared__ __attribute__((aligned(16))) uint16_t s_dinv[HPW][NB * 256];        // (I + X_tt)^-1, fragment order
+    __shared__ __attribute__((aligned(16))) float s_xd[HPW][NB * 256];             // diagonal X blocks, fp32
+    __shared__ __attribute__((aligned(16))) uint32_t s_mask[NP * MW];
+    __shared__ __attribute__((aligned(16))) int32_t s_jump[NP];
+    __shared__ __attribute__((aligned(16))) float s_lg[HPW][NP];
+    __shared__ __attribute__((aligned(16))) float s_beta[HPW][NP];
+    __shared__ int s_flag;
+
+    const int N = a.N, Hv = a.Hv, Hk = a.Hk, G = Hv / Hk, GG = G / HPW;
+    const int W = (N + 31) / 32;
+    int b, hk, hg;
+    group_of(blockIdx.x, a.B, Hk, GG, b, hk, hg);
+    const int h0 = hk * G + hg * HPW;                 // first value head here
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hp = wave >> 2, wc = wave & 3;          // this wave: head h0+hp, cols 32wc..
+    const int ln = lane & 15, lq = lane >> 4;
+    const int h = h0 + hp;
+
+    // ---- 0. every global load, oldest first in the order they are needed ----
+    int my_par = 0;
+    float my_g[HPW], my_beta[HPW];
+#pragma unroll
+    for (int p = 0; p < HPW; ++p) { my_g[p] = 1.f; my_beta[p] = 0.f; }
+    if (tid < N) {
+        my_par = a.parent[(size_t)b * N + tid];
+#pragma unroll
+        for (int p = 0; p < HPW; ++p) {
+            const size_t bg = ((size_t)b * N + tid) * Hv + h0 + p;
+            my_g[p] = a.g[bg];
+            my_beta[p] = a.beta[bg];
+        }
+    }
+    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + ((size_t)b * N * Hk + hk) * kD;
+    u32x4 kq[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int x = tid + c * NT;
+        const int mat = x / (NP * 16), rem = x % (NP * 16), row = rem >> 4, q = rem & 15;
+        const uint16_t* src = (mat ? Qb : Kb) + (size_t)row * Hk * kD + q * 8;
+        kq[c] = row < N ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+    }
+    const float* S0 = a.S0 + ((size_t)b * Hv + h) * kD * kD;
+    float4 s0raw[2][4][2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) {
+            const float* p = S0 + (size_t)(32 * wc + 16 * ct + ln) * kD + 32 * cs + 8 * lq;
+            s0raw[ct][cs][0] = *reinterpret_cast<const float4*>(p);
+            s0raw[ct][cs][1] = *reinterpret_cast<const float4*>(p + 4);
+        }
+    const size_t vo_row = (size_t)Hv * kD;                    // stride between nodes
+    const size_t vo_base = ((size_t)b * N * Hv + h) * kD;     // node 0 of head h
+    const uint16_t* V = static_cast<const uint16_t*>(a.v);
+    u32x4 vfr[NB];                                            // v rows of each block
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+        const int i = 16 * t + ln;
+        vfr[t] = i < N ? *reinterpret_cast<const u32x4*>(V + vo_base + (size_t)i * vo_row +
+                                                        32 * wc + 8 * lq)
+                       : u32x4{0, 0, 0, 0};
+    }
+
+    // ---- 1. tree, k / q to LDS, gates -------------------------------------
+    if (tid < N) s_jump[tid] = my_par;            // tree_build_lds reads it after a barrier
+    const int status = tree_build_lds(s_jump, N, W, s_mask, s_jump, &s_flag);
+    if (hk == 0 && hg == 0) {
+        uint32_t* gm = a.anc_mask + (size_t)b * N * W;
+        for (int x = tid; x < N * W; x += NT) gm[x] = s_mask[x];
+        for (int i = tid; i < N; i += NT)
+            a.depth[(size_t)b * N + i] = status ? -1 : row_popc(s_mask + i * W, W);
+        if (tid == 0) a.status[b] = status;
+    }
+    uint16_t* O = static_cast<uint16_t*>(a.o);
+    if (status) {
+        const float qnan = __uint_as_float(0x7fc00000u);
+#pragma unroll
+        for (int p = 0; p < HPW; ++p) {
+            const size_t ob = ((size_t)b * N * Hv + h0 + p) * kD;
+            float* Up = a.u + ((size_t)b * Hv + h0 + p) * (size_t)N * kD;
+            for (int x = tid; x < N * kD; x += NT) {
+                O[ob + (size_t)(x / kD) * vo_row + x % kD] = 0x7fc0;
+                Up[x] = qnan;
+            }
+            for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h0 + p) * N + i] = qnan;
+        }
+        return;
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int x = tid + c * NT;
+        const int mat = x / (NP * 16), rem = x % (NP * 16), row = rem >> 4, q = rem & 15;
+        *reinterpret_cast<u32x4*>((mat ? s_q : s_k) + kq_off(row, q)) = kq[c];
+    }
+    if (tid < NP) {
+#pragma unroll
+        for (int p = 0; p < HPW; ++p) {
+            s_lg[p][tid] = tid < N ? logf(my_g[p]) : 0.f;
+            s_beta[p][tid] = tid < N ? my_beta[p] : 0.f;
+        }
+    }
+    __syncthreads();
+    float my_lg[HPW];
+#pragma unroll
+    for (int p = 0; p < HPW; ++p) my_lg[p] = 0.f;
+    if (tid < N) {
+        for (int w = 0; w < W; ++w) {
+            uint32_t x = s_mask[tid * W + w];
+            while (x) {
+                const int j = w * 32 + __ffs(x) - 1;
+#pragma unroll
+                for (int p = 0; p < HPW; ++p) my_lg[p] += s_lg[p][j];
+                x &= x - 1u;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < HPW; ++p) {
+            my_lg[p] += s_lg[p][tid];
+            a.log_gamma[((size_t)b * Hv + h0 + p) * N + tid] = my_lg[p];
+        }
+    }
+    __syncthreads();
+    if (tid < NP) {
+#pragma unroll
+        for (int p = 0; p < HPW; ++p) s_lg[p][tid] = my_lg[p];
+    }
+    __syncthreads();
+
+    // ---- 2. Gram tiles -> masked, decayed X / Y tiles per head --------------
+    // Computed transposed, K_s K_t^T and K_s Q_t^T: lane l then holds row
+    // i = 16t + l%16 and columns j = 16s + 4(l/16)..+3, which is exactly its slot
+    // in the A-operand fragment order, so each lane stores 8 contiguous bytes.
+    for (int pi = wave; pi < NPAIR; pi += NT / 64) {
+        int t = 0;
+        while ((t + 1) * (t + 2) / 2 <= pi) ++t;
+        const int s = pi - t * (t + 1) / 2;
+        if (16 * t >= N) continue;
+        f32x4 A = {0.f, 0.f, 0.f, 0.f}, C = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) {
+            const bf16x8 ks = lds_frag(s_k, s, cs, lane);
+            A = mfma32(ks, lds_frag(s_k, t, cs, lane), A);
+            C = mfma32(ks, lds_frag(s_q, t, cs, lane), C);
+        }
+        const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
+        // strict-ancestor bits of row i for columns j0..j0+3 (one word holds all four)
+        const uint32_t bits = i < N ? (s_mask[i * W + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
+#pragma unroll
+        for (int p = 0; p < HPW; ++p) {
+            const float lgi = s_lg[p][i], bei = s_beta[p][i];
+            const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[p][j0]);
+            const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
+            float xv[4];
+            uint16_t yv[4], nxv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool anc = (bits >> e) & 1u;
+                const bool self = (j0 + e == i) && i < N;
+                const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
+                xv[e] = anc ? bei * d * A[e] : 0.f;
+                yv[e] = bf16_rne(d * C[e]);
+                nxv[e] = bf16_rne(-xv[e]);
+            }
+            *reinterpret_cast<uint2*>(&s_tiles[p][(NX + t * (t + 1) / 2 + s) * 256 + lane * 4]) =
+                make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
+            if (s < t)
+                *reinterpret_cast<uint2*>(&s_tiles[p][(t * (t - 1) / 2 + s) * 256 + lane * 4]) =
+                    make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
+            else
+                *reinterpret_cast<float4*>(&s_xd[p][t * 256 + ln * 16 + 4 * lq]) =
+                    make_float4(xv[0], xv[1], xv[2], xv[3]);
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. diagonal blocks: (I + X_tt)^-1 in fp32 ------------------------
+    {
+        const int blk = tid >> 4, p = blk / NB, t = blk % NB;
+        if (blk < HPW * NB && 16 * t < N) {
+            const float* xd = s_xd[p] + t * 256;
+            float y[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = (i == ln) ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc = fmaf(-xd[i * 16 + m], y[m], acc);
+                y[i] = acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s_dinv[p][t * 256 + frag_pos(i, ln)] = bf16_rne(y[i]);
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. per wave: projection, blocked substitution, output -------------
+    // Register fragments and the layouts they serve (16x16 MFMA tiles):
+    //   sb[ct][cs]  S0 rows r = 32wc + 16ct + l%16, cols 32cs + 8(l/16)..+7:
+    //               B operand of K S0^T and A operand of S0 Q^T;
+    //   k / q frags rows of block t (LDS): A operand of K S0^T, B operand of
+    //               S0 Q^T;
+    //   vfr[t]      v rows of block t, this wave's 32 columns (A operand), moved
+    //               into accumulator layout by an exact 0/1 selection product;
+    //   uhi / ulo   U_s in accumulator layout (node rows): B operand of X U,
+    //               and, read as U_s^T, A operand of U^T Y^T.
+    bf16x8 sb[2][4];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) sb[ct][cs] = to_bf16x8(s0raw[ct][cs][0], s0raw[ct][cs][1]);
+    bf16x8 sel[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            sel[ct][e] = (8 * lq + e == 16 * ct + ln) ? (__bf16)1.0f : (__bf16)0.0f;
+
+    const uint16_t* tiles = s_tiles[hp];
+    const float* lgp = s_lg[hp];
+    const float* bep = s_beta[hp];
+    float* Ug = a.u + ((size_t)b * Hv + h) * (size_t)N * kD;
+    s16x4 uhi[NB][2], ulo[NB][2];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+        if (16 * t >= N) break;                             // uniform
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 pk[2], pqT[2], vd[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            pk[ct] = z;
+            pqT[ct] = z;
+            vd[ct] = mfma32(__builtin_bit_cast(bf16x8, vfr[t]), sel[ct], z);
+        }
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) {
+            const bf16x8 kf = lds_frag(s_k, t, cs, lane), qf = lds_frag(s_q, t, cs, lane);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                pk[ct] = mfma32(kf, sb[ct][cs], pk[ct]);      // [node][r]
+                pqT[ct] = mfma32(sb[ct][cs], qf, pqT[ct]);    // [r][node]
+            }
+        }
+        // R_t = beta (V - e^G P_K) on rows i = 16t + 4(l/16) + m
+        f32x4 R[2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = 16 * t + 4 * lq + m;
+            const float eg = __expf(lgp[i]), be = bep[i];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) R[ct][m] = be * (vd[ct][m] - eg * pk[ct][m]);
+        }
+        // R_t += sum_{s<t} (-X_ts) U_s
+#pragma unroll
+        for (int s = 0; s < t; ++s) {
+            const s16x4 nx = *reinterpret_cast<const s16x4*>(tiles + (t * (t - 1) / 2 + s) * 256 + lane * 4);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                R[ct] = mfma16(nx, uhi[s][ct], R[ct]);
+                R[ct] = mfma16(nx, ulo[s][ct], R[ct]);
+            }
+        }
+        // U_t = (I + X_tt)^-1 R_t, kept as [node][r]; U_t^T = R_t^T Dinv^T is stored
+        const s16x4 di = *reinterpret_cast<const s16x4*>(s_dinv[hp] + t * 256 + lane * 4);
+        const int node = 16 * t + ln;                        // this lane's node in ^T tiles
+        const float egn = __expf(lgp[node]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            s16x4 rh, rl;
+            split4(R[ct], rh, rl);
+            f32x4 U = mfma16(di, rh, z);
+            U = mfma16(di, rl, U);
+            split4(U, uhi[t][ct], ulo[t][ct]);
+            f32x4 UT = mfma16(rh, di, z);
+            UT = mfma16(rl, di, UT);
+            if (node < N)
+                *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + 32 * wc + 16 * ct + 4 * lq) = UT;
+        }
+        // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            f32x4 OT = egn * pqT[ct];
+#pragma unroll
+            for (int s = 0; s <= t; ++s) {
+                const s16x4 yt = *reinterpret_cast<const s16x4*>(tiles + (NX + t * (t + 1) / 2 + s) * 256 + lane * 4);
+                OT = mfma16(uhi[s][ct], yt, OT);
+                OT = mfma16(ulo[s][ct], yt, OT);
+            }
+            if (node < N) {
+                uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
+                uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
+                *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + 32 * wc +
+                                          16 * ct + 4 * lq) = make_uint2(lo, hi);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool verify_tiled_supported(const VerifyArgs& a, int io) {
+    return io == GDN_BF16 && a.dk == kD && a.dv == kD && a.N <= 128;
+}
+
+hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream) {
+    (void)io;
+    const int G = a.Hv / a.Hk;
+    const int hpw = (G % 2 == 0) ? 2 : 1;
+    const void* fn;
+    if (a.N <= 64)
+        fn = hpw == 2 ? (const void*)verify_tiled_kernel<4, 2> : (const void*)verify_tiled_kernel<4, 1>;
+    else
+        fn = hpw == 2 ? (const void*)verify_tiled_kernel<8, 2> : (const void*)verify_tiled_kernel<8, 1>;
+    VerifyArgs copy = a;
+    void* args[] = {&copy};
+    const unsigned groups = (unsigned)(a.B * a.Hk * (G / hpw));
+    return hipLaunchKernel(fn, dim3(groups), dim3(256 * hpw), args, 0, stream);
+}
+
+}  // namespace gdn
