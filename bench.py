@@ -194,6 +194,32 @@ def cpu_baseline(s, budget_s):
                       f"{nb * s.n_nodes} nodes), fp64 path walk, {dt:.2f} s"}
 
 
+# ---------------------------------------------------------------- copy
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of a known size (torch's copy kernel): the
+    reference for scaling FETCH_SIZE / WRITE_SIZE counters and the achievable
+    streaming bandwidth on this machine."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    moved = 2 * n * 4
+    print(json.dumps({"copy_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4,
+                      "us_per_copy": ms * 1e3, "GBs": moved / (ms * 1e-3) / 1e9}), flush=True)
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -204,7 +230,12 @@ def main():
     ap.add_argument("--workload", default="mary128_b64_l36")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every (sequence, value head) unit is "

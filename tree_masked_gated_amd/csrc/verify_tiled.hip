@@ -128,8 +128,9 @@ __device__ __forceinline__ int frag_pos(int row, int col) {
 }
 
 template <int NB, int HPW>
-__global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a) {
-    constexpr int NT = 256 * HPW;               // threads
+__global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a) {
+    constexpr int WPH = 8;                      // waves per value head (16 columns each)
+    constexpr int NT = 64 * WPH * HPW;          // threads
     constexpr int NP = 16 * NB;                 // padded node count
     constexpr int NX = NB * (NB - 1) / 2;       // strictly-lower X tiles
     constexpr int NPAIR = NB * (NB + 1) / 2;    // Gram tiles (s <= t)
@@ -137,9 +138,9 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     constexpr int CH = 2 * NP * 16 / NT;        // 16-byte k/q chunks per thread
     __shared__ __attribute__((aligned(16))) uint16_t s_k[NP * kD];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[NP * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t s_tiles[HPW][NB * NB * 256];  // -X (s < t) then Y (s <= t)
-    __shared__ __attribute__((aligned(16))) uint16_t s_dinv[HPW][NB * 256];        // (I + X_tt)^-1, fragment order
-    __shared__ __attribute__((aligned(16))) float s_xd[HPW][NB * 256];             // diagonal X blocks, fp32
+    __shared__ __attribute__((aligned(16))) uint16_t s_tiles[HPW][NB * NB * 256];  // -X then Y
+    __shared__ __attribute__((aligned(16))) uint16_t s_dinv[HPW][NB * 256];
+    __shared__ __attribute__((aligned(16))) float s_xd[HPW][NB * 256];
     __shared__ __attribute__((aligned(16))) uint32_t s_mask[NP * MW];
     __shared__ __attribute__((aligned(16))) int32_t s_jump[NP];
     __shared__ __attribute__((aligned(16))) float s_lg[HPW][NP];
@@ -152,9 +153,10 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     group_of(blockIdx.x, a.B, Hk, GG, b, hk, hg);
     const int h0 = hk * G + hg * HPW;                 // first value head here
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int hp = wave >> 2, wc = wave & 3;          // this wave: head h0+hp, cols 32wc..
+    const int hp = wave / WPH, wc = wave % WPH;       // this wave: head h0+hp, cols 16wc..
     const int ln = lane & 15, lq = lane >> 4;
     const int h = h0 + hp;
+    const int col0 = 16 * wc;
 
     // ---- 0. every global load, oldest first in the order they are needed ----
     int my_par = 0;
@@ -181,25 +183,23 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         kq[c] = row < N ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
     }
     const float* S0 = a.S0 + ((size_t)b * Hv + h) * kD * kD;
-    float4 s0raw[2][4][2];
+    float4 s0raw[4][2];                               // rows col0 + l%16, 32-col chunks
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-            const float* p = S0 + (size_t)(32 * wc + 16 * ct + ln) * kD + 32 * cs + 8 * lq;
-            s0raw[ct][cs][0] = *reinterpret_cast<const float4*>(p);
-            s0raw[ct][cs][1] = *reinterpret_cast<const float4*>(p + 4);
-        }
+    for (int cs = 0; cs < 4; ++cs) {
+        const float* p = S0 + (size_t)(col0 + ln) * kD + 32 * cs + 8 * lq;
+        s0raw[cs][0] = *reinterpret_cast<const float4*>(p);
+        s0raw[cs][1] = *reinterpret_cast<const float4*>(p + 4);
+    }
     const size_t vo_row = (size_t)Hv * kD;                    // stride between nodes
     const size_t vo_base = ((size_t)b * N * Hv + h) * kD;     // node 0 of head h
     const uint16_t* V = static_cast<const uint16_t*>(a.v);
-    u32x4 vfr[NB];                                            // v rows of each block
+    uint2 vfr[NB];                                            // v: node 16t + l%16, 4 cols
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
         const int i = 16 * t + ln;
-        vfr[t] = i < N ? *reinterpret_cast<const u32x4*>(V + vo_base + (size_t)i * vo_row +
-                                                        32 * wc + 8 * lq)
-                       : u32x4{0, 0, 0, 0};
+        vfr[t] = i < N ? *reinterpret_cast<const uint2*>(V + vo_base + (size_t)i * vo_row +
+                                                        col0 + 4 * lq)
+                       : make_uint2(0u, 0u);
     }
 
     // ---- 1. tree, k / q to LDS, gates -------------------------------------
@@ -335,102 +335,77 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 
     // ---- 4. per wave: projection, blocked substitution, output -------------
     // Register fragments and the layouts they serve (16x16 MFMA tiles):
-    //   sb[ct][cs]  S0 rows r = 32wc + 16ct + l%16, cols 32cs + 8(l/16)..+7:
-    //               B operand of K S0^T and A operand of S0 Q^T;
+    //   sb[cs]      S0 rows r = col0 + l%16, cols 32cs + 8(l/16)..+7: B operand of
+    //               K S0^T and A operand of S0 Q^T;
     //   k / q frags rows of block t (LDS): A operand of K S0^T, B operand of
     //               S0 Q^T;
-    //   vfr[t]      v rows of block t, this wave's 32 columns (A operand), moved
-    //               into accumulator layout by an exact 0/1 selection product;
+    //   vfr[t]      v rows of block t, this wave's 16 columns (A operand), moved
+    //               into accumulator layout by an exact product with I;
     //   uhi / ulo   U_s in accumulator layout (node rows): B operand of X U,
     //               and, read as U_s^T, A operand of U^T Y^T.
-    bf16x8 sb[2][4];
+    // Sums over s run in separate hi / lo accumulators to halve chain depth.
+    bf16x8 sb[4];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int cs = 0; cs < 4; ++cs) sb[cs] = to_bf16x8(s0raw[cs][0], s0raw[cs][1]);
+    s16x4 ident;
 #pragma unroll
-        for (int cs = 0; cs < 4; ++cs) sb[ct][cs] = to_bf16x8(s0raw[ct][cs][0], s0raw[ct][cs][1]);
-    bf16x8 sel[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            sel[ct][e] = (8 * lq + e == 16 * ct + ln) ? (__bf16)1.0f : (__bf16)0.0f;
+    for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
 
     const uint16_t* tiles = s_tiles[hp];
     const float* lgp = s_lg[hp];
     const float* bep = s_beta[hp];
     float* Ug = a.u + ((size_t)b * Hv + h) * (size_t)N * kD;
-    s16x4 uhi[NB][2], ulo[NB][2];
+    s16x4 uhi[NB], ulo[NB];
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
         if (16 * t >= N) break;                             // uniform
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 pk[2], pqT[2], vd[2];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            pk[ct] = z;
-            pqT[ct] = z;
-            vd[ct] = mfma32(__builtin_bit_cast(bf16x8, vfr[t]), sel[ct], z);
-        }
+        f32x4 pk = z, pqT = z;
+        const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vfr[t]), ident, z);
 #pragma unroll
         for (int cs = 0; cs < 4; ++cs) {
-            const bf16x8 kf = lds_frag(s_k, t, cs, lane), qf = lds_frag(s_q, t, cs, lane);
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                pk[ct] = mfma32(kf, sb[ct][cs], pk[ct]);      // [node][r]
-                pqT[ct] = mfma32(sb[ct][cs], qf, pqT[ct]);    // [r][node]
-            }
+            pk = mfma32(lds_frag(s_k, t, cs, lane), sb[cs], pk);      // [node][r]
+            pqT = mfma32(sb[cs], lds_frag(s_q, t, cs, lane), pqT);    // [r][node]
         }
-        // R_t = beta (V - e^G P_K) on rows i = 16t + 4(l/16) + m
-        f32x4 R[2];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int i = 16 * t + 4 * lq + m;
-            const float eg = __expf(lgp[i]), be = bep[i];
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) R[ct][m] = be * (vd[ct][m] - eg * pk[ct][m]);
-        }
-        // R_t += sum_{s<t} (-X_ts) U_s
+        // R_t = beta (V - e^G P_K) + sum_{s<t} (-X_ts) U_s
+        f32x4 R, Rh = z, Rl = z;
 #pragma unroll
         for (int s = 0; s < t; ++s) {
             const s16x4 nx = *reinterpret_cast<const s16x4*>(tiles + (t * (t - 1) / 2 + s) * 256 + lane * 4);
+            Rh = mfma16(nx, uhi[s], Rh);
+            Rl = mfma16(nx, ulo[s], Rl);
+        }
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                R[ct] = mfma16(nx, uhi[s][ct], R[ct]);
-                R[ct] = mfma16(nx, ulo[s][ct], R[ct]);
-            }
+        for (int m = 0; m < 4; ++m) {
+            const int i = 16 * t + 4 * lq + m;
+            R[m] = bep[i] * (vd[m] - __expf(lgp[i]) * pk[m]) + (Rh[m] + Rl[m]);
         }
         // U_t = (I + X_tt)^-1 R_t, kept as [node][r]; U_t^T = R_t^T Dinv^T is stored
         const s16x4 di = *reinterpret_cast<const s16x4*>(s_dinv[hp] + t * 256 + lane * 4);
         const int node = 16 * t + ln;                        // this lane's node in ^T tiles
-        const float egn = __expf(lgp[node]);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            s16x4 rh, rl;
-            split4(R[ct], rh, rl);
-            f32x4 U = mfma16(di, rh, z);
-            U = mfma16(di, rl, U);
-            split4(U, uhi[t][ct], ulo[t][ct]);
-            f32x4 UT = mfma16(rh, di, z);
-            UT = mfma16(rl, di, UT);
-            if (node < N)
-                *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + 32 * wc + 16 * ct + 4 * lq) = UT;
-        }
+        s16x4 rh, rl;
+        split4(R, rh, rl);
+        const f32x4 U = mfma16(di, rl, mfma16(di, rh, z));
+        split4(U, uhi[t], ulo[t]);
+        const f32x4 UT = mfma16(rl, di, mfma16(rh, di, z));
+        if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 4 * lq) = UT;
         // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T
+        f32x4 Oh = z, Ol = z;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            f32x4 OT = egn * pqT[ct];
+        for (int s = 0; s <= t; ++s) {
+            const s16x4 yt = *reinterpret_cast<const s16x4*>(tiles + (NX + t * (t + 1) / 2 + s) * 256 + lane * 4);
+            Oh = mfma16(uhi[s], yt, Oh);
+            Ol = mfma16(ulo[s], yt, Ol);
+        }
+        if (node < N) {
+            const float egn = __expf(lgp[node]);
+            f32x4 OT;
 #pragma unroll
-            for (int s = 0; s <= t; ++s) {
-                const s16x4 yt = *reinterpret_cast<const s16x4*>(tiles + (NX + t * (t + 1) / 2 + s) * 256 + lane * 4);
-                OT = mfma16(uhi[s][ct], yt, OT);
-                OT = mfma16(ulo[s][ct], yt, OT);
-            }
-            if (node < N) {
-                uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
-                uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
-                *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + 32 * wc +
-                                          16 * ct + 4 * lq) = make_uint2(lo, hi);
-            }
+            for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[m] + (Oh[m] + Ol[m]);
+            const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
+            const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
+            *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + col0 + 4 * lq) =
+                make_uint2(lo, hi);
         }
     }
 }
@@ -453,7 +428,7 @@ hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream) 
     VerifyArgs copy = a;
     void* args[] = {&copy};
     const unsigned groups = (unsigned)(a.B * a.Hk * (G / hpw));
-    return hipLaunchKernel(fn, dim3(groups), dim3(256 * hpw), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(groups), dim3(512 * hpw), args, 0, stream);
 }
 
 }  // namespace gdn
