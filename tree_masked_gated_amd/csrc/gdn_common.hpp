@@ -91,6 +91,15 @@ __device__ __forceinline__ void lds_store_relaxed(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Workgroup barrier that orders LDS only: this wave's LDS operations are
+// complete, then all waves meet.  Unlike __syncthreads() it does not wait for
+// the wave's outstanding global loads and stores, so prefetches and output
+// stores stay in flight across it.  Only valid where no thread reads global
+// memory written by another thread of the workgroup.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Validate one tree's parent row and build its strict-ancestor bit rows in LDS
 // (the ancestor relation behind the interaction matrices X and Y).
 //
@@ -107,27 +116,33 @@ __device__ __forceinline__ void lds_store_relaxed(uint32_t* p, uint32_t v) {
 // seeing a later value of either only adds true ancestors.  Every step moves
 // J_i strictly rootward, so the loop ends; the segment at least doubles per
 // round, so ceil(log2(N)) + 1 rounds suffice.
+// kLdsOnly selects lds_barrier() (parent row already in LDS, nothing global
+// read here) instead of __syncthreads().
+template <bool kLdsOnly = false>
 __device__ inline int tree_build_lds(const int32_t* __restrict__ par, int N, int W,
                                      uint32_t* mask, int32_t* jump, int* s_flag) {
+    auto bar = [] {
+        if constexpr (kLdsOnly) lds_barrier(); else __syncthreads();
+    };
     const int tid = threadIdx.x, nt = blockDim.x;
     if (tid == 0) *s_flag = 0x7fffffff;
     for (int x = tid; x < N * W; x += nt) mask[x] = 0u;
-    __syncthreads();
+    bar();
     for (int i = tid; i < N; i += nt) {
         int p = par[i];
         jump[i] = p;
         if (p < -1 || p >= i) atomicMin(s_flag, i);
     }
-    __syncthreads();
+    bar();
     const int first_bad = *s_flag;
-    __syncthreads();
+    bar();
     if (first_bad != 0x7fffffff) return first_bad + 1;
 
     for (int i = tid; i < N; i += nt) {
         int p = jump[i];
         if (p >= 0) mask[i * W + (p >> 5)] = 1u << (p & 31);
     }
-    __syncthreads();
+    bar();
     for (int round = 0; round < 12; ++round) {
         int active = 0;
         for (int i = tid; i < N; i += nt) {
@@ -142,9 +157,15 @@ __device__ inline int tree_build_lds(const int32_t* __restrict__ par, int N, int
             lds_store_release(&jump[i], nxt);
             active |= (nxt >= 0);
         }
-        if (!__syncthreads_or(active)) break;
+        // any thread still jumping?  (s_flag is free after the validity check)
+        if (tid == 0) *s_flag = 0;
+        bar();
+        if (active) *s_flag = 1;
+        bar();
+        const int any = *s_flag;
+        bar();
+        if (!any) break;
     }
-    __syncthreads();
     return 0;
 }
 

@@ -77,6 +77,13 @@ __device__ __forceinline__ void split4(f32x4 x, s16x4& hi, s16x4& lo) {
     }
 }
 
+__device__ __forceinline__ s16x4 to_bf16x4(f32x4 x) {
+    s16x4 r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) r[m] = (short)bf16_rne(x[m]);
+    return r;
+}
+
 // 8 fp32 -> bf16x8 (RNE).
 __device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
     bf16x8 r;
@@ -127,15 +134,26 @@ __device__ __forceinline__ int frag_pos(int row, int col) {
     return (row + 16 * (col >> 2)) * 4 + (col & 3);
 }
 
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Persistent workgroups, one per CU, each looping over (sequence, key head,
+// head group) work items.  As soon as item n's solve is done, item n+1's inputs
+// are requested, oldest first in the order they are needed: parent / g / beta
+// and S0 rows into registers, k / q rows straight from HBM into LDS
+// (global_load_lds); its v rows follow once those have landed and are used only
+// after its Gram.  Their latency overlaps item n+1's tree build, and the solve
+// itself never waits on a load queued behind a prefetch (loads retire in order).
 template <int NB, int HPW>
-__global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a) {
-    constexpr int WPH = 8;                      // waves per value head (16 columns each)
-    constexpr int NT = 64 * WPH * HPW;          // threads
+__global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a, int nitems) {
+    constexpr int WPH = 8;                      // waves per value head, 16 columns each
+    constexpr int NW = WPH * HPW;               // waves
+    constexpr int NT = 64 * NW;                 // threads
     constexpr int NP = 16 * NB;                 // padded node count
     constexpr int NX = NB * (NB - 1) / 2;       // strictly-lower X tiles
     constexpr int NPAIR = NB * (NB + 1) / 2;    // Gram tiles (s <= t)
     constexpr int MW = NP / 32 > 0 ? NP / 32 : 1;
-    constexpr int CH = 2 * NP * 16 / NT;        // 16-byte k/q chunks per thread
+    constexpr int KQ_INS = 2 * NP / 4;          // 1 KB direct-to-LDS loads for k and q
     __shared__ __attribute__((aligned(16))) uint16_t s_k[NP * kD];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[NP * kD];
     __shared__ __attribute__((aligned(16))) uint16_t s_tiles[HPW][NB * NB * 256];  // -X then Y
@@ -149,264 +167,325 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 
     const int N = a.N, Hv = a.Hv, Hk = a.Hk, G = Hv / Hk, GG = G / HPW;
     const int W = (N + 31) / 32;
-    int b, hk, hg;
-    group_of(blockIdx.x, a.B, Hk, GG, b, hk, hg);
-    const int h0 = hk * G + hg * HPW;                 // first value head here
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nblk = (N + 15) / 16;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hp = wave / WPH, wc = wave % WPH;       // this wave: head h0+hp, cols 16wc..
-    const int ln = lane & 15, lq = lane >> 4;
-    const int h = h0 + hp;
     const int col0 = 16 * wc;
+    const size_t vo_row = (size_t)Hv * kD;            // stride between nodes in v / o
+    // Thread index, re-read through an empty asm at every item so that the many
+    // thread-derived LDS / global addresses are recomputed per item instead of
+    // being hoisted out of the item loop (which would pin them in registers).
+    int tid = threadIdx.x;
+    int lane = tid & 63;
+    int ln = lane & 15, lq = lane >> 4;
 
-    // ---- 0. every global load, oldest first in the order they are needed ----
+    // item -> (sequence, key head, head group)
+    auto decode = [&](int it, int& b, int& hk, int& hg) {
+        hg = it % GG;
+        const int bh = it / GG;
+        hk = bh % Hk;
+        b = bh / Hk;
+    };
+
+    // ---- prefetch helpers (registers / LDS written by loads in flight) ----
     int my_par = 0;
     float my_g[HPW], my_beta[HPW];
-#pragma unroll
-    for (int p = 0; p < HPW; ++p) { my_g[p] = 1.f; my_beta[p] = 0.f; }
-    if (tid < N) {
-        my_par = a.parent[(size_t)b * N + tid];
+    // Prefetches into registers are unconditional (clamped indices): a load
+    // under a branch would leave a control-flow merge that copies its result,
+    // and the copy would wait for every older load and store of the wave.
+    auto load_small = [&](int it) {
+        int b, hk, hg;
+        decode(it, b, hk, hg);
+        const int h0 = hk * G + hg * HPW;
+        const int ii = tid < N ? tid : 0;              // rows past N are never used
+        my_par = a.parent[(size_t)b * N + ii];
 #pragma unroll
         for (int p = 0; p < HPW; ++p) {
-            const size_t bg = ((size_t)b * N + tid) * Hv + h0 + p;
+            const size_t bg = ((size_t)b * N + ii) * Hv + h0 + p;
             my_g[p] = a.g[bg];
             my_beta[p] = a.beta[bg];
         }
-    }
-    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
-    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + ((size_t)b * N * Hk + hk) * kD;
-    u32x4 kq[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int x = tid + c * NT;
-        const int mat = x / (NP * 16), rem = x % (NP * 16), row = rem >> 4, q = rem & 15;
-        const uint16_t* src = (mat ? Qb : Kb) + (size_t)row * Hk * kD + q * 8;
-        kq[c] = row < N ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
-    }
-    const float* S0 = a.S0 + ((size_t)b * Hv + h) * kD * kD;
-    float4 s0raw[4][2];                               // rows col0 + l%16, 32-col chunks
-#pragma unroll
-    for (int cs = 0; cs < 4; ++cs) {
-        const float* p = S0 + (size_t)(col0 + ln) * kD + 32 * cs + 8 * lq;
-        s0raw[cs][0] = *reinterpret_cast<const float4*>(p);
-        s0raw[cs][1] = *reinterpret_cast<const float4*>(p + 4);
-    }
-    const size_t vo_row = (size_t)Hv * kD;                    // stride between nodes
-    const size_t vo_base = ((size_t)b * N * Hv + h) * kD;     // node 0 of head h
-    const uint16_t* V = static_cast<const uint16_t*>(a.v);
-    uint2 vfr[NB];                                            // v: node 16t + l%16, 4 cols
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-        const int i = 16 * t + ln;
-        vfr[t] = i < N ? *reinterpret_cast<const uint2*>(V + vo_base + (size_t)i * vo_row +
-                                                        col0 + 4 * lq)
-                       : make_uint2(0u, 0u);
-    }
+    };
+    // k and q rows of the item's tree into s_k / s_q: each wave instruction
+    // fills 1 KB (4 rows) of LDS, lane l landing on row r0 + l/16, physical chunk
+    // l%16, which holds logical chunk (l%16) ^ (row & 15).  Rows past N copy
+    // row N-1 (finite values; masks and beta = 0 keep them out of every result).
+    auto kq_dma = [&](int it) {
+        int b, hk, hg;
+        decode(it, b, hk, hg);
+        const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
+        const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + ((size_t)b * N * Hk + hk) * kD;
+        for (int ins = wave; ins < KQ_INS; ins += NW) {
+            const int mat = ins / (NP / 4), r0 = (ins % (NP / 4)) * 4;
+            const int row = r0 + (lane >> 4), pc = lane & 15;
+            const int srow = row < N ? row : N - 1;
+            const uint16_t* src = (mat ? Qb : Kb) + (size_t)srow * Hk * kD + ((pc ^ (row & 15)) << 3);
+            uint16_t* dst = (mat ? s_q : s_k) + r0 * kD;
+            __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+        }
+    };
+    float4 s0raw[4][2];
+    // chunk c of this wave's S0 rows (col0 + l%16): key columns 32c + 8(l/16)..+7
+    auto load_s0 = [&](int it, int c) {
+        int b, hk, hg;
+        decode(it, b, hk, hg);
+        const int h = hk * G + hg * HPW + hp;
+        const float* p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(col0 + ln) * kD +
+                         32 * c + 8 * lq;
+        s0raw[c][0] = *reinterpret_cast<const float4*>(p);
+        s0raw[c][1] = *reinterpret_cast<const float4*>(p + 4);
+    };
 
-    // ---- 1. tree, k / q to LDS, gates -------------------------------------
-    if (tid < N) s_jump[tid] = my_par;            // tree_build_lds reads it after a barrier
-    const int status = tree_build_lds(s_jump, N, W, s_mask, s_jump, &s_flag);
-    if (hk == 0 && hg == 0) {
-        uint32_t* gm = a.anc_mask + (size_t)b * N * W;
-        for (int x = tid; x < N * W; x += NT) gm[x] = s_mask[x];
-        for (int i = tid; i < N; i += NT)
-            a.depth[(size_t)b * N + i] = status ? -1 : row_popc(s_mask + i * W, W);
-        if (tid == 0) a.status[b] = status;
-    }
-    uint16_t* O = static_cast<uint16_t*>(a.o);
-    if (status) {
-        const float qnan = __uint_as_float(0x7fc00000u);
-#pragma unroll
-        for (int p = 0; p < HPW; ++p) {
-            const size_t ob = ((size_t)b * N * Hv + h0 + p) * kD;
-            float* Up = a.u + ((size_t)b * Hv + h0 + p) * (size_t)N * kD;
-            for (int x = tid; x < N * kD; x += NT) {
-                O[ob + (size_t)(x / kD) * vo_row + x % kD] = 0x7fc0;
-                Up[x] = qnan;
-            }
-            for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h0 + p) * N + i] = qnan;
-        }
-        return;
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int x = tid + c * NT;
-        const int mat = x / (NP * 16), rem = x % (NP * 16), row = rem >> 4, q = rem & 15;
-        *reinterpret_cast<u32x4*>((mat ? s_q : s_k) + kq_off(row, q)) = kq[c];
-    }
-    if (tid < NP) {
-#pragma unroll
-        for (int p = 0; p < HPW; ++p) {
-            s_lg[p][tid] = tid < N ? logf(my_g[p]) : 0.f;
-            s_beta[p][tid] = tid < N ? my_beta[p] : 0.f;
-        }
-    }
-    __syncthreads();
-    float my_lg[HPW];
-#pragma unroll
-    for (int p = 0; p < HPW; ++p) my_lg[p] = 0.f;
-    if (tid < N) {
-        for (int w = 0; w < W; ++w) {
-            uint32_t x = s_mask[tid * W + w];
-            while (x) {
-                const int j = w * 32 + __ffs(x) - 1;
-#pragma unroll
-                for (int p = 0; p < HPW; ++p) my_lg[p] += s_lg[p][j];
-                x &= x - 1u;
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < HPW; ++p) {
-            my_lg[p] += s_lg[p][tid];
-            a.log_gamma[((size_t)b * Hv + h0 + p) * N + tid] = my_lg[p];
-        }
-    }
-    __syncthreads();
-    if (tid < NP) {
-#pragma unroll
-        for (int p = 0; p < HPW; ++p) s_lg[p][tid] = my_lg[p];
-    }
-    __syncthreads();
-
-    // ---- 2. Gram tiles -> masked, decayed X / Y tiles per head --------------
-    // Computed transposed, K_s K_t^T and K_s Q_t^T: lane l then holds row
-    // i = 16t + l%16 and columns j = 16s + 4(l/16)..+3, which is exactly its slot
-    // in the A-operand fragment order, so each lane stores 8 contiguous bytes.
-    for (int pi = wave; pi < NPAIR; pi += NT / 64) {
-        int t = 0;
-        while ((t + 1) * (t + 2) / 2 <= pi) ++t;
-        const int s = pi - t * (t + 1) / 2;
-        if (16 * t >= N) continue;
-        f32x4 A = {0.f, 0.f, 0.f, 0.f}, C = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-            const bf16x8 ks = lds_frag(s_k, s, cs, lane);
-            A = mfma32(ks, lds_frag(s_k, t, cs, lane), A);
-            C = mfma32(ks, lds_frag(s_q, t, cs, lane), C);
-        }
-        const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
-        // strict-ancestor bits of row i for columns j0..j0+3 (one word holds all four)
-        const uint32_t bits = i < N ? (s_mask[i * W + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
-#pragma unroll
-        for (int p = 0; p < HPW; ++p) {
-            const float lgi = s_lg[p][i], bei = s_beta[p][i];
-            const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[p][j0]);
-            const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
-            float xv[4];
-            uint16_t yv[4], nxv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool anc = (bits >> e) & 1u;
-                const bool self = (j0 + e == i) && i < N;
-                const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
-                xv[e] = anc ? bei * d * A[e] : 0.f;
-                yv[e] = bf16_rne(d * C[e]);
-                nxv[e] = bf16_rne(-xv[e]);
-            }
-            *reinterpret_cast<uint2*>(&s_tiles[p][(NX + t * (t + 1) / 2 + s) * 256 + lane * 4]) =
-                make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
-            if (s < t)
-                *reinterpret_cast<uint2*>(&s_tiles[p][(t * (t - 1) / 2 + s) * 256 + lane * 4]) =
-                    make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
-            else
-                *reinterpret_cast<float4*>(&s_xd[p][t * 256 + ln * 16 + 4 * lq]) =
-                    make_float4(xv[0], xv[1], xv[2], xv[3]);
-        }
-    }
-    __syncthreads();
-
-    // ---- 3. diagonal blocks: (I + X_tt)^-1 in fp32 ------------------------
-    {
-        const int blk = tid >> 4, p = blk / NB, t = blk % NB;
-        if (blk < HPW * NB && 16 * t < N) {
-            const float* xd = s_xd[p] + t * 256;
-            float y[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == ln) ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc = fmaf(-xd[i * 16 + m], y[m], acc);
-                y[i] = acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s_dinv[p][t * 256 + frag_pos(i, ln)] = bf16_rne(y[i]);
-        }
-    }
-    __syncthreads();
-
-    // ---- 4. per wave: projection, blocked substitution, output -------------
-    // Register fragments and the layouts they serve (16x16 MFMA tiles):
-    //   sb[cs]      S0 rows r = col0 + l%16, cols 32cs + 8(l/16)..+7: B operand of
-    //               K S0^T and A operand of S0 Q^T;
-    //   k / q frags rows of block t (LDS): A operand of K S0^T, B operand of
-    //               S0 Q^T;
-    //   vfr[t]      v rows of block t, this wave's 16 columns (A operand), moved
-    //               into accumulator layout by an exact product with I;
-    //   uhi / ulo   U_s in accumulator layout (node rows): B operand of X U,
-    //               and, read as U_s^T, A operand of U^T Y^T.
-    // Sums over s run in separate hi / lo accumulators to halve chain depth.
-    bf16x8 sb[4];
-#pragma unroll
-    for (int cs = 0; cs < 4; ++cs) sb[cs] = to_bf16x8(s0raw[cs][0], s0raw[cs][1]);
-    s16x4 ident;
+    s16x4 ident;                                      // I as a 16x16x16 B operand
 #pragma unroll
     for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
 
-    const uint16_t* tiles = s_tiles[hp];
-    const float* lgp = s_lg[hp];
-    const float* bep = s_beta[hp];
-    float* Ug = a.u + ((size_t)b * Hv + h) * (size_t)N * kD;
-    s16x4 uhi[NB], ulo[NB];
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    int item = blockIdx.x;                                    // grid <= nitems
+    load_small(item);
+    kq_dma(item);
 #pragma unroll
-    for (int t = 0; t < NB; ++t) {
-        if (16 * t >= N) break;                             // uniform
-        f32x4 pk = z, pqT = z;
-        const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vfr[t]), ident, z);
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-            pk = mfma32(lds_frag(s_k, t, cs, lane), sb[cs], pk);      // [node][r]
-            pqT = mfma32(sb[cs], lds_frag(s_q, t, cs, lane), pqT);    // [r][node]
+    for (int c = 0; c < 4; ++c) load_s0(item, c);
+
+    for (; item < nitems; item += gridDim.x) {
+        asm volatile("" : "+v"(tid));
+        lane = tid & 63;
+        ln = lane & 15;
+        lq = lane >> 4;
+        const int nxt = item + gridDim.x;
+        const bool more = nxt < nitems;
+        int b, hk, hg;
+        decode(item, b, hk, hg);
+        const int h0 = hk * G + hg * HPW;
+        const int h = h0 + hp;
+        const size_t vo_base = ((size_t)b * N * Hv + h) * kD;     // node 0 of head h
+        lds_barrier();                                        // LDS of the last item is free
+
+        // ---- 1. tree, gates -----------------------------------------------
+        if (tid < N) s_jump[tid] = my_par;        // tree_build_lds reads it after a barrier
+        const int status = tree_build_lds<true>(s_jump, N, W, s_mask, s_jump, &s_flag);
+        if (hk == 0 && hg == 0) {
+            uint32_t* gm = a.anc_mask + (size_t)b * N * W;
+            for (int x = tid; x < N * W; x += NT) gm[x] = s_mask[x];
+            for (int i = tid; i < N; i += NT)
+                a.depth[(size_t)b * N + i] = status ? -1 : row_popc(s_mask + i * W, W);
+            if (tid == 0) a.status[b] = status;
         }
-        // R_t = beta (V - e^G P_K) + sum_{s<t} (-X_ts) U_s
-        f32x4 R, Rh = z, Rl = z;
+        uint16_t* O = static_cast<uint16_t*>(a.o);
+        if (status) {
+            const float qnan = __uint_as_float(0x7fc00000u);
 #pragma unroll
-        for (int s = 0; s < t; ++s) {
-            const s16x4 nx = *reinterpret_cast<const s16x4*>(tiles + (t * (t - 1) / 2 + s) * 256 + lane * 4);
-            Rh = mfma16(nx, uhi[s], Rh);
-            Rl = mfma16(nx, ulo[s], Rl);
-        }
+            for (int p = 0; p < HPW; ++p) {
+                const size_t ob = ((size_t)b * N * Hv + h0 + p) * kD;
+                float* Up = a.u + ((size_t)b * Hv + h0 + p) * (size_t)N * kD;
+                for (int x = tid; x < N * kD; x += NT) {
+                    O[ob + (size_t)(x / kD) * vo_row + x % kD] = 0x7fc0;
+                    Up[x] = qnan;
+                }
+                for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h0 + p) * N + i] = qnan;
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this item's k/q copies landed
+            lds_barrier();
+            const int pf = more ? nxt : item;
+            load_small(pf);
+            if (more) kq_dma(nxt);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int i = 16 * t + 4 * lq + m;
-            R[m] = bep[i] * (vd[m] - __expf(lgp[i]) * pk[m]) + (Rh[m] + Rl[m]);
+            for (int c = 0; c < 4; ++c) load_s0(pf, c);
+            continue;
         }
-        // U_t = (I + X_tt)^-1 R_t, kept as [node][r]; U_t^T = R_t^T Dinv^T is stored
-        const s16x4 di = *reinterpret_cast<const s16x4*>(s_dinv[hp] + t * 256 + lane * 4);
-        const int node = 16 * t + ln;                        // this lane's node in ^T tiles
-        s16x4 rh, rl;
-        split4(R, rh, rl);
-        const f32x4 U = mfma16(di, rl, mfma16(di, rh, z));
-        split4(U, uhi[t], ulo[t]);
-        const f32x4 UT = mfma16(rl, di, mfma16(rh, di, z));
-        if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 4 * lq) = UT;
-        // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T
-        f32x4 Oh = z, Ol = z;
+        if (tid < NP) {
 #pragma unroll
-        for (int s = 0; s <= t; ++s) {
-            const s16x4 yt = *reinterpret_cast<const s16x4*>(tiles + (NX + t * (t + 1) / 2 + s) * 256 + lane * 4);
-            Oh = mfma16(uhi[s], yt, Oh);
-            Ol = mfma16(ulo[s], yt, Ol);
+            for (int p = 0; p < HPW; ++p) {
+                s_lg[p][tid] = tid < N ? logf(my_g[p]) : 0.f;
+                s_beta[p][tid] = tid < N ? my_beta[p] : 0.f;
+            }
         }
-        if (node < N) {
-            const float egn = __expf(lgp[node]);
-            f32x4 OT;
+        lds_barrier();
+        float my_lg[HPW];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[m] + (Oh[m] + Ol[m]);
-            const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
-            const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
-            *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + col0 + 4 * lq) =
-                make_uint2(lo, hi);
+        for (int p = 0; p < HPW; ++p) my_lg[p] = 0.f;
+        if (tid < N) {
+            for (int w = 0; w < W; ++w) {
+                uint32_t x = s_mask[tid * W + w];
+                while (x) {
+                    const int j = w * 32 + __ffs(x) - 1;
+#pragma unroll
+                    for (int p = 0; p < HPW; ++p) my_lg[p] += s_lg[p][j];
+                    x &= x - 1u;
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < HPW; ++p) {
+                my_lg[p] += s_lg[p][tid];
+                a.log_gamma[((size_t)b * Hv + h0 + p) * N + tid] = my_lg[p];
+            }
         }
+        // S0 rows (registers) and the direct-to-LDS k / q rows were issued before
+        // anything still in flight: one wait covers both, the barrier publishes
+        // every wave's copies.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (tid < NP) {
+#pragma unroll
+            for (int p = 0; p < HPW; ++p) s_lg[p][tid] = my_lg[p];
+        }
+        // this item's v rows, needed only after the Gram
+        const uint16_t* V = static_cast<const uint16_t*>(a.v);
+        uint2 vfr[NB];                                // node 16t + l%16, columns col0 + 4(l/16)..+3
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            const int i = 16 * t + ln;
+            vfr[t] = i < N ? *reinterpret_cast<const uint2*>(V + vo_base + (size_t)i * vo_row + col0 + 4 * lq)
+                           : make_uint2(0u, 0u);
+        }
+
+        // this item's S0 rows as bf16 B / A operands (registers for the whole item)
+        bf16x8 sb[4];
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) sb[cs] = to_bf16x8(s0raw[cs][0], s0raw[cs][1]);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        lds_barrier();                                      // s_lg holds G from here
+
+        // ---- 3. Gram tiles -> masked, decayed X / Y tiles per head ----------
+        // Computed transposed, K_s K_t^T and K_s Q_t^T: lane l then holds row
+        // i = 16t + l%16 and columns j = 16s + 4(l/16)..+3, which is exactly its
+        // slot in the A-operand fragment order (8 contiguous bytes per lane).
+        for (int pi = wave; pi < NPAIR; pi += NW) {
+            int t = 0;
+            while ((t + 1) * (t + 2) / 2 <= pi) ++t;
+            const int s = pi - t * (t + 1) / 2;
+            if (t >= nblk) continue;
+            f32x4 A = z, C = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) {
+                const bf16x8 ks = lds_frag(s_k, s, cs, lane);
+                A = mfma32(ks, lds_frag(s_k, t, cs, lane), A);
+                C = mfma32(ks, lds_frag(s_q, t, cs, lane), C);
+            }
+            const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
+            const uint32_t bits = i < N ? (s_mask[i * W + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
+#pragma unroll
+            for (int p = 0; p < HPW; ++p) {
+                const float lgi = s_lg[p][i], bei = s_beta[p][i];
+                const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[p][j0]);
+                const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
+                float xv[4];
+                uint16_t yv[4], nxv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool anc = (bits >> e) & 1u;
+                    const bool self = (j0 + e == i) && i < N;
+                    const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
+                    xv[e] = anc ? bei * d * A[e] : 0.f;
+                    yv[e] = bf16_rne(d * C[e]);
+                    nxv[e] = bf16_rne(-xv[e]);
+                }
+                *reinterpret_cast<uint2*>(&s_tiles[p][(NX + t * (t + 1) / 2 + s) * 256 + lane * 4]) =
+                    make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
+                if (s < t)
+                    *reinterpret_cast<uint2*>(&s_tiles[p][(t * (t - 1) / 2 + s) * 256 + lane * 4]) =
+                        make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
+                else
+                    *reinterpret_cast<float4*>(&s_xd[p][t * 256 + ln * 16 + 4 * lq]) =
+                        make_float4(xv[0], xv[1], xv[2], xv[3]);
+            }
+        }
+        lds_barrier();
+
+        // ---- 4. diagonal blocks: (I + X_tt)^-1 in fp32 ----------------------
+        {
+            const int blk = tid >> 4, p = blk / NB, t = blk % NB;
+            if (blk < HPW * NB && t < nblk) {
+                const float* xd = s_xd[p] + t * 256;
+                float y[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float acc = (i == ln) ? 1.f : 0.f;
+#pragma unroll
+                    for (int m = 0; m < i; ++m) acc = fmaf(-xd[i * 16 + m], y[m], acc);
+                    y[i] = acc;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s_dinv[p][t * 256 + frag_pos(i, ln)] = bf16_rne(y[i]);
+            }
+        }
+        lds_barrier();
+
+        // ---- 5. per wave: projection, blocked substitution, output ---------
+        //   sb[cs]      S0 rows r = col0 + l%16: B operand of K S0^T, A operand of
+        //               S0 Q^T;  k / q frags of block t (LDS): A / B operands;
+        //   vfr[t]      v rows of block t, this wave's 16 columns (A operand), moved
+        //               into accumulator layout by an exact product with I;
+        //   uhi[s]      U_s rounded to bf16, accumulator layout (node rows): B
+        //               operand of X U and, read as U_s^T, A operand of U^T Y^T.
+        //               U itself (stored to the cache) stays fp32: it comes from
+        //               R_t split into bf16 hi + lo against (I + X_tt)^-1.
+        const uint16_t* tiles = s_tiles[hp];
+        const float* lgp = s_lg[hp];
+        const float* bep = s_beta[hp];
+        float* Ug = a.u + ((size_t)b * Hv + h) * (size_t)N * kD;
+        s16x4 uhi[NB];
+        // the next item's parent / g / beta, ahead of this solve's output stores
+        // (loads and stores retire in order: issued after them, the next tree
+        // build would wait for every store)
+        const int pf = more ? nxt : item;                     // (the last item re-reads itself)
+        load_small(pf);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            if (t >= nblk) continue;                          // uniform
+            f32x4 pk = z, pqT = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) {
+                pk = mfma32(lds_frag(s_k, t, cs, lane), sb[cs], pk);      // [node][r]
+                pqT = mfma32(sb[cs], lds_frag(s_q, t, cs, lane), pqT);    // [r][node]
+            }
+            const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vfr[t]), ident, z);
+            f32x4 R, Ra = z, Rb = z;                          // two chains: even / odd s
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int i = 16 * t + 4 * lq + m;
+                R[m] = bep[i] * (vd[m] - __expf(lgp[i]) * pk[m]);
+            }
+            // R_t += sum_{s<t} (-X_ts) U_s
+#pragma unroll
+            for (int s = 0; s < t; ++s) {
+                const s16x4 nx = *reinterpret_cast<const s16x4*>(tiles + (t * (t - 1) / 2 + s) * 256 + lane * 4);
+                if (s & 1) Rb = mfma16(nx, uhi[s], Rb);
+                else Ra = mfma16(nx, uhi[s], Ra);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) R[m] += Ra[m] + Rb[m];
+            // U_t = (I + X_tt)^-1 R_t, kept as [node][r]; U_t^T = R_t^T Dinv^T is stored
+            const s16x4 di = *reinterpret_cast<const s16x4*>(s_dinv[hp] + t * 256 + lane * 4);
+            const int node = 16 * t + ln;                     // this lane's node in ^T tiles
+            s16x4 rh, rl;
+            split4(R, rh, rl);
+            const f32x4 U = mfma16(di, rl, mfma16(di, rh, z));
+            uhi[t] = to_bf16x4(U);
+            const f32x4 UT = mfma16(rl, di, mfma16(rh, di, z));
+            if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 4 * lq) = UT;
+            // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T
+            f32x4 Oa = z, Ob = z;
+#pragma unroll
+            for (int s = 0; s <= t; ++s) {
+                const s16x4 yt = *reinterpret_cast<const s16x4*>(tiles + (NX + t * (t + 1) / 2 + s) * 256 + lane * 4);
+                if (s & 1) Ob = mfma16(uhi[s], yt, Ob);
+                else Oa = mfma16(uhi[s], yt, Oa);
+            }
+            if (node < N) {
+                const float egn = __expf(lgp[node]);
+                f32x4 OT;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[m] + (Oa[m] + Ob[m]);
+                const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
+                const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
+                *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + col0 + 4 * lq) =
+                    make_uint2(lo, hi);
+            }
+        }
+        lds_barrier();                                      // k / q in LDS are free now
+        if (more) kq_dma(nxt);                                // the next item's k / q and S0
+#pragma unroll
+        for (int c = 0; c < 4; ++c) load_s0(pf, c);
     }
 }
 
@@ -425,10 +504,16 @@ hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream) 
         fn = hpw == 2 ? (const void*)verify_tiled_kernel<4, 2> : (const void*)verify_tiled_kernel<4, 1>;
     else
         fn = hpw == 2 ? (const void*)verify_tiled_kernel<8, 2> : (const void*)verify_tiled_kernel<8, 1>;
+    int nitems = a.B * a.Hk * (G / hpw);
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)(nitems < cus ? nitems : cus);
     VerifyArgs copy = a;
-    void* args[] = {&copy};
-    const unsigned groups = (unsigned)(a.B * a.Hk * (G / hpw));
-    return hipLaunchKernel(fn, dim3(groups), dim3(512 * hpw), args, 0, stream);
+    void* args[] = {&copy, &nitems};
+    return hipLaunchKernel(fn, dim3(grid), dim3(512 * hpw), args, 0, stream);
 }
 
 }  // namespace gdn
