@@ -154,6 +154,8 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     constexpr int NPAIR = NB * (NB + 1) / 2;    // Gram tiles (s <= t)
     constexpr int MW = NP / 32 > 0 ? NP / 32 : 1;
     constexpr int KQ_INS = 2 * NP / 4;          // 1 KB direct-to-LDS loads for k and q
+    constexpr int NPL = NP / 64;                // nodes per lane of the tree wave
+    static_assert(NPL >= 1 && NW >= 1 + NPL, "tree wave plus beta waves");
     __shared__ __attribute__((aligned(16))) uint16_t s_k[NP * kD];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[NP * kD];
     __shared__ __attribute__((aligned(16))) uint16_t s_tiles[HPW][NB * NB * 256];  // -X then Y
@@ -188,22 +190,29 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     };
 
     // ---- prefetch helpers (registers / LDS written by loads in flight) ----
-    int my_par = 0;
-    float my_g[HPW], my_beta[HPW];
-    // Prefetches into registers are unconditional (clamped indices): a load
-    // under a branch would leave a control-flow merge that copies its result,
-    // and the copy would wait for every older load and store of the wave.
+    // Per item, wave 0 needs parent and g of nodes lane + 64k (k < NPL), and the
+    // threads 64 .. 64 + NP - 1 need beta of node tid - 64; every thread issues
+    // the same number of loads into the same registers (addresses chosen per
+    // wave, indices clamped), so no load sits under a branch: a load under a
+    // branch would leave a control-flow merge that copies its result, and the
+    // copy would wait for every older load and store of the wave.
+    constexpr int NSM = NPL * (1 + HPW);
+    uint32_t sm[NSM];
     auto load_small = [&](int it) {
         int b, hk, hg;
         decode(it, b, hk, hg);
         const int h0 = hk * G + hg * HPW;
-        const int ii = tid < N ? tid : 0;              // rows past N are never used
-        my_par = a.parent[(size_t)b * N + ii];
+        const uint32_t* par = reinterpret_cast<const uint32_t*>(a.parent) + (size_t)b * N;
+        const uint32_t* gg = reinterpret_cast<const uint32_t*>(wave == 0 ? a.g : a.beta) +
+                             (size_t)b * N * Hv + h0;
+        const int nb = min(max(tid - 64, 0), N - 1);
 #pragma unroll
-        for (int p = 0; p < HPW; ++p) {
-            const size_t bg = ((size_t)b * N + ii) * Hv + h0 + p;
-            my_g[p] = a.g[bg];
-            my_beta[p] = a.beta[bg];
+        for (int k = 0; k < NPL; ++k) {
+            const int i = min(lane + 64 * k, N - 1);
+            sm[k] = par[i];
+#pragma unroll
+            for (int p = 0; p < HPW; ++p)
+                sm[NPL + k * HPW + p] = gg[(size_t)(wave == 0 ? i : nb) * Hv + p];
         }
     };
     // k and q rows of the item's tree into s_k / s_q: each wave instruction
@@ -236,6 +245,113 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         s0raw[c][1] = *reinterpret_cast<const float4*>(p + 4);
     };
 
+    // The item's tree, built by wave 0 alone, with no workgroup barrier, by
+    // synchronous pointer doubling.  Lane l owns nodes l + 64k.  Node i keeps a
+    // covered set C_i (itself and its nearest ancestors, a bit row), the sums of
+    // ln g over C_i for each value head, and nx_i, its nearest ancestor outside
+    // C_i (-1 once C_i reaches the root).  A round adds C_(nx_i) and its sums
+    // and moves nx_i to nx_(nx_i); all lanes finish reading before any lane
+    // writes, so a round sees only the previous round's values and C_i doubles:
+    // ceil(log2(depth)) + 1 rounds.  Then C_i is i with all its ancestors and
+    // the sums are the path log-gates G_i.  Leaves the strict-ancestor rows in
+    // s_mask (row stride MW), G in s_lg and the tree status in s_flag.
+    auto tree_wave = [&]() {
+        int status = 0;
+#pragma unroll
+        for (int k = NPL - 1; k >= 0; --k) {                // lowest bad node wins
+            const int i = lane + 64 * k, pi = (int)sm[k];
+            const uint64_t bad = __ballot(i < N && (pi < -1 || pi >= i));
+            if (bad) status = 64 * k + __ffsll((unsigned long long)bad);
+        }
+        int nx[NPL];
+        uint32_t m[NPL][MW];
+        float gv[NPL][HPW];
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+            const int i = lane + 64 * k;
+            const bool valid = i < N && status == 0;
+            nx[k] = valid ? (int)sm[k] : -1;
+#pragma unroll
+            for (int w = 0; w < MW; ++w) m[k][w] = (valid && (i >> 5) == w) ? 1u << (i & 31) : 0u;
+#pragma unroll
+            for (int p = 0; p < HPW; ++p)
+                gv[k][p] = valid ? logf(__uint_as_float(sm[NPL + k * HPW + p])) : 0.f;
+            s_jump[i] = nx[k];
+#pragma unroll
+            for (int w = 0; w < MW; ++w) s_mask[i * MW + w] = m[k][w];
+#pragma unroll
+            for (int p = 0; p < HPW; ++p) s_lg[p][i] = gv[k][p];
+        }
+        for (;;) {
+            bool act = false;
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) act |= nx[k] >= 0;
+            if (!__any(act)) break;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // last round's writes done
+            int nn[NPL];
+            uint32_t mj[NPL][MW];
+            float gj[NPL][HPW];
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) {
+                const int j = nx[k] >= 0 ? nx[k] : lane + 64 * k;
+                nn[k] = s_jump[j];
+#pragma unroll
+                for (int w = 0; w < MW; ++w) mj[k][w] = s_mask[j * MW + w];
+#pragma unroll
+                for (int p = 0; p < HPW; ++p) gj[k][p] = s_lg[p][j];
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // every read done
+#pragma unroll
+            for (int k = 0; k < NPL; ++k) {
+                const int i = lane + 64 * k;
+                if (nx[k] >= 0) {
+#pragma unroll
+                    for (int w = 0; w < MW; ++w) m[k][w] |= mj[k][w];
+#pragma unroll
+                    for (int p = 0; p < HPW; ++p) gv[k][p] += gj[k][p];
+                    nx[k] = nn[k];
+                }
+                s_jump[i] = nx[k];
+#pragma unroll
+                for (int w = 0; w < MW; ++w) s_mask[i * MW + w] = m[k][w];
+#pragma unroll
+                for (int p = 0; p < HPW; ++p) s_lg[p][i] = gv[k][p];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {                     // strict-ancestor rows
+            const int i = lane + 64 * k;
+#pragma unroll
+            for (int w = 0; w < MW; ++w)
+                s_mask[i * MW + w] = (i >> 5) == w ? m[k][w] & ~(1u << (i & 31)) : m[k][w];
+        }
+        if (lane == 0) s_flag = status;
+    };
+    // The tree part of the cache, from LDS once the tree is published: ancestor
+    // rows, depth and status (one head group per sequence writes them) and the
+    // path log-gates of this item's value heads.
+    auto write_tree_cache = [&](int b, int h0, bool writer, int status) {
+        uint32_t* gm = a.anc_mask + (size_t)b * N * W;
+        for (int i = lane; i < N; i += 64) {
+            if (writer) {
+                int cnt = 0;
+#pragma unroll
+                for (int w = 0; w < MW; ++w) {
+                    const uint32_t x = s_mask[i * MW + w];
+                    if (w < W) gm[(size_t)i * W + w] = x;
+                    cnt += __popc(x);
+                }
+                a.depth[(size_t)b * N + i] = status ? -1 : cnt;
+            }
+            if (status == 0) {
+#pragma unroll
+                for (int p = 0; p < HPW; ++p)
+                    a.log_gamma[((size_t)b * Hv + h0 + p) * N + i] = s_lg[p][i];
+            }
+        }
+        if (writer && lane == 0) a.status[b] = status;
+    };
+
     s16x4 ident;                                      // I as a 16x16x16 B operand
 #pragma unroll
     for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
@@ -260,16 +376,22 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         const size_t vo_base = ((size_t)b * N * Hv + h) * kD;     // node 0 of head h
         lds_barrier();                                        // LDS of the last item is free
 
-        // ---- 1. tree, gates -----------------------------------------------
-        if (tid < N) s_jump[tid] = my_par;        // tree_build_lds reads it after a barrier
-        const int status = tree_build_lds<true>(s_jump, N, W, s_mask, s_jump, &s_flag);
-        if (hk == 0 && hg == 0) {
-            uint32_t* gm = a.anc_mask + (size_t)b * N * W;
-            for (int x = tid; x < N * W; x += NT) gm[x] = s_mask[x];
-            for (int i = tid; i < N; i += NT)
-                a.depth[(size_t)b * N + i] = status ? -1 : row_popc(s_mask + i * W, W);
-            if (tid == 0) a.status[b] = status;
+        // ---- 1. tree and path log-gates (wave 0), beta (waves 1 ..) ---------
+        if (wave == 0) {
+            tree_wave();
+        } else if (tid < 64 + NP) {
+            const int i = tid - 64;
+#pragma unroll
+            for (int p = 0; p < HPW; ++p)
+                s_beta[p][i] = i < N ? __uint_as_float(sm[NPL + p]) : 0.f;
         }
+        // S0 rows (registers) and the direct-to-LDS k / q rows were issued before
+        // anything still in flight: one wait covers both, the barrier publishes
+        // every wave's copies and the tree.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        const int status = s_flag;
+        if (wave == NW - 1) write_tree_cache(b, h0, hk == 0 && hg == 0, status);
         uint16_t* O = static_cast<uint16_t*>(a.o);
         if (status) {
             const float qnan = __uint_as_float(0x7fc00000u);
@@ -283,50 +405,12 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
                 }
                 for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h0 + p) * N + i] = qnan;
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this item's k/q copies landed
-            lds_barrier();
             const int pf = more ? nxt : item;
             load_small(pf);
             if (more) kq_dma(nxt);
 #pragma unroll
             for (int c = 0; c < 4; ++c) load_s0(pf, c);
             continue;
-        }
-        if (tid < NP) {
-#pragma unroll
-            for (int p = 0; p < HPW; ++p) {
-                s_lg[p][tid] = tid < N ? logf(my_g[p]) : 0.f;
-                s_beta[p][tid] = tid < N ? my_beta[p] : 0.f;
-            }
-        }
-        lds_barrier();
-        float my_lg[HPW];
-#pragma unroll
-        for (int p = 0; p < HPW; ++p) my_lg[p] = 0.f;
-        if (tid < N) {
-            for (int w = 0; w < W; ++w) {
-                uint32_t x = s_mask[tid * W + w];
-                while (x) {
-                    const int j = w * 32 + __ffs(x) - 1;
-#pragma unroll
-                    for (int p = 0; p < HPW; ++p) my_lg[p] += s_lg[p][j];
-                    x &= x - 1u;
-                }
-            }
-#pragma unroll
-            for (int p = 0; p < HPW; ++p) {
-                my_lg[p] += s_lg[p][tid];
-                a.log_gamma[((size_t)b * Hv + h0 + p) * N + tid] = my_lg[p];
-            }
-        }
-        // S0 rows (registers) and the direct-to-LDS k / q rows were issued before
-        // anything still in flight: one wait covers both, the barrier publishes
-        // every wave's copies.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();
-        if (tid < NP) {
-#pragma unroll
-            for (int p = 0; p < HPW; ++p) s_lg[p][tid] = my_lg[p];
         }
         // this item's v rows, needed only after the Gram
         const uint16_t* V = static_cast<const uint16_t*>(a.v);
@@ -343,7 +427,6 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 #pragma unroll
         for (int cs = 0; cs < 4; ++cs) sb[cs] = to_bf16x8(s0raw[cs][0], s0raw[cs][1]);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        lds_barrier();                                      // s_lg holds G from here
 
         // ---- 3. Gram tiles -> masked, decayed X / Y tiles per head ----------
         // Computed transposed, K_s K_t^T and K_s Q_t^T: lane l then holds row
@@ -362,7 +445,7 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
                 C = mfma32(ks, lds_frag(s_q, t, cs, lane), C);
             }
             const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
-            const uint32_t bits = i < N ? (s_mask[i * W + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
+            const uint32_t bits = i < N ? (s_mask[i * MW + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
 #pragma unroll
             for (int p = 0; p < HPW; ++p) {
                 const float lgi = s_lg[p][i], bei = s_beta[p][i];
