@@ -100,6 +100,23 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wait until every global load and store of this wave has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).  Issued through
+// the builtin rather than inline asm so that the compiler's own wait
+// insertion knows the loads are done, in particular the direct-to-LDS loads,
+// which it otherwise waits for again before later LDS reads.
+__device__ __forceinline__ void wait_vmem_all() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Wait until at most n global loads / stores of this wave are in flight
+// (they retire in issue order): a compile-time n, encoded for gfx9 s_waitcnt.
+template <int n>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
 // Validate one tree's parent row and build its strict-ancestor bit rows in LDS
 // (the ancestor relation behind the interaction matrices X and Y).
 //

@@ -138,15 +138,23 @@ typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Persistent workgroups, one per CU, each looping over (sequence, key head,
-// head group) work items.  As soon as item n's solve is done, item n+1's inputs
-// are requested, oldest first in the order they are needed: parent / g / beta
-// and S0 rows into registers, k / q rows straight from HBM into LDS
-// (global_load_lds); its v rows follow once those have landed and are used only
-// after its Gram.  Their latency overlaps item n+1's tree build, and the solve
-// itself never waits on a load queued behind a prefetch (loads retire in order).
+// head group) work items with the next item's inputs in flight:
+//  - at the start of item n's solve (before its output stores, since loads
+//    and stores retire in order): item n+1's parent / g / beta words and S0
+//    rows into registers;
+//  - once item n's solve is done with k / q: item n+1's k / q rows straight
+//    from HBM into LDS (global_load_lds);
+//  - item n+1's v rows after its tree, used only after its Gram.
+// One explicit wait per item (its k / q / S0 landed) before the Gram, one
+// (its v landed) before the solve; the solve itself never waits on memory.
+//
+// Waves: four per value head; wave (hp, wc) owns value columns 32 wc .. +31 of
+// head h0 + hp as two 16-column groups, so every k / q / tile fragment it
+// reads from LDS feeds two MFMA chains.
 template <int NB, int HPW>
-__global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a, int nitems) {
-    constexpr int WPH = 8;                      // waves per value head, 16 columns each
+__global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a, int nitems) {
+    constexpr int WPH = 4;                      // waves per value head
+    constexpr int CG = 2;                       // 16-column groups per wave
     constexpr int NW = WPH * HPW;               // waves
     constexpr int NT = 64 * NW;                 // threads
     constexpr int NP = 16 * NB;                 // padded node count
@@ -155,7 +163,8 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     constexpr int MW = NP / 32 > 0 ? NP / 32 : 1;
     constexpr int KQ_INS = 2 * NP / 4;          // 1 KB direct-to-LDS loads for k and q
     constexpr int NPL = NP / 64;                // nodes per lane of the tree wave
-    static_assert(NPL >= 1 && NW >= 1 + NPL, "tree wave plus beta waves");
+    static_assert(NPL >= 1 && NT >= 64 + NP, "tree wave plus beta threads");
+    static_assert(KQ_INS % NW == 0, "whole direct-to-LDS loads per wave");
     __shared__ __attribute__((aligned(16))) uint16_t s_k[NP * kD];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[NP * kD];
     __shared__ __attribute__((aligned(16))) uint16_t s_tiles[HPW][NB * NB * 256];  // -X then Y
@@ -171,8 +180,8 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     const int W = (N + 31) / 32;
     const int nblk = (N + 15) / 16;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int hp = wave / WPH, wc = wave % WPH;       // this wave: head h0+hp, cols 16wc..
-    const int col0 = 16 * wc;
+    const int hp = wave / WPH, wc = wave % WPH;       // this wave: head h0+hp, cols 32wc..
+    const int col0 = 32 * wc;
     const size_t vo_row = (size_t)Hv * kD;            // stride between nodes in v / o
     // Thread index, re-read through an empty asm at every item so that the many
     // thread-derived LDS / global addresses are recomputed per item instead of
@@ -224,7 +233,9 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         decode(it, b, hk, hg);
         const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
         const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + ((size_t)b * N * Hk + hk) * kD;
-        for (int ins = wave; ins < KQ_INS; ins += NW) {
+#pragma unroll
+        for (int kk = 0; kk < KQ_INS / NW; ++kk) {      // compile-time count: a loop of
+            const int ins = wave + kk * NW;            // loads would get a full wait ahead
             const int mat = ins / (NP / 4), r0 = (ins % (NP / 4)) * 4;
             const int row = r0 + (lane >> 4), pc = lane & 15;
             const int srow = row < N ? row : N - 1;
@@ -233,16 +244,19 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
             __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
         }
     };
-    float4 s0raw[4][2];
-    // chunk c of this wave's S0 rows (col0 + l%16): key columns 32c + 8(l/16)..+7
-    auto load_s0 = [&](int it, int c) {
+    float4 s0raw[CG][4][2];
+    // this wave's S0 rows of column group g (col0 + 16g + l%16), key columns
+    // 32c + 8(l/16)..+7
+    auto load_s0 = [&](int it, int g) {
         int b, hk, hg;
         decode(it, b, hk, hg);
         const int h = hk * G + hg * HPW + hp;
-        const float* p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(col0 + ln) * kD +
-                         32 * c + 8 * lq;
-        s0raw[c][0] = *reinterpret_cast<const float4*>(p);
-        s0raw[c][1] = *reinterpret_cast<const float4*>(p + 4);
+        const float* p0 = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(col0 + 16 * g + ln) * kD + 8 * lq;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            s0raw[g][c][0] = *reinterpret_cast<const float4*>(p0 + 32 * c);
+            s0raw[g][c][1] = *reinterpret_cast<const float4*>(p0 + 32 * c + 4);
+        }
     };
 
     // The item's tree, built by wave 0 alone, with no workgroup barrier, by
@@ -360,7 +374,7 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     load_small(item);
     kq_dma(item);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) load_s0(item, c);
+    for (int g = 0; g < CG; ++g) load_s0(item, g);
 
     for (; item < nitems; item += gridDim.x) {
         asm volatile("" : "+v"(tid));
@@ -369,6 +383,7 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         lq = lane >> 4;
         const int nxt = item + gridDim.x;
         const bool more = nxt < nitems;
+        const int pf = more ? nxt : item;                     // (the last item re-reads itself)
         int b, hk, hg;
         decode(item, b, hk, hg);
         const int h0 = hk * G + hg * HPW;
@@ -376,7 +391,7 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         const size_t vo_base = ((size_t)b * N * Hv + h) * kD;     // node 0 of head h
         lds_barrier();                                        // LDS of the last item is free
 
-        // ---- 1. tree and path log-gates (wave 0), beta (waves 1 ..) ---------
+        // ---- 1. tree and path log-gates (wave 0), beta (threads 64 ..) -------
         if (wave == 0) {
             tree_wave();
         } else if (tid < 64 + NP) {
@@ -388,12 +403,24 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         // S0 rows (registers) and the direct-to-LDS k / q rows were issued before
         // anything still in flight: one wait covers both, the barrier publishes
         // every wave's copies and the tree.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vmem_all();
         lds_barrier();
-        const int status = s_flag;
-        if (wave == NW - 1) write_tree_cache(b, h0, hk == 0 && hg == 0, status);
+        const int status = __builtin_amdgcn_readfirstlane(s_flag);   // uniform branch below
         uint16_t* O = static_cast<uint16_t*>(a.o);
-        if (status) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        uint2 vfr[CG][NB];                            // node 16t + l%16, columns col0 + 16g + 4(l/16)..+3
+        // this item's S0 rows as bf16 B / A operands (registers for the whole item)
+        // (pinned here by an empty asm: sunk to its uses in the solve, the
+        // conversion would keep s0raw alive under the next item's prefetch)
+        bf16x8 sb[CG][4];
+#pragma unroll
+        for (int g = 0; g < CG; ++g)
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) {
+                sb[g][cs] = to_bf16x8(s0raw[g][cs][0], s0raw[g][cs][1]);
+                asm volatile("" : "+v"(sb[g][cs]));
+            }
+        if (status) {                                 // invalid tree: NaN outputs, no solve
             const float qnan = __uint_as_float(0x7fc00000u);
 #pragma unroll
             for (int p = 0; p < HPW; ++p) {
@@ -405,100 +432,101 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
                 }
                 for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h0 + p) * N + i] = qnan;
             }
-            const int pf = more ? nxt : item;
-            load_small(pf);
-            if (more) kq_dma(nxt);
+        } else {
+            // this item's v rows, needed only in the solve (unconditional: rows
+            // past N re-read row N - 1, and beta = 0 there)
+            const uint16_t* V = static_cast<const uint16_t*>(a.v);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) load_s0(pf, c);
-            continue;
-        }
-        // this item's v rows, needed only after the Gram
-        const uint16_t* V = static_cast<const uint16_t*>(a.v);
-        uint2 vfr[NB];                                // node 16t + l%16, columns col0 + 4(l/16)..+3
+            for (int t = 0; t < NB; ++t) {
+                const int i = min(16 * t + ln, N - 1);
 #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            const int i = 16 * t + ln;
-            vfr[t] = i < N ? *reinterpret_cast<const uint2*>(V + vo_base + (size_t)i * vo_row + col0 + 4 * lq)
-                           : make_uint2(0u, 0u);
-        }
-
-        // this item's S0 rows as bf16 B / A operands (registers for the whole item)
-        bf16x8 sb[4];
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) sb[cs] = to_bf16x8(s0raw[cs][0], s0raw[cs][1]);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-
-        // ---- 3. Gram tiles -> masked, decayed X / Y tiles per head ----------
-        // Computed transposed, K_s K_t^T and K_s Q_t^T: lane l then holds row
-        // i = 16t + l%16 and columns j = 16s + 4(l/16)..+3, which is exactly its
-        // slot in the A-operand fragment order (8 contiguous bytes per lane).
-        for (int pi = wave; pi < NPAIR; pi += NW) {
-            int t = 0;
-            while ((t + 1) * (t + 2) / 2 <= pi) ++t;
-            const int s = pi - t * (t + 1) / 2;
-            if (t >= nblk) continue;
-            f32x4 A = z, C = z;
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs) {
-                const bf16x8 ks = lds_frag(s_k, s, cs, lane);
-                A = mfma32(ks, lds_frag(s_k, t, cs, lane), A);
-                C = mfma32(ks, lds_frag(s_q, t, cs, lane), C);
+                for (int g = 0; g < CG; ++g)
+                    vfr[g][t] = *reinterpret_cast<const uint2*>(V + vo_base + (size_t)i * vo_row + col0 + 16 * g + 4 * lq);
             }
-            const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
-            const uint32_t bits = i < N ? (s_mask[i * MW + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
+            // ---- 3. Gram tiles -> masked, decayed X / Y tiles per head ----------
+            // Computed transposed, K_s K_t^T and K_s Q_t^T: lane l then holds row
+            // i = 16t + l%16 and columns j = 16s + 4(l/16)..+3, which is exactly its
+            // slot in the A-operand fragment order (8 contiguous bytes per lane).
+            for (int pi = wave; pi < NPAIR; pi += NW) {
+                int t = 0;
+                while ((t + 1) * (t + 2) / 2 <= pi) ++t;
+                const int s = pi - t * (t + 1) / 2;
+                if (t >= nblk) continue;
+                f32x4 A = z, C = z;
 #pragma unroll
-            for (int p = 0; p < HPW; ++p) {
-                const float lgi = s_lg[p][i], bei = s_beta[p][i];
-                const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[p][j0]);
-                const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
-                float xv[4];
-                uint16_t yv[4], nxv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool anc = (bits >> e) & 1u;
-                    const bool self = (j0 + e == i) && i < N;
-                    const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
-                    xv[e] = anc ? bei * d * A[e] : 0.f;
-                    yv[e] = bf16_rne(d * C[e]);
-                    nxv[e] = bf16_rne(-xv[e]);
+                for (int cs = 0; cs < 4; ++cs) {
+                    const bf16x8 ks = lds_frag(s_k, s, cs, lane);
+                    A = mfma32(ks, lds_frag(s_k, t, cs, lane), A);
+                    C = mfma32(ks, lds_frag(s_q, t, cs, lane), C);
                 }
-                *reinterpret_cast<uint2*>(&s_tiles[p][(NX + t * (t + 1) / 2 + s) * 256 + lane * 4]) =
-                    make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
-                if (s < t)
-                    *reinterpret_cast<uint2*>(&s_tiles[p][(t * (t - 1) / 2 + s) * 256 + lane * 4]) =
-                        make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
-                else
-                    *reinterpret_cast<float4*>(&s_xd[p][t * 256 + ln * 16 + 4 * lq]) =
-                        make_float4(xv[0], xv[1], xv[2], xv[3]);
-            }
-        }
-        lds_barrier();
-
-        // ---- 4. diagonal blocks: (I + X_tt)^-1 in fp32 ----------------------
-        {
-            const int blk = tid >> 4, p = blk / NB, t = blk % NB;
-            if (blk < HPW * NB && t < nblk) {
-                const float* xd = s_xd[p] + t * 256;
-                float y[16];
+                const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
+                const uint32_t bits = i < N ? (s_mask[i * MW + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float acc = (i == ln) ? 1.f : 0.f;
+                for (int p = 0; p < HPW; ++p) {
+                    const float lgi = s_lg[p][i], bei = s_beta[p][i];
+                    const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[p][j0]);
+                    const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
+                    float xv[4];
+                    uint16_t yv[4], nxv[4];
 #pragma unroll
-                    for (int m = 0; m < i; ++m) acc = fmaf(-xd[i * 16 + m], y[m], acc);
-                    y[i] = acc;
+                    for (int e = 0; e < 4; ++e) {
+                        const bool anc = (bits >> e) & 1u;
+                        const bool self = (j0 + e == i) && i < N;
+                        const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
+                        xv[e] = anc ? bei * d * A[e] : 0.f;
+                        yv[e] = bf16_rne(d * C[e]);
+                        nxv[e] = bf16_rne(-xv[e]);
+                    }
+                    *reinterpret_cast<uint2*>(&s_tiles[p][(NX + t * (t + 1) / 2 + s) * 256 + lane * 4]) =
+                        make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
+                    if (s < t)
+                        *reinterpret_cast<uint2*>(&s_tiles[p][(t * (t - 1) / 2 + s) * 256 + lane * 4]) =
+                            make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
+                    else
+                        *reinterpret_cast<float4*>(&s_xd[p][t * 256 + ln * 16 + 4 * lq]) =
+                            make_float4(xv[0], xv[1], xv[2], xv[3]);
                 }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s_dinv[p][t * 256 + frag_pos(i, ln)] = bf16_rne(y[i]);
             }
-        }
-        lds_barrier();
+            lds_barrier();
 
+        }
+        // s0raw is free: the next item's parent / g / beta and S0 rows load
+        // during the inversion, ahead of the solve's output stores (loads and
+        // stores retire in order).  One program point for both paths, so no
+        // register copy of a load in flight is needed where they meet.
+        load_small(pf);
+#pragma unroll
+        for (int g = 0; g < CG; ++g) load_s0(pf, g);
+        if (!status) {
+            // ---- 4. diagonal blocks: (I + X_tt)^-1 in fp32 ----------------------
+            for (int blk = tid >> 4; blk < HPW * NB; blk += NT / 16) {
+                const int p = blk / NB, t = blk % NB;
+                if (t < nblk) {
+                    const float* xd = s_xd[p] + t * 256;
+                    float y[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float acc = (i == ln) ? 1.f : 0.f;
+#pragma unroll
+                        for (int m = 0; m < i; ++m) acc = fmaf(-xd[i * 16 + m], y[m], acc);
+                        y[i] = acc;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s_dinv[p][t * 256 + frag_pos(i, ln)] = bf16_rne(y[i]);
+                }
+            }
+            lds_barrier();
+        }
+        // v landed: only the 8 * CG S0 loads issued last may still be in flight
+        // (the explicit count lets them overlap the solve).
+        wait_vmem_le<8 * CG>();
+        if (wave == NW - 1) write_tree_cache(b, h0, hk == 0 && hg == 0, status);
         // ---- 5. per wave: projection, blocked substitution, output ---------
-        //   sb[cs]      S0 rows r = col0 + l%16: B operand of K S0^T, A operand of
-        //               S0 Q^T;  k / q frags of block t (LDS): A / B operands;
-        //   vfr[t]      v rows of block t, this wave's 16 columns (A operand), moved
-        //               into accumulator layout by an exact product with I;
-        //   uhi[s]      U_s rounded to bf16, accumulator layout (node rows): B
+        //   sb[g][cs]   S0 rows r = col0 + 16g + l%16: B operand of K S0^T, A
+        //               operand of S0 Q^T;  k / q frags of block t (LDS): A / B;
+        //   vfr[g][t]   v rows of block t (A operand), moved into accumulator
+        //               layout by an exact product with I;
+        //   uhi[g][s]   U_s rounded to bf16, accumulator layout (node rows): B
         //               operand of X U and, read as U_s^T, A operand of U^T Y^T.
         //               U itself (stored to the cache) stays fp32: it comes from
         //               R_t split into bf16 hi + lo against (I + X_tt)^-1.
@@ -506,69 +534,78 @@ __global__ __launch_bounds__(512 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         const float* lgp = s_lg[hp];
         const float* bep = s_beta[hp];
         float* Ug = a.u + ((size_t)b * Hv + h) * (size_t)N * kD;
-        s16x4 uhi[NB];
-        // the next item's parent / g / beta, ahead of this solve's output stores
-        // (loads and stores retire in order: issued after them, the next tree
-        // build would wait for every store)
-        const int pf = more ? nxt : item;                     // (the last item re-reads itself)
-        load_small(pf);
+        s16x4 uhi[CG][NB];
+        const int nsolve = status ? 0 : nblk;
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
-            if (t >= nblk) continue;                          // uniform
-            f32x4 pk = z, pqT = z;
+            if (t >= nsolve) continue;                        // uniform
+            f32x4 pk[CG], pqT[CG];
+#pragma unroll
+            for (int g = 0; g < CG; ++g) pk[g] = pqT[g] = z;
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) {
-                pk = mfma32(lds_frag(s_k, t, cs, lane), sb[cs], pk);      // [node][r]
-                pqT = mfma32(sb[cs], lds_frag(s_q, t, cs, lane), pqT);    // [r][node]
-            }
-            const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vfr[t]), ident, z);
-            f32x4 R, Ra = z, Rb = z;                          // two chains: even / odd s
+                const bf16x8 kf = lds_frag(s_k, t, cs, lane), qf = lds_frag(s_q, t, cs, lane);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int i = 16 * t + 4 * lq + m;
-                R[m] = bep[i] * (vd[m] - __expf(lgp[i]) * pk[m]);
+                for (int g = 0; g < CG; ++g) {
+                    pk[g] = mfma32(kf, sb[g][cs], pk[g]);           // [node][r]
+                    pqT[g] = mfma32(sb[g][cs], qf, pqT[g]);         // [r][node]
+                }
+            }
+            f32x4 R[CG];
+#pragma unroll
+            for (int g = 0; g < CG; ++g) {
+                const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vfr[g][t]), ident, z);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int i = 16 * t + 4 * lq + m;
+                    R[g][m] = bep[i] * (vd[m] - __expf(lgp[i]) * pk[g][m]);
+                }
             }
             // R_t += sum_{s<t} (-X_ts) U_s
 #pragma unroll
             for (int s = 0; s < t; ++s) {
                 const s16x4 nx = *reinterpret_cast<const s16x4*>(tiles + (t * (t - 1) / 2 + s) * 256 + lane * 4);
-                if (s & 1) Rb = mfma16(nx, uhi[s], Rb);
-                else Ra = mfma16(nx, uhi[s], Ra);
-            }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) R[m] += Ra[m] + Rb[m];
+                for (int g = 0; g < CG; ++g) R[g] = mfma16(nx, uhi[g][s], R[g]);
+            }
             // U_t = (I + X_tt)^-1 R_t, kept as [node][r]; U_t^T = R_t^T Dinv^T is stored
             const s16x4 di = *reinterpret_cast<const s16x4*>(s_dinv[hp] + t * 256 + lane * 4);
             const int node = 16 * t + ln;                     // this lane's node in ^T tiles
-            s16x4 rh, rl;
-            split4(R, rh, rl);
-            const f32x4 U = mfma16(di, rl, mfma16(di, rh, z));
-            uhi[t] = to_bf16x4(U);
-            const f32x4 UT = mfma16(rl, di, mfma16(rh, di, z));
-            if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 4 * lq) = UT;
+#pragma unroll
+            for (int g = 0; g < CG; ++g) {
+                s16x4 rh, rl;
+                split4(R[g], rh, rl);
+                const f32x4 U = mfma16(di, rl, mfma16(di, rh, z));
+                uhi[g][t] = to_bf16x4(U);
+                const f32x4 UT = mfma16(rl, di, mfma16(rh, di, z));
+                if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 16 * g + 4 * lq) = UT;
+            }
             // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T
-            f32x4 Oa = z, Ob = z;
+            f32x4 Oc[CG];
+#pragma unroll
+            for (int g = 0; g < CG; ++g) Oc[g] = z;
 #pragma unroll
             for (int s = 0; s <= t; ++s) {
                 const s16x4 yt = *reinterpret_cast<const s16x4*>(tiles + (NX + t * (t + 1) / 2 + s) * 256 + lane * 4);
-                if (s & 1) Ob = mfma16(uhi[s], yt, Ob);
-                else Oa = mfma16(uhi[s], yt, Oa);
+#pragma unroll
+                for (int g = 0; g < CG; ++g) Oc[g] = mfma16(uhi[g][s], yt, Oc[g]);
             }
             if (node < N) {
                 const float egn = __expf(lgp[node]);
-                f32x4 OT;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[m] + (Oa[m] + Ob[m]);
-                const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
-                const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
-                *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + col0 + 4 * lq) =
-                    make_uint2(lo, hi);
+                for (int g = 0; g < CG; ++g) {
+                    f32x4 OT;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[g][m] + Oc[g][m];
+                    const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
+                    const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
+                    *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + col0 + 16 * g + 4 * lq) =
+                        make_uint2(lo, hi);
+                }
             }
         }
         lds_barrier();                                      // k / q in LDS are free now
-        if (more) kq_dma(nxt);                                // the next item's k / q and S0
-#pragma unroll
-        for (int c = 0; c < 4; ++c) load_s0(pf, c);
+        if (more) kq_dma(nxt);                                // the next item's k / q
     }
 }
 
@@ -596,7 +633,7 @@ hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream) 
     const unsigned grid = (unsigned)(nitems < cus ? nitems : cus);
     VerifyArgs copy = a;
     void* args[] = {&copy, &nitems};
-    return hipLaunchKernel(fn, dim3(grid), dim3(512 * hpw), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(grid), dim3(256 * hpw), args, 0, stream);
 }
 
 }  // namespace gdn
