@@ -128,10 +128,32 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* m, int blk, int cs, i
                                           m + kq_off(row, 4 * cs + (lane >> 4))));
 }
 
-// Position of element (row, col) of a 16x16 tile stored in A-operand fragment
-// order of the 16x16x16 MFMA (lane L holds row L%16, columns 4(L/16)..+3).
-__device__ __forceinline__ int frag_pos(int row, int col) {
-    return (row + 16 * (col >> 2)) * 4 + (col & 3);
+// 16x16 bf16 tiles in LDS are stored as half of a 16x16x32 A operand: element
+// (row, col) at 16-byte slot row + 16 (col / 8), position col % 8.  Two tiles
+// stored back to back then form one 16 x 32 operand [T_0 | T_1]: lane l reads
+// 16 bytes at slot l and holds row l % 16, columns 8 (l / 16) .. +7.
+__device__ __forceinline__ int a32_pos(int row, int col) {
+    return (row + 16 * (col >> 3)) * 8 + (col & 7);
+}
+
+// Two 16x16 blocks X, Y held in accumulator layout (lane (n, q): rows
+// 4q .. 4q+3 of column n, as bf16) -> the stacked 32 x 16 matrix [X; Y] as a
+// 16x16x32 B operand (lane (n, q): rows 8q .. 8q+7 of column n).  Read as an A
+// operand the same registers are [X^T | Y^T].  Two cross-lane swaps: the
+// 32-lane swap gives [X rows 0-7 | Y rows 0-7] and [X rows 8-15 | Y rows 8-15]
+// by lane halves, the 16-lane swap interleaves them into 8-row runs.
+__device__ __forceinline__ bf16x8 stack_pair(s16x4 x, s16x4 y) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 xv = __builtin_bit_cast(u32x2, x), yv = __builtin_bit_cast(u32x2, y);
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const auto w = __builtin_amdgcn_permlane32_swap(xv[h], yv[h], false, false);
+        const auto v = __builtin_amdgcn_permlane16_swap(w[0], w[1], false, false);
+        r[h] = v[0];
+        r[2 + h] = v[1];
+    }
+    return __builtin_bit_cast(bf16x8, r);
 }
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
@@ -167,7 +189,9 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     static_assert(KQ_INS % NW == 0, "whole direct-to-LDS loads per wave");
     __shared__ __attribute__((aligned(16))) uint16_t s_k[NP * kD];
     __shared__ __attribute__((aligned(16))) uint16_t s_q[NP * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t s_tiles[HPW][NB * NB * 256];  // -X then Y
+    // -X then Y tiles; one spare tile at the end: a row's last pair may read
+    // 512 bytes past its last tile (those lanes are zeroed before use)
+    __shared__ __attribute__((aligned(16))) uint16_t s_tiles[HPW][NB * NB * 256 + 256];
     __shared__ __attribute__((aligned(16))) uint16_t s_dinv[HPW][NB * 256];
     __shared__ __attribute__((aligned(16))) float s_xd[HPW][NB * 256];
     __shared__ __attribute__((aligned(16))) uint32_t s_mask[NP * MW];
@@ -190,8 +214,16 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     int lane = tid & 63;
     int ln = lane & 15, lq = lane >> 4;
 
-    // item -> (sequence, key head, head group)
+    // work slot -> (sequence, key head, head group).  Slot it runs on workgroup
+    // it % grid in round it / grid; workgroups are dealt to the eight XCDs
+    // round robin, so within a full round the slots are renumbered XCD by XCD:
+    // the grid / 8 workgroups of one XCD take consecutive items, and the items
+    // of one sequence (which share its parent row and the g / beta lines) meet
+    // in one L2.
+    const int grid = gridDim.x;
     auto decode = [&](int it, int& b, int& hk, int& hg) {
+        const int r = it / grid, x = it - r * grid;
+        if ((grid & 7) == 0 && (r + 1) * grid <= nitems) it = r * grid + (x & 7) * (grid >> 3) + (x >> 3);
         hg = it % GG;
         const int bh = it / GG;
         hk = bh % Hk;
@@ -207,17 +239,19 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     // copy would wait for every older load and store of the wave.
     constexpr int NSM = NPL * (1 + HPW);
     uint32_t sm[NSM];
-    auto load_small = [&](int it) {
+    // (real = false: a placeholder after the last item, every lane reading one
+    // word, so that the loads still happen but move next to no bytes)
+    auto load_small = [&](int it, bool real) {
         int b, hk, hg;
         decode(it, b, hk, hg);
         const int h0 = hk * G + hg * HPW;
         const uint32_t* par = reinterpret_cast<const uint32_t*>(a.parent) + (size_t)b * N;
         const uint32_t* gg = reinterpret_cast<const uint32_t*>(wave == 0 ? a.g : a.beta) +
                              (size_t)b * N * Hv + h0;
-        const int nb = min(max(tid - 64, 0), N - 1);
+        const int nb = real ? min(max(tid - 64, 0), N - 1) : 0;
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
-            const int i = min(lane + 64 * k, N - 1);
+            const int i = real ? min(lane + 64 * k, N - 1) : 0;
             sm[k] = par[i];
 #pragma unroll
             for (int p = 0; p < HPW; ++p)
@@ -245,17 +279,24 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         }
     };
     float4 s0raw[CG][4][2];
-    // this wave's S0 rows of column group g (col0 + 16g + l%16), key columns
-    // 32c + 8(l/16)..+7
-    auto load_s0 = [&](int it, int g) {
+    // this wave's S0 rows of column group g, key columns 32c + 8(l/16)..+7.
+    // Group g's local row rho is value column col0 + 8 (rho / 4) + 4g + rho % 4:
+    // the groups interleave in runs of 4, so the 4 + 4 values a lane holds for
+    // one node in the transposed outputs (and the v values it needs) are 8
+    // consecutive columns, one 16-byte access for both groups.
+    // (real = false: the placeholder loads of the last item, all from one line)
+    auto load_s0 = [&](int it, int g, bool real) {
         int b, hk, hg;
         decode(it, b, hk, hg);
         const int h = hk * G + hg * HPW + hp;
-        const float* p0 = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(col0 + 16 * g + ln) * kD + 8 * lq;
+        const int row = col0 + 8 * (ln >> 2) + 4 * g + (ln & 3);
+        const float* p0 = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)row * kD + 8 * lq;
+        const int cstep = real ? 32 : 0;
+        if (!real) p0 = a.S0;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            s0raw[g][c][0] = *reinterpret_cast<const float4*>(p0 + 32 * c);
-            s0raw[g][c][1] = *reinterpret_cast<const float4*>(p0 + 32 * c + 4);
+            s0raw[g][c][0] = *reinterpret_cast<const float4*>(p0 + cstep * c);
+            s0raw[g][c][1] = *reinterpret_cast<const float4*>(p0 + cstep * c + (real ? 4 : 0));
         }
     };
 
@@ -371,10 +412,10 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
 
     int item = blockIdx.x;                                    // grid <= nitems
-    load_small(item);
+    load_small(item, true);
     kq_dma(item);
 #pragma unroll
-    for (int g = 0; g < CG; ++g) load_s0(item, g);
+    for (int g = 0; g < CG; ++g) load_s0(item, g, true);
 
     for (; item < nitems; item += gridDim.x) {
         asm volatile("" : "+v"(tid));
@@ -383,7 +424,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         lq = lane >> 4;
         const int nxt = item + gridDim.x;
         const bool more = nxt < nitems;
-        const int pf = more ? nxt : item;                     // (the last item re-reads itself)
+        const int pf = more ? nxt : item;                     // (the last item: placeholders)
         int b, hk, hg;
         decode(item, b, hk, hg);
         const int h0 = hk * G + hg * HPW;
@@ -408,7 +449,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         const int status = __builtin_amdgcn_readfirstlane(s_flag);   // uniform branch below
         uint16_t* O = static_cast<uint16_t*>(a.o);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        uint2 vfr[CG][NB];                            // node 16t + l%16, columns col0 + 16g + 4(l/16)..+3
+        u32x4 vfr[NB];                                // node 16t + l%16, columns col0 + 8(l/16)..+7
         // this item's S0 rows as bf16 B / A operands (registers for the whole item)
         // (pinned here by an empty asm: sunk to its uses in the solve, the
         // conversion would keep s0raw alive under the next item's prefetch)
@@ -439,52 +480,81 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 #pragma unroll
             for (int t = 0; t < NB; ++t) {
                 const int i = min(16 * t + ln, N - 1);
-#pragma unroll
-                for (int g = 0; g < CG; ++g)
-                    vfr[g][t] = *reinterpret_cast<const uint2*>(V + vo_base + (size_t)i * vo_row + col0 + 16 * g + 4 * lq);
+                vfr[t] = *reinterpret_cast<const u32x4*>(V + vo_base + (size_t)i * vo_row + col0 + 8 * lq);
             }
             // ---- 3. Gram tiles -> masked, decayed X / Y tiles per head ----------
             // Computed transposed, K_s K_t^T and K_s Q_t^T: lane l then holds row
-            // i = 16t + l%16 and columns j = 16s + 4(l/16)..+3, which is exactly its
-            // slot in the A-operand fragment order (8 contiguous bytes per lane).
-            for (int pi = wave; pi < NPAIR; pi += NW) {
+            // i = 16t + l%16 and columns j = 16s + 4(l/16)..+3, which is its place
+            // in the tile layout (8 contiguous bytes per lane).  Each wave takes a
+            // contiguous run of the (t, s), s <= t, pairs in row order: it keeps row
+            // t's k / q fragments across its pairs of that row, and the next pair's
+            // fragments are requested before the current pair's masking.
+            {
+                constexpr int MAXC = (NPAIR + NW - 1) / NW;
+                const int p0 = wave * NPAIR / NW, p1 = (wave + 1) * NPAIR / NW;
                 int t = 0;
-                while ((t + 1) * (t + 2) / 2 <= pi) ++t;
-                const int s = pi - t * (t + 1) / 2;
-                if (t >= nblk) continue;
-                f32x4 A = z, C = z;
+                while ((t + 1) * (t + 2) / 2 <= p0) ++t;
+                int s = p0 - t * (t + 1) / 2;
+                bf16x8 fk[4], fq[4], fs[4];
 #pragma unroll
                 for (int cs = 0; cs < 4; ++cs) {
-                    const bf16x8 ks = lds_frag(s_k, s, cs, lane);
-                    A = mfma32(ks, lds_frag(s_k, t, cs, lane), A);
-                    C = mfma32(ks, lds_frag(s_q, t, cs, lane), C);
+                    fk[cs] = lds_frag(s_k, t, cs, lane);
+                    fq[cs] = lds_frag(s_q, t, cs, lane);
+                    fs[cs] = lds_frag(s_k, s, cs, lane);
                 }
-                const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
-                const uint32_t bits = i < N ? (s_mask[i * MW + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
 #pragma unroll
-                for (int p = 0; p < HPW; ++p) {
-                    const float lgi = s_lg[p][i], bei = s_beta[p][i];
-                    const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[p][j0]);
-                    const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
-                    float xv[4];
-                    uint16_t yv[4], nxv[4];
+                for (int c = 0; c < MAXC; ++c) {
+                    if (p0 + c >= p1 || t >= nblk) break;      // uniform
+                    f32x4 A = z, C = z;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool anc = (bits >> e) & 1u;
-                        const bool self = (j0 + e == i) && i < N;
-                        const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
-                        xv[e] = anc ? bei * d * A[e] : 0.f;
-                        yv[e] = bf16_rne(d * C[e]);
-                        nxv[e] = bf16_rne(-xv[e]);
+                    for (int cs = 0; cs < 4; ++cs) {
+                        A = mfma32(fs[cs], fk[cs], A);
+                        C = mfma32(fs[cs], fq[cs], C);
                     }
-                    *reinterpret_cast<uint2*>(&s_tiles[p][(NX + t * (t + 1) / 2 + s) * 256 + lane * 4]) =
-                        make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
-                    if (s < t)
-                        *reinterpret_cast<uint2*>(&s_tiles[p][(t * (t - 1) / 2 + s) * 256 + lane * 4]) =
-                            make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
-                    else
-                        *reinterpret_cast<float4*>(&s_xd[p][t * 256 + ln * 16 + 4 * lq]) =
-                            make_float4(xv[0], xv[1], xv[2], xv[3]);
+                    const int tc = t, sc = s;
+                    // the next pair's fragments (rows past N re-read earlier
+                    // rows: harmless, never used)
+                    if (++s > t) { ++t; s = 0; }
+                    if (c + 1 < MAXC) {
+                        const int tl = min(t, NB - 1);
+                        if (s == 0) {
+#pragma unroll
+                            for (int cs = 0; cs < 4; ++cs) {
+                                fk[cs] = lds_frag(s_k, tl, cs, lane);
+                                fq[cs] = lds_frag(s_q, tl, cs, lane);
+                            }
+                        }
+#pragma unroll
+                        for (int cs = 0; cs < 4; ++cs) fs[cs] = lds_frag(s_k, min(s, NB - 1), cs, lane);
+                    }
+                    const int i = 16 * tc + ln, j0 = 16 * sc + 4 * lq;
+                    const uint32_t bits = i < N ? (s_mask[i * MW + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
+#pragma unroll
+                    for (int p = 0; p < HPW; ++p) {
+                        const float lgi = s_lg[p][i], bei = s_beta[p][i];
+                        const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[p][j0]);
+                        const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
+                        float xv[4];
+                        uint16_t yv[4], nxv[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const bool anc = (bits >> e) & 1u;
+                            const bool self = (j0 + e == i) && i < N;
+                            const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
+                            xv[e] = anc ? bei * d * A[e] : 0.f;
+                            yv[e] = bf16_rne(d * C[e]);
+                            nxv[e] = bf16_rne(-xv[e]);
+                        }
+                        const int tp = a32_pos(ln, 4 * lq);       // 4 consecutive columns: 8 bytes
+                        *reinterpret_cast<uint2*>(&s_tiles[p][(NX + tc * (tc + 1) / 2 + sc) * 256 + tp]) =
+                            make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
+                        if (sc < tc)
+                            *reinterpret_cast<uint2*>(&s_tiles[p][(tc * (tc - 1) / 2 + sc) * 256 + tp]) =
+                                make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
+                        else
+                            *reinterpret_cast<float4*>(&s_xd[p][tc * 256 + ln * 16 + 4 * lq]) =
+                                make_float4(xv[0], xv[1], xv[2], xv[3]);
+                    }
                 }
             }
             lds_barrier();
@@ -494,9 +564,9 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         // during the inversion, ahead of the solve's output stores (loads and
         // stores retire in order).  One program point for both paths, so no
         // register copy of a load in flight is needed where they meet.
-        load_small(pf);
+        load_small(pf, more);
 #pragma unroll
-        for (int g = 0; g < CG; ++g) load_s0(pf, g);
+        for (int g = 0; g < CG; ++g) load_s0(pf, g, more);
         if (!status) {
             // ---- 4. diagonal blocks: (I + X_tt)^-1 in fp32 ----------------------
             for (int blk = tid >> 4; blk < HPW * NB; blk += NT / 16) {
@@ -512,7 +582,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
                         y[i] = acc;
                     }
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) s_dinv[p][t * 256 + frag_pos(i, ln)] = bf16_rne(y[i]);
+                    for (int i = 0; i < 16; ++i) s_dinv[p][t * 256 + a32_pos(i, ln)] = bf16_rne(y[i]);
                 }
             }
             lds_barrier();
@@ -522,19 +592,27 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         wait_vmem_le<8 * CG>();
         if (wave == NW - 1) write_tree_cache(b, h0, hk == 0 && hg == 0, status);
         // ---- 5. per wave: projection, blocked substitution, output ---------
-        //   sb[g][cs]   S0 rows r = col0 + 16g + l%16: B operand of K S0^T, A
+        //   sb[g][cs]   S0 rows of group g (local row l%16): B operand of K S0^T, A
         //               operand of S0 Q^T;  k / q frags of block t (LDS): A / B;
-        //   vfr[g][t]   v rows of block t (A operand), moved into accumulator
-        //               layout by an exact product with I;
-        //   uhi[g][s]   U_s rounded to bf16, accumulator layout (node rows): B
-        //               operand of X U and, read as U_s^T, A operand of U^T Y^T.
-        //               U itself (stored to the cache) stays fp32: it comes from
-        //               R_t split into bf16 hi + lo against (I + X_tt)^-1.
+        //   vfr[t]      v rows of block t, both groups' columns; group g's half
+        //               (A operand) is moved into accumulator layout by an exact
+        //               product with I;
+        //   up[g][p]    [U_2p; U_2p+1] rounded to bf16 as a 16x16x32 B operand
+        //               (stack_pair): B operand of [X_t,2p | X_t,2p+1] U and,
+        //               read as [U_2p^T | U_2p+1^T], A operand of U^T Y^T.  Until
+        //               U_2p+1 exists its half is zero.  U itself (stored to the
+        //               cache) stays fp32: R_t is split into bf16 hi + lo and
+        //               [D | D] [hi; lo] is one MFMA, D = (I + X_tt)^-1.
+        //   Every tile product takes two node blocks at once (K = 32); a row's
+        //   last pair with one block only has its second half zeroed.
         const uint16_t* tiles = s_tiles[hp];
         const float* lgp = s_lg[hp];
         const float* bep = s_beta[hp];
         float* Ug = a.u + ((size_t)b * Hv + h) * (size_t)N * kD;
-        s16x4 uhi[CG][NB];
+        const s16x4 zero4 = {0, 0, 0, 0};
+        const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        const bool hi_half = lq >= 2;                          // lanes of the pair's second block
+        bf16x8 up[CG][(NB + 1) / 2];
         const int nsolve = status ? 0 : nblk;
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
@@ -554,54 +632,66 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
             f32x4 R[CG];
 #pragma unroll
             for (int g = 0; g < CG; ++g) {
-                const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vfr[g][t]), ident, z);
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 vg = {vfr[t][2 * g], vfr[t][2 * g + 1]};   // group g's 4 columns
+                const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vg), ident, z);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int i = 16 * t + 4 * lq + m;
                     R[g][m] = bep[i] * (vd[m] - __expf(lgp[i]) * pk[g][m]);
                 }
             }
-            // R_t += sum_{s<t} (-X_ts) U_s
+            // R_t += sum_{s<t} (-X_ts) U_s, two blocks per product
 #pragma unroll
-            for (int s = 0; s < t; ++s) {
-                const s16x4 nx = *reinterpret_cast<const s16x4*>(tiles + (t * (t - 1) / 2 + s) * 256 + lane * 4);
+            for (int s = 0; s < t; s += 2) {
+                bf16x8 nx = *reinterpret_cast<const bf16x8*>(tiles + (t * (t - 1) / 2 + s) * 256 + lane * 8);
+                if (s + 1 == t) nx = hi_half ? zero8 : nx;        // X_tt is not in the sum
 #pragma unroll
-                for (int g = 0; g < CG; ++g) R[g] = mfma16(nx, uhi[g][s], R[g]);
+                for (int g = 0; g < CG; ++g) R[g] = mfma32(nx, up[g][s / 2], R[g]);
             }
-            // U_t = (I + X_tt)^-1 R_t, kept as [node][r]; U_t^T = R_t^T Dinv^T is stored
-            const s16x4 di = *reinterpret_cast<const s16x4*>(s_dinv[hp] + t * 256 + lane * 4);
+            // U_t = D R_t, kept as [node][r]; U_t^T = R_t^T D^T is stored
+            const bf16x8 di = *reinterpret_cast<const bf16x8*>(s_dinv[hp] + t * 256 + (ln + 16 * (lq & 1)) * 8);
             const int node = 16 * t + ln;                     // this lane's node in ^T tiles
 #pragma unroll
             for (int g = 0; g < CG; ++g) {
                 s16x4 rh, rl;
                 split4(R[g], rh, rl);
-                const f32x4 U = mfma16(di, rl, mfma16(di, rh, z));
-                uhi[g][t] = to_bf16x4(U);
-                const f32x4 UT = mfma16(rl, di, mfma16(rh, di, z));
-                if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 16 * g + 4 * lq) = UT;
+                const bf16x8 rr = stack_pair(rh, rl);
+                const f32x4 U = mfma32(di, rr, z);
+                const f32x4 UT = mfma32(rr, di, z);
+                // (the halves of a stacked pair sit in disjoint lanes: the odd
+                // block is OR-ed into the pair its even partner started)
+                const s16x4 ut = to_bf16x4(U);
+                if (t & 1)
+                    up[g][t / 2] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, up[g][t / 2]) |
+                                                                  __builtin_bit_cast(u32x4, stack_pair(zero4, ut)));
+                else
+                    up[g][t / 2] = stack_pair(ut, zero4);
+                if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 8 * lq + 4 * g) = UT;
             }
-            // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T
+            // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T, two blocks per product
             f32x4 Oc[CG];
 #pragma unroll
             for (int g = 0; g < CG; ++g) Oc[g] = z;
 #pragma unroll
-            for (int s = 0; s <= t; ++s) {
-                const s16x4 yt = *reinterpret_cast<const s16x4*>(tiles + (NX + t * (t + 1) / 2 + s) * 256 + lane * 4);
+            for (int s = 0; s <= t; s += 2) {
+                bf16x8 yt = *reinterpret_cast<const bf16x8*>(tiles + (NX + t * (t + 1) / 2 + s) * 256 + lane * 8);
+                if (s == t) yt = hi_half ? zero8 : yt;            // no block t + 1 in row t
 #pragma unroll
-                for (int g = 0; g < CG; ++g) Oc[g] = mfma16(uhi[g][s], yt, Oc[g]);
+                for (int g = 0; g < CG; ++g) Oc[g] = mfma32(up[g][s / 2], yt, Oc[g]);
             }
             if (node < N) {
                 const float egn = __expf(lgp[node]);
+                u32x4 ov;
 #pragma unroll
                 for (int g = 0; g < CG; ++g) {
                     f32x4 OT;
 #pragma unroll
                     for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[g][m] + Oc[g][m];
-                    const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
-                    const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
-                    *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + col0 + 16 * g + 4 * lq) =
-                        make_uint2(lo, hi);
+                    ov[2 * g] = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
+                    ov[2 * g + 1] = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
                 }
+                *reinterpret_cast<u32x4*>(O + vo_base + (size_t)node * vo_row + col0 + 8 * lq) = ov;
             }
         }
         lds_barrier();                                      // k / q in LDS are free now
