@@ -220,6 +220,28 @@ def copy_calibration(mib):
                       "us_per_copy": ms * 1e3, "GBs": moved / (ms * 1e-3) / 1e9}), flush=True)
 
 
+# ---------------------------------------------------------------- traffic
+
+def profiled_traffic(workload):
+    """HBM bytes per verify launch measured by the FETCH_SIZE / WRITE_SIZE
+    counter passes (profiles/verify_traffic_<workload>.txt), or None when there
+    is no such record or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"verify_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    traffic, ok = None, True
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("traffic_bytes="):
+            traffic = int(line.split("=", 1)[1])
+        elif line.startswith("sha256 "):
+            rel, digest = line[len("sha256 "):].split("=", 1)
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                ok &= hashlib.sha256(f.read()).hexdigest() == digest
+    return traffic if ok else None
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -277,7 +299,7 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "verify", "achieved": achieved,
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None, "alg_bytes_per_launch": vb,
+            "traffic": profiled_traffic(s.name), "alg_bytes_per_launch": vb,
             "launch_us": r["verify_ms"] * 1e3,
         },
         "commit": {

@@ -11,31 +11,22 @@
 // The section names the three fused stages this kernel runs in one pass: the
 // Gram matrix, a tiled forward substitution, and the output stage.
 //
-// One workgroup per (sequence, key head, group of HPW value heads), four waves
-// per value head.  Every global load is issued at entry (parent, g, beta; the
-// tree's k and q rows; each wave's S0 rows and v columns), so that after the
-// tree is built nothing waits on global memory except the output stores:
-//  1. the tree's strict-ancestor bit rows go to LDS (in-place pointer
-//     jumping), then k / q rows (bf16, XOR-swizzled 16-byte chunks) and, per
-//     value head, G and beta;
-//  2. Gram tiles K_t K_s^T and Q_t K_s^T (16 x 16, s <= t) on
-//     v_mfma_f32_16x16x32_bf16, shared by the HPW heads, masked and decayed
-//     per head into bf16 X / Y tiles (X negated) and fp32 diagonal X blocks;
-//  3. each diagonal block (I + X_tt) is inverted in fp32 (16 x 16 unit lower
-//     triangular, forward substitution per column) and stored as bf16;
-//  4. each wave owns 32 of its head's 128 value columns and runs, block by
-//     block, with no barrier: P_K = K_t S0^T and P_Q^T = S0 Q_t^T (S0 held in
-//     registers as bf16), R_t, the blocked substitution
-//     R_t += sum_{s<t} (-X_ts) U_s, U_t = (I + X_tt)^-1 R_t and
-//     O_t = e^G P_Q + sum_{s<=t} Y_ts U_s on the 16x16x16 MFMA.  The
-//     accumulator layout (lane l: rows 4(l/16)..+3 of column l%16) is also
-//     the B-operand layout of that MFMA, and, read transposed, its A-operand
-//     layout, so U stays in registers as a bf16 hi + lo pair (about 16
-//     mantissa bits) and the outputs come out transposed, four consecutive
-//     columns per lane, for 8- and 16-byte row stores.
+// Persistent workgroups (one per CU) loop over work items = (sequence, key
+// head, group of HPW value heads); four waves per value head, each owning 32
+// value columns as two interleaved 16-column groups.  Per item:
+//  1. one wave builds the tree's strict-ancestor bit rows and the path
+//     log-gates G by synchronous pointer doubling in LDS;
+//  2. Gram tiles K_s K_t^T and K_s Q_t^T (16 x 16, s <= t) on
+//     v_mfma_f32_16x16x32_bf16, shared by the HPW heads, masked and decayed per
+//     head into bf16 -X / Y tiles (stored as halves of 16x16x32 A operands)
+//     and fp32 diagonal X blocks;
+//  3. each diagonal block (I + X_tt) is inverted in fp32;
+//  4. each wave runs its columns through the blocked substitution and the
+//     output stage with no barrier, two node blocks per MFMA.
+// The next item's inputs load while this one computes (details at the kernel).
 //
 // HBM traffic is the algorithm's own: S0 once (fp32, rounded to bf16 on
-// chip), k / q once per workgroup, v once, o (bf16) and the u / G cache (fp32)
+// chip), k / q once per item, v once, o (bf16) and the u / G cache (fp32)
 // written once.  Nothing writes S0.
 #include "gdn_common.hpp"
 #include "launch.hpp"
@@ -45,8 +36,6 @@ namespace gdn {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -90,28 +79,6 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
     r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
     r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
     return r;
-}
-
-// Map a workgroup id to (sequence b, key head hk, head group hg).  Workgroups
-// are handed to the eight XCDs round robin, so ids x and x + 8 share an XCD and
-// its L2; when a key head has several head groups (GG > 1) they get ids 8
-// apart, so all but the first find that pair's q and k in L2.
-__device__ __forceinline__ void group_of(int x, int B, int Hk, int GG, int& b, int& hk,
-                                         int& hg) {
-    const int P = B * Hk;
-    const int full = (P / 8) * 8 * GG;
-    int pair;
-    if (x < full) {
-        const int q = x / (8 * GG), rem = x % (8 * GG);
-        hg = rem / 8;
-        pair = q * 8 + rem % 8;
-    } else {
-        const int y = x - full;
-        pair = (P / 8) * 8 + y / GG;
-        hg = y % GG;
-    }
-    b = pair / Hk;
-    hk = pair % Hk;
 }
 
 // 16-byte chunk (row, chunk) of a k / q row in LDS; chunks are XOR-swizzled by
