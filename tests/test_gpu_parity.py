@@ -66,7 +66,7 @@ def custom(seed, parents, Hk, Hv, d, io="bf16", beta_mu=0.0):
     return parent, lay
 
 
-RAGGED = [1, 2, 33, 37, 64, 100, 127, 129, 200, 255, 300]
+RAGGED = [1, 2, 33, 37, 64, 100, 127, 129, 200, 255, 256, 257, 300, 512, 513]
 
 
 @pytest.mark.parametrize("N", RAGGED)
@@ -170,6 +170,50 @@ def test_deterministic_and_non_ancestor_independent():
     others = [j for j in range(N) if j != node and j not in anc]
     lay2 = {key: val.copy() for key, val in lay.items()}
     pert = W.draw_layer(np.random.default_rng(65), 1, N, 1, 2, 128)
+    for key in ("q", "k", "v", "beta", "g"):
+        lay2[key][:, others] = pert[key][:, others]
+    r3 = gpu_run(parent, acc, lay2, "bf16", 1, 2)
+    assert np.array_equal(r3["o"][0, node], r1["o"][0, node])
+    assert np.array_equal(r3["S_commit"], r1["S_commit"])
+
+
+def test_invalid_trees_large():
+    """Tree errors on the path for 129 .. 512 nodes (a separate tree launch)."""
+    rng = np.random.default_rng(66)
+    N = 200
+    good = W.tree_random_recursive(rng, N)
+    bad1 = good.copy(); bad1[150] = 150         # self parent
+    bad2 = good.copy(); bad2[130] = 199         # forward parent
+    bad3 = good.copy(); bad3[3] = -5            # below -1
+    parent, lay = custom(67, [good, bad1, bad2, bad3], 1, 2, 128)
+    accepted = np.array([N - 1, 2, 2, 2], np.int32)
+    gpu, ref, _ = check_case(parent, accepted, lay, "bf16", 1, 2, name="invalid large")
+    assert gpu["status"].tolist() == [0, 151, 131, 4]
+    assert gpu["path_len"].tolist()[1:] == [-1, -1, -1]
+    for b in (1, 2, 3):
+        assert np.array_equal(gpu["S_commit"][b], lay["S0"][b].astype(np.float64))
+
+
+def test_deterministic_large():
+    """The larger-tree path gives identical bits on two runs, and a node's
+    output does not move when every non-ancestor's inputs change."""
+    rng = np.random.default_rng(68)
+    N = 300
+    par = W.tree_random_recursive(rng, N)
+    parent, lay = custom(69, [par], 1, 2, 128)
+    acc = np.array([N - 1], np.int32)
+    r1 = gpu_run(parent, acc, lay, "bf16", 1, 2)
+    r2 = gpu_run(parent, acc, lay, "bf16", 1, 2)
+    for key in ("o", "u", "log_gamma", "S_commit"):
+        assert np.array_equal(r1[key], r2[key]), key
+    node = N - 1
+    anc = set()
+    j = par[node]
+    while j >= 0:
+        anc.add(int(j)); j = par[j]
+    others = [j for j in range(N) if j != node and j not in anc]
+    lay2 = {key: val.copy() for key, val in lay.items()}
+    pert = W.draw_layer(np.random.default_rng(70), 1, N, 1, 2, 128)
     for key in ("q", "k", "v", "beta", "g"):
         lay2[key][:, others] = pert[key][:, others]
     r3 = gpu_run(parent, acc, lay2, "bf16", 1, 2)

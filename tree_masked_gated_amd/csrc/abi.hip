@@ -68,9 +68,9 @@ int gdn_tree_verify(const gdn_tree_dims* dims, const float* S0, const void* q,
                  S0, q, k, v, beta, g, parent, o,
                  cache->anc_mask, cache->depth, cache->u, cache->log_gamma,
                  cache->tree_status};
-    hipError_t e = verify_tiled_supported(a, dims->io_dtype)
-                       ? launch_verify_tiled(a, dims->io_dtype, stream)
-                       : launch_verify_generic(a, dims->io_dtype, stream);
+    hipError_t e = verify_tiled_supported(a, dims->io_dtype)   ? launch_verify_tiled(a, dims->io_dtype, stream)
+                   : verify_large_supported(a, dims->io_dtype) ? launch_verify_large(a, dims->io_dtype, stream)
+                                                               : launch_verify_generic(a, dims->io_dtype, stream);
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

@@ -15,6 +15,11 @@ hipError_t launch_verify_generic(const VerifyArgs& a, int io, hipStream_t stream
 bool verify_tiled_supported(const VerifyArgs& a, int io);
 hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream);
 
+// MFMA verification of larger trees: d_k = d_v = 128, bf16 io, 129 .. 512 nodes
+// (two launches: the tree's ancestor rows into the cache, then the solve).
+bool verify_large_supported(const VerifyArgs& a, int io);
+hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream);
+
 // Deferred commit of the accepted node's state.
 hipError_t launch_commit(const CommitArgs& a, int io, hipStream_t stream);
 
