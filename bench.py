@@ -97,7 +97,11 @@ def run_gpu(args, s):
     dims = T.dims(s.batch, s.n_nodes, s.h_k, s.h_v, s.d, s.d, s.io)
     par = W.to_device(parent, device=dev)
     acc = W.to_device(accepted, device=dev)
-    caches = [T.TreeCache(dims, dev) for _ in range(L)]
+    # two caches per layer: the fused step reads the previous tree's while it
+    # writes the new tree's
+    caches2 = [[T.TreeCache(dims, dev), T.TreeCache(dims, dev) if args.fused else None]
+               for _ in range(L)]
+    caches = [c[0] for c in caches2]
     o = [torch.empty((s.batch, s.n_nodes, s.h_v, s.d), dtype=layers[0]["q"].dtype,
                      device=dev) for _ in range(L)]
     path = torch.empty((s.batch, s.n_nodes), dtype=torch.int32, device=dev)
@@ -116,12 +120,29 @@ def run_gpu(args, s):
         T.gdn_tree_commit(dims, x["S"][phase[0]], x["S"][1 - phase[0]], x["k"], caches[l],
                           acc, path, plen, sptr)
 
+    cur = [0]
+
+    def commit_verify(l):
+        x = layers[l]
+        T.gdn_tree_commit_verify(dims, x["S"][phase[0]], x["S"][1 - phase[0]], x["k"],
+                                 caches2[l][cur[0]], acc, path, plen, x["q"], x["k"], x["v"],
+                                 x["beta"], x["g"], par, o[l], caches2[l][1 - cur[0]], sptr)
+
     def step():
-        for l in range(L):
-            verify(l)
-            commit(l)
+        if args.fused:
+            # commit of the tree verified last step, then this step's tree
+            for l in range(L):
+                commit_verify(l)
+            cur[0] ^= 1
+        else:
+            for l in range(L):
+                verify(l)
+                commit(l)
         phase[0] ^= 1
 
+    if args.fused:
+        for l in range(L):            # the first tree has no commit before it
+            verify(l)
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
@@ -151,12 +172,15 @@ def run_gpu(args, s):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * L)
 
+    fused_ms = timed(commit_verify) if args.fused else None
     verify_ms = timed(verify)
     commit_ms = timed(commit)
-    log(f"verify {verify_ms * 1e3:.1f} us/launch, commit {commit_ms * 1e3:.1f} us/launch")
+    log(f"verify {verify_ms * 1e3:.1f} us/launch, commit {commit_ms * 1e3:.1f} us/launch"
+        + (f", commit+verify {fused_ms * 1e3:.1f} us/launch" if args.fused else ""))
     path_lens = plen.cpu().numpy()
     return {
         "total_ms": total_ms, "verify_ms": verify_ms, "commit_ms": commit_ms,
+        "fused_ms": fused_ms,
         "verify_bytes": verify_bytes(s, e), "commit_bytes": commit_bytes(s, e, path_lens),
         "path_lens": path_lens, "parent": parent, "accepted": accepted,
     }
@@ -222,12 +246,12 @@ def copy_calibration(mib):
 
 # ---------------------------------------------------------------- traffic
 
-def profiled_traffic(workload):
-    """HBM bytes per verify launch measured by the FETCH_SIZE / WRITE_SIZE
-    counter passes (profiles/verify_traffic_<workload>.txt), or None when there
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch of kernel measured by the FETCH_SIZE / WRITE_SIZE
+    counter passes (profiles/<kernel>_traffic_<workload>.txt), or None when there
     is no such record or the kernel sources changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"verify_traffic_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     traffic, ok = None, True
@@ -254,6 +278,8 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--fused", action="store_true",
+                    help="one launch per layer: commit the previous tree, verify the next")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -270,8 +296,14 @@ def main():
     L = s.layers
     nodes = s.batch * s.n_nodes
     value = nodes * L * args.steps / (r["total_ms"] * 1e-3)
-    vb = r["verify_bytes"]
-    achieved = vb / (r["verify_ms"] * 1e-3) / 1e9
+    if args.fused:
+        # the fused launch reads the state once for both halves
+        kernel, launch_ms = "commit_verify", r["fused_ms"]
+        vb = r["verify_bytes"] + r["commit_bytes"] - 4 * s.batch * s.h_v * s.d * s.d
+    else:
+        kernel, launch_ms = "verify", r["verify_ms"]
+        vb = r["verify_bytes"]
+    achieved = vb / (launch_ms * 1e-3) / 1e9
     base = None
     if args.cpu_budget > 0:
         log("timing the oracle on the host")
@@ -297,10 +329,14 @@ def main():
             "state": "f32",
         },
         "roofline": {
-            "bound": "hbm", "kernel": "verify", "achieved": achieved,
+            "bound": "hbm", "kernel": kernel, "achieved": achieved,
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-            "traffic": profiled_traffic(s.name), "alg_bytes_per_launch": vb,
-            "launch_us": r["verify_ms"] * 1e3,
+            "traffic": profiled_traffic(kernel, s.name), "alg_bytes_per_launch": vb,
+            "launch_us": launch_ms * 1e3,
+        },
+        "verify": {
+            "launch_us": r["verify_ms"] * 1e3, "alg_bytes_per_launch": r["verify_bytes"],
+            "achieved_GBs": r["verify_bytes"] / (r["verify_ms"] * 1e-3) / 1e9,
         },
         "commit": {
             "launch_us": r["commit_ms"] * 1e3, "alg_bytes_per_launch": r["commit_bytes"],

@@ -71,7 +71,8 @@ typedef enum {
     GDN_ERR_DIMS = -2,    /* sizes outside the supported range                   */
     GDN_ERR_DTYPE = -3,   /* io_dtype not a gdn_dtype                            */
     GDN_ERR_LAUNCH = -4,  /* a kernel launch failed                              */
-    GDN_ERR_ALIGN = -5    /* a device pointer is not 16-byte aligned             */
+    GDN_ERR_ALIGN = -5,   /* a device pointer is not 16-byte aligned             */
+    GDN_ERR_ALIAS = -6    /* two caches that must be distinct share a buffer     */
 } gdn_status;
 
 /* Problem sizes: B sequences (one draft tree each), N nodes per tree, h_k key
@@ -145,6 +146,39 @@ int gdn_tree_verify(const gdn_tree_dims* dims, const float* S0, const void* q,
 int gdn_tree_commit(const gdn_tree_dims* dims, const float* S_in, float* S_out,
                     const void* k, const gdn_tree_cache* cache, const int32_t* accepted,
                     int32_t* path, int32_t* path_len, hipStream_t stream);
+
+/*
+ * One decode step with the commit deferred into it (section 3: the state is
+ * committed once the accepted branch is known, and the pages' design folds it
+ * into the next iteration).  The results are those of
+ *
+ *   gdn_tree_commit(dims, S_prev, S_new, k_prev, cache_prev, accepted_prev,
+ *                   path_prev, path_len_prev, stream);
+ *   gdn_tree_verify(dims, S_new, q, k, v, beta, g, parent, o, cache, stream);
+ *
+ * but S_prev is read once: the committed state is formed on chip, written to
+ * S_new and used directly as the new tree's prefix state (fp32 rounding order
+ * may differ from the two-call sequence).
+ *
+ *   S_prev, S_new  [B][H_v][d_v][d_k] fp32  S_new may alias S_prev
+ *   k_prev, cache_prev, accepted_prev, path_prev, path_len_prev
+ *                  as for gdn_tree_commit (the previous tree)
+ *   q, k, v, beta, g, parent, o, cache
+ *                  as for gdn_tree_verify (the new tree)
+ *
+ * Both trees have the shape dims.  cache_prev is read while cache is written,
+ * so no buffer of one may be a buffer of the other (GDN_ERR_ALIAS); a decode
+ * loop alternates two caches.  Every size gdn_tree_verify accepts is
+ * accepted; the single-pass form covers d_k = d_v = 128 with bf16 io and
+ * N <= 128, other sizes run the two calls.
+ */
+int gdn_tree_commit_verify(const gdn_tree_dims* dims, const float* S_prev, float* S_new,
+                           const void* k_prev, const gdn_tree_cache* cache_prev,
+                           const int32_t* accepted_prev, int32_t* path_prev,
+                           int32_t* path_len_prev, const void* q, const void* k,
+                           const void* v, const float* beta, const float* g,
+                           const int32_t* parent, void* o, const gdn_tree_cache* cache,
+                           hipStream_t stream);
 
 /* Static description of a gdn_status value. */
 const char* gdn_tree_strerror(int status);

@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["gdn_tree_cache_bytes", "gdn_tree_commit", "gdn_tree_strerror",
-                     "gdn_tree_verify"]
+    assert names == ["gdn_tree_cache_bytes", "gdn_tree_commit", "gdn_tree_commit_verify",
+                     "gdn_tree_strerror", "gdn_tree_verify"]
     out = subprocess.run(["nm", "-D", "--defined-only", T.lib_path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)", out))
@@ -51,6 +51,11 @@ def C(d, ptrs, cache=None, tail=(None, None, None)):
     return T._lib.gdn_tree_commit(ctypes.byref(d) if d is not None else None, *ptrs,
                                   ctypes.byref(cache) if cache is not None else None,
                                   *tail, None)
+
+
+def CV(d, head, cache_prev, mid, cache):
+    r = lambda c: ctypes.byref(c) if c is not None else None
+    return T._lib.gdn_tree_commit_verify(r(d), *head, r(cache_prev), *mid, r(cache), None)
 
 
 FAKE = 0x10000          # a 16-byte-aligned pointer value, never dereferenced here
@@ -84,10 +89,24 @@ def test_error_codes():
     assert C(good, [FAKE, ODD, FAKE], cache, (FAKE,) * 3) == -5
     assert C(T.dims(0, 7, 1, 2, 16, 16, 0), [None] * 3, None) == 0
     assert C(T.dims(2, 7, 1, 2, 16, 16, 9), ok3, cache, (FAKE,) * 3) == -3
+    # fused commit + verify: the same checks, and the two caches must not share a buffer
+    other = T.Cache(FAKE + 256, FAKE + 512, FAKE + 768, FAKE + 1024, FAKE + 1280)
+    ok10 = [FAKE] * 10
+    assert CV(None, ok3, cache, ok10, other) == -1
+    assert CV(good, ok3, None, ok10, other) == -1
+    assert CV(good, ok3, cache, ok10[:4] + [None] + ok10[5:], other) == -1
+    assert CV(good, ok3, cache, ok10, T.Cache(FAKE, FAKE, ODD, FAKE, FAKE)) == -5
+    assert CV(good, [FAKE, ODD, FAKE], cache, ok10, other) == -5
+    assert CV(T.dims(2, 7, 1, 2, 16, 16, 5), ok3, cache, ok10, other) == -3
+    assert CV(T.dims(2, 0, 1, 2, 16, 16, 0), ok3, cache, ok10, other) == -2
+    assert CV(good, ok3, cache, ok10, cache) == -6
+    assert CV(good, ok3, other, ok10,
+              T.Cache(FAKE, FAKE, FAKE, FAKE + 1280, FAKE)) == -6
+    assert CV(T.dims(0, 7, 1, 2, 16, 16, 0), [None] * 3, None, [None] * 10, None) == 0
 
 
 def test_strerror_and_cache_bytes():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert T.gdn_tree_strerror(code) and T.gdn_tree_strerror(code) != "unknown gdn_status"
     assert T.gdn_tree_strerror(-99) == "unknown gdn_status"
     d = T.dims(3, 70, 2, 4, 32, 64, "bf16")

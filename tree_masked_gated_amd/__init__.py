@@ -16,7 +16,7 @@ from typing import Dict, Optional
 
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "Dims", "Cache", "lib_path", "dims",
-    "gdn_tree_cache_bytes", "gdn_tree_verify", "gdn_tree_commit",
+    "gdn_tree_cache_bytes", "gdn_tree_verify", "gdn_tree_commit", "gdn_tree_commit_verify",
     "gdn_tree_strerror", "TreeCache",
 ]
 
@@ -56,6 +56,9 @@ _lib.gdn_tree_verify.restype = _i
 _lib.gdn_tree_commit.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 3 + \
     [ctypes.POINTER(Cache)] + [_vp] * 3 + [_vp]
 _lib.gdn_tree_commit.restype = _i
+_lib.gdn_tree_commit_verify.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 3 + [ctypes.POINTER(Cache)] + \
+    [_vp] * 10 + [ctypes.POINTER(Cache), _vp]
+_lib.gdn_tree_commit_verify.restype = _i
 _lib.gdn_tree_strerror.argtypes = [_i]
 _lib.gdn_tree_strerror.restype = ctypes.c_char_p
 
@@ -200,6 +203,40 @@ def gdn_tree_commit(d: Dims, S_in, S_out, k, cache, accepted, path, path_len,
                               *tail, _stream(stream))
     if rc:
         raise GdnError(rc, "gdn_tree_commit")
+
+
+def gdn_tree_commit_verify(d: Dims, S_prev, S_new, k_prev, cache_prev, accepted_prev, path_prev,
+                           path_len_prev, q, k, v, beta, g, parent, o, cache, stream=None) -> None:
+    """Enqueue the previous tree's commit and the new tree's verification as one
+    step, the committed state used directly as the new prefix state (see
+    gdn_tree.h)."""
+    torch = _torch()
+    B, N, Hk, Hv, dk, dv = d.batch, d.n_nodes, d.h_k, d.h_v, d.d_k, d.d_v
+    io = _io_dtype(d)
+    for c in (cache_prev, cache):
+        if isinstance(c, TreeCache):
+            _check_cache(c, d)
+    head = [
+        _ptr(S_prev, (B, Hv, dv, dk), torch.float32, "S_prev"),
+        _ptr(S_new, (B, Hv, dv, dk), torch.float32, "S_new"),
+        _ptr(k_prev, (B, N, Hk, dk), io, "k_prev"),
+    ]
+    mid = [
+        _ptr(accepted_prev, (B,), torch.int32, "accepted_prev"),
+        _ptr(path_prev, (B, N), torch.int32, "path_prev"),
+        _ptr(path_len_prev, (B,), torch.int32, "path_len_prev"),
+        _ptr(q, (B, N, Hk, dk), io, "q"),
+        _ptr(k, (B, N, Hk, dk), io, "k"),
+        _ptr(v, (B, N, Hv, dv), io, "v"),
+        _ptr(beta, (B, N, Hv), torch.float32, "beta"),
+        _ptr(g, (B, N, Hv), torch.float32, "g"),
+        _ptr(parent, (B, N), torch.int32, "parent"),
+        _ptr(o, (B, N, Hv, dv), io, "o"),
+    ]
+    rc = _lib.gdn_tree_commit_verify(ctypes.byref(d), *head, ctypes.byref(_cache_struct(cache_prev)),
+                                     *mid, ctypes.byref(_cache_struct(cache)), _stream(stream))
+    if rc:
+        raise GdnError(rc, "gdn_tree_commit_verify")
 
 
 def _check_cache(c: TreeCache, d: Dims):

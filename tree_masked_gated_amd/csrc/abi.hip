@@ -94,6 +94,56 @@ int gdn_tree_commit(const gdn_tree_dims* dims, const float* S_in, float* S_out,
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+int gdn_tree_commit_verify(const gdn_tree_dims* dims, const float* S_prev, float* S_new,
+                           const void* k_prev, const gdn_tree_cache* cache_prev,
+                           const int32_t* accepted_prev, int32_t* path_prev,
+                           int32_t* path_len_prev, const void* q, const void* k,
+                           const void* v, const float* beta, const float* g,
+                           const int32_t* parent, void* o, const gdn_tree_cache* cache,
+                           hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->batch == 0) return GDN_OK;
+    if (!S_prev || !S_new || !k_prev || !accepted_prev || !path_prev || !path_len_prev || !q || !k ||
+        !v || !beta || !g || !parent || !o)
+        return GDN_ERR_NULL;
+    rc = check_cache(cache_prev);
+    if (rc) return rc;
+    rc = check_cache(cache);
+    if (rc) return rc;
+    if (misaligned(S_prev) || misaligned(S_new) || misaligned(k_prev) || misaligned(accepted_prev) ||
+        misaligned(path_prev) || misaligned(path_len_prev) || misaligned(q) || misaligned(k) ||
+        misaligned(v) || misaligned(beta) || misaligned(g) || misaligned(parent) || misaligned(o))
+        return GDN_ERR_ALIGN;
+    const void* prev_bufs[] = {cache_prev->anc_mask, cache_prev->depth, cache_prev->u,
+                               cache_prev->log_gamma, cache_prev->tree_status};
+    const void* new_bufs[] = {cache->anc_mask, cache->depth, cache->u, cache->log_gamma,
+                              cache->tree_status};
+    for (const void* x : prev_bufs)
+        for (const void* y : new_bufs)
+            if (x == y) return GDN_ERR_ALIAS;
+
+    CommitArgs c{dims->batch, dims->n_nodes, dims->h_k, dims->h_v, dims->d_k, dims->d_v,
+                 S_prev, S_new, k_prev, cache_prev->anc_mask, cache_prev->u, cache_prev->log_gamma,
+                 cache_prev->tree_status, accepted_prev, path_prev, path_len_prev};
+    VerifyArgs a{dims->batch, dims->n_nodes, dims->h_k, dims->h_v, dims->d_k, dims->d_v,
+                 S_prev, q, k, v, beta, g, parent, o,
+                 cache->anc_mask, cache->depth, cache->u, cache->log_gamma,
+                 cache->tree_status};
+    hipError_t e;
+    if (verify_tiled_supported(a, dims->io_dtype)) {
+        e = launch_commit_verify_tiled(a, c, dims->io_dtype, stream);
+    } else {
+        e = launch_commit(c, dims->io_dtype, stream);
+        if (e == hipSuccess) {
+            a.S0 = S_new;
+            e = verify_large_supported(a, dims->io_dtype) ? launch_verify_large(a, dims->io_dtype, stream)
+                                                           : launch_verify_generic(a, dims->io_dtype, stream);
+        }
+    }
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 const char* gdn_tree_strerror(int status) {
     switch (status) {
         case GDN_OK: return "ok";
@@ -102,6 +152,7 @@ const char* gdn_tree_strerror(int status) {
         case GDN_ERR_DTYPE: return "io_dtype is not GDN_F32 or GDN_BF16";
         case GDN_ERR_LAUNCH: return "a kernel launch failed";
         case GDN_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+        case GDN_ERR_ALIAS: return "two caches that must be distinct share a buffer";
         default: return "unknown gdn_status";
     }
 }

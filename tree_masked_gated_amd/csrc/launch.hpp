@@ -14,6 +14,8 @@ hipError_t launch_verify_generic(const VerifyArgs& a, int io, hipStream_t stream
 // MFMA verification: d_k = d_v = 128, bf16 io, up to 128 nodes.
 bool verify_tiled_supported(const VerifyArgs& a, int io);
 hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream);
+// The same with the previous tree's commit fused in front (a.S0 = c.S_in).
+hipError_t launch_commit_verify_tiled(const VerifyArgs& a, const CommitArgs& c, int io, hipStream_t stream);
 
 // MFMA verification of larger trees: d_k = d_v = 128, bf16 io, 129 .. 512 nodes
 // (two launches: the tree's ancestor rows into the cache, then the solve).

@@ -67,8 +67,11 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // Waves: four per value head; wave (hp, wc) owns value columns 32 wc .. +31 of
 // head h0 + hp as two 16-column groups, so every k / q / tile fragment it
 // reads from LDS feeds two MFMA chains.
-template <int NB, int HPW>
-__global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a, int nitems) {
+// FUSED: the kernel first commits the previous tree's accepted node (args c;
+// its state is this launch's S0, a.S0 = c.S_in) into the S0 rows each wave
+// holds, writes them to c.S_out and verifies with them (see the commit prologue).
+template <int NB, int HPW, bool FUSED>
+__global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a, CommitArgs c, int nitems) {
     constexpr int WPH = 4;                      // waves per value head
     constexpr int CG = 2;                       // 16-column groups per wave
     constexpr int NW = WPH * HPW;               // waves
@@ -156,7 +159,8 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     // fills 1 KB (4 rows) of LDS, lane l landing on row r0 + l/16, physical chunk
     // l%16, which holds logical chunk (l%16) ^ (row & 15).  Rows past N copy
     // row N-1 (finite values; masks and beta = 0 keep them out of every result).
-    auto kq_dma = [&](int it) {
+    // (real = false: a placeholder after the last item, every lane reading one line)
+    auto kq_dma = [&](int it, bool real) {
         int b, hk, hg;
         decode(it, b, hk, hg);
         const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
             const int mat = ins / (NP / 4), r0 = (ins % (NP / 4)) * 4;
             const int row = r0 + (lane >> 4), pc = lane & 15;
             const int srow = row < N ? row : N - 1;
-            const uint16_t* src = (mat ? Qb : Kb) + (size_t)srow * Hk * kD + ((pc ^ (row & 15)) << 3);
+            const uint16_t* src = real ? (mat ? Qb : Kb) + (size_t)srow * Hk * kD + ((pc ^ (row & 15)) << 3) : Kb;
             uint16_t* dst = (mat ? s_q : s_k) + r0 * kD;
             __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
         }
@@ -305,9 +309,225 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 #pragma unroll
     for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
 
+    // ---- commit of the previous tree (FUSED) ----------------------------------
+    // Page section 3 defers the commit of the accepted node to the next step;
+    // here it runs on the S0 rows each wave holds for the item (s0raw, which
+    // hold S_prev): S_a = e^(G_a) S_prev + sum_{j in P} e^(G_a - G_j) u_j k_j^T
+    // with G, u from the previous tree's cache and k its keys.  P is the
+    // accepted node with its ancestors (its ancestor row), enumerated root
+    // first: slot m < |P| - 1 is the m-th set bit of the row, the last slot the
+    // accepted node.  The update is a rank-|P| product on the matrix cores:
+    // per 32 path slots, D^T += K_P^T (w u_P) with K_P^T (key column x slot,
+    // bf16 inputs, exact) and w u_P (slot x value row) split into bf16 hi + lo,
+    // staged transposed in the tile area (free until the Gram).  D^T comes out
+    // in exactly the layout s0raw holds.  The committed rows go to c.S_out and
+    // become this item's S0; one item per sequence writes the previous tree's
+    // path.  Latency is hidden by prefetch: the accepted node and tree status
+    // load with the item's small loads one item ahead, the ancestor row at the
+    // end of the item before, and the first 32 slots' k / u rows and log-gates
+    // at the item's start, landing with its tree.
+    constexpr int SLOT_BYTES = kD * 2 + HPW * kD * 4;           // k column, w u hi + lo
+    constexpr int PC_ROOM = ((int)sizeof(s_tiles) - NW * NP * 4) / SLOT_BYTES;
+    constexpr int PC = PC_ROOM >= 32 ? 32 : PC_ROOM >= 16 ? 16 : 8;
+    static_assert(PC * SLOT_BYTES <= (int)sizeof(s_tiles), "path staging fits the tile area");
+    constexpr int KR = FUSED ? (PC * 16 + NT - 1) / NT : 0;     // k loads per thread
+    constexpr int UR = FUSED ? (HPW * PC * 32 + NT - 1) / NT : 0;   // u loads per thread
+    int cm_acc_v = 0, cm_st_v = 0;              // loads in flight
+    int cm_acc = 0, cm_st = 0;                  // the same, uniform
+    uint32_t cm_row_v[MW];
+#pragma unroll
+    for (int w = 0; w < MW; ++w) cm_row_v[w] = 0u;
+    uint32_t pw[MW];                            // this item: path row (uniform)
+    int plen = -1;                              // |P|; 0 nothing accepted, -1 no commit
+    u32x4 st_k[KR > 0 ? KR : 1];
+    float4 st_u[UR > 0 ? UR : 1];
+    float st_lj[UR > 0 ? UR : 1];
+    float st_la[HPW];
+    // staging, transposed: kT[kk][slot], wh / wl[head][value row][slot]; slots
+    // past the path are zero.  After it, each wave's slot -> node table.
+    uint16_t* const kT = reinterpret_cast<uint16_t*>(&s_tiles[0][0]);
+    uint16_t* const wh = kT + kD * PC;
+    uint16_t* const wl = wh + HPW * kD * PC;
+    int* const ptab = reinterpret_cast<int*>(wl + HPW * kD * PC) + wave * NP;
+    static_assert(PC * SLOT_BYTES + NW * NP * 4 <= (int)sizeof(s_tiles), "slot tables fit");
+    static_assert(MW == 2 * NPL && NP % PC == 0, "word / lane split of the path row");
+    auto commit_small = [&](int it) {
+        int b, hk, hg;
+        decode(it, b, hk, hg);
+        cm_acc_v = c.accepted[b];
+        cm_st_v = c.status[b];
+    };
+    auto commit_take_small = [&]() {
+        cm_acc = __builtin_amdgcn_readfirstlane(cm_acc_v);
+        cm_st = __builtin_amdgcn_readfirstlane(cm_st_v);
+    };
+    auto commit_row = [&](int it) {
+        int b, hk, hg;
+        decode(it, b, hk, hg);
+        const uint32_t* prow = c.anc_mask + ((size_t)b * N + min(max(cm_acc, 0), N - 1)) * W;
+#pragma unroll
+        for (int w = 0; w < MW; ++w) cm_row_v[w] = prow[min(w, W - 1)];
+    };
+    auto commit_path = [&]() {
+        const bool valid = cm_st == 0 && cm_acc >= -1 && cm_acc < N;
+        int pc = 0;
+#pragma unroll
+        for (int w = 0; w < MW; ++w) {
+            const uint32_t x = (uint32_t)__builtin_amdgcn_readfirstlane((int)cm_row_v[w]);
+            pw[w] = (w < W && valid && cm_acc >= 0) ? x : 0u;
+            pc += __popc(pw[w]);
+        }
+        plen = valid ? (cm_acc < 0 ? 0 : pc + 1) : -1;
+        // slot -> node table, one private copy per wave: lane l tests nodes
+        // l + 64k, a set bit's slot is its rank among the set bits
+        int base = 0;
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+            const uint32_t word = lane < 32 ? pw[2 * k] : pw[2 * k + 1];
+            const bool on = (word >> (lane & 31)) & 1u;
+            const uint64_t bal = __ballot(on);
+            const int rank = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (on) ptab[rank] = lane + 64 * k;
+            base += __popcll(bal);
+        }
+        asm volatile("" ::: "memory");
+    };
+    // node of path slot s (s < plen); other slots: the accepted node (clamped),
+    // so that every load stays in bounds and padding rereads a cached row
+    auto slot_node = [&](int s) {
+        const int last = min(max(cm_acc, 0), N - 1);
+        const int t = ptab[s];                          // s < NP: always in the table
+        return s < plen - 1 ? min(t, N - 1) : last;
+    };
+    auto commit_issue = [&](int b, int hk, int h0, int p0) {
+        const uint16_t* Kp = static_cast<const uint16_t*>(c.k) + (size_t)b * N * Hk * kD + hk * kD;
+        const float* Up = c.u + ((size_t)b * Hv + h0) * (size_t)N * kD;
+        const float* lgprev = c.log_gamma + ((size_t)b * Hv + h0) * N;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const int x = min(tid + r * NT, PC * 16 - 1);
+            const int m = x % PC, ck = x / PC;
+            const int j = slot_node(p0 + m);
+            st_k[r] = *reinterpret_cast<const u32x4*>(Kp + (size_t)j * Hk * kD + 8 * ck);
+        }
+#pragma unroll
+        for (int r = 0; r < UR; ++r) {
+            const int x = min(tid + r * NT, HPW * PC * 32 - 1);
+            const int m = x % PC, f = (x / PC) % 32, p = x / (PC * 32);
+            const int j = slot_node(p0 + m);
+            st_u[r] = *reinterpret_cast<const float4*>(Up + ((size_t)p * N + j) * kD + 4 * f);
+            st_lj[r] = lgprev[(size_t)p * N + j];
+        }
+        const int ja = min(max(cm_acc, 0), N - 1);
+#pragma unroll
+        for (int p = 0; p < HPW; ++p) st_la[p] = lgprev[(size_t)p * N + ja];
+    };
+    auto commit_stage = [&](int p0) {
+        const int pn = plen - p0;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const int x = tid + r * NT;
+            if (PC * 16 % NT == 0 || x < PC * 16) {
+                const int m = x % PC, ck = x / PC;
+                const u32x4 kv = m < pn ? st_k[r] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kT[(8 * ck + 2 * e) * PC + m] = (uint16_t)(kv[e] & 0xffffu);
+                    kT[(8 * ck + 2 * e + 1) * PC + m] = (uint16_t)(kv[e] >> 16);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < UR; ++r) {
+            const int x = tid + r * NT;
+            if (HPW * PC * 32 % NT == 0 || x < HPW * PC * 32) {
+                const int m = x % PC, f = (x / PC) % 32, p = x / (PC * 32);
+                const float wgt = __expf(st_la[p] - st_lj[r]);
+                const float uu[4] = {st_u[r].x, st_u[r].y, st_u[r].z, st_u[r].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float val = m < pn ? wgt * uu[i] : 0.f;
+                    const uint16_t hi = bf16_rne(val);
+                    const int at = (p * kD + 4 * f + i) * PC + m;
+                    wh[at] = hi;
+                    wl[at] = bf16_rne(val - bf16_val(hi));
+                }
+            }
+        }
+    };
+    auto commit_apply = [&](int b, int hk, int hg, int h0, int h) {
+        if (hk == 0 && hg == 0) {
+            for (int m = tid; m < N; m += NT) c.path[(size_t)b * N + m] = m < plen ? slot_node(m) : -1;
+            if (tid == 0) c.path_len[b] = plen;
+        }
+        if (plen > 0) {
+            const float dec = __expf(st_la[hp]);
+#pragma unroll
+            for (int g = 0; g < CG; ++g)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; ++q2) {
+                        s0raw[g][cc][q2].x *= dec; s0raw[g][cc][q2].y *= dec;
+                        s0raw[g][cc][q2].z *= dec; s0raw[g][cc][q2].w *= dec;
+                    }
+            const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+            const bool lane_on = 8 * lq < PC;               // K = 32 operand lanes past PC slots: 0
+            const int lqs = lane_on ? lq : 0;
+            for (int p0 = 0;;) {
+                bf16x8 bh[CG], bl[CG];
+#pragma unroll
+                for (int g = 0; g < CG; ++g) {
+                    const int row = col0 + 8 * (ln >> 2) + 4 * g + (ln & 3);
+                    const int at = (hp * kD + row) * PC + 8 * lqs;
+                    bh[g] = lane_on ? *reinterpret_cast<const bf16x8*>(wh + at) : zero8;
+                    bl[g] = lane_on ? *reinterpret_cast<const bf16x8*>(wl + at) : zero8;
+                }
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; ++q2) {
+                        const int kk = 32 * cc + 8 * (ln >> 2) + 4 * q2 + (ln & 3);
+                        const bf16x8 ak = lane_on ? *reinterpret_cast<const bf16x8*>(kT + kk * PC + 8 * lqs) : zero8;
+#pragma unroll
+                        for (int g = 0; g < CG; ++g) {
+                            f32x4 d = __builtin_bit_cast(f32x4, s0raw[g][cc][q2]);
+                            d = mfma32(ak, bh[g], d);
+                            d = mfma32(ak, bl[g], d);
+                            s0raw[g][cc][q2] = __builtin_bit_cast(float4, d);
+                        }
+                    }
+                p0 += PC;
+                lds_barrier();                              // staging read by every wave
+                if (p0 >= plen) break;
+                commit_issue(b, hk, h0, p0);
+                wait_vmem_all();
+                commit_stage(p0);
+                lds_barrier();
+            }
+        }
+        // this wave's rows of the committed state, where S0 was read from
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+            const int row = col0 + 8 * (ln >> 2) + 4 * g + (ln & 3);
+            float* p = c.S_out + ((size_t)b * Hv + h) * kD * kD + (size_t)row * kD + 8 * lq;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                *reinterpret_cast<float4*>(p + 32 * cc) = s0raw[g][cc][0];
+                *reinterpret_cast<float4*>(p + 32 * cc + 4) = s0raw[g][cc][1];
+            }
+        }
+    };
+
     int item = blockIdx.x;                                    // grid <= nitems
     load_small(item, true);
-    kq_dma(item);
+    if constexpr (FUSED) {
+        commit_small(item);
+        commit_take_small();
+        commit_row(item);
+    }
+    kq_dma(item, true);
 #pragma unroll
     for (int g = 0; g < CG; ++g) load_s0(item, g, true);
 
@@ -325,6 +545,10 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         const int h = h0 + hp;
         const size_t vo_base = ((size_t)b * N * Hv + h) * kD;     // node 0 of head h
         lds_barrier();                                        // LDS of the last item is free
+        if constexpr (FUSED) {                                // the previous tree's path rows
+            commit_path();
+            commit_issue(b, hk, h0, 0);
+        }
 
         // ---- 1. tree and path log-gates (wave 0), beta (threads 64 ..) -------
         if (wave == 0) {
@@ -339,8 +563,10 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         // anything still in flight: one wait covers both, the barrier publishes
         // every wave's copies and the tree.
         wait_vmem_all();
+        if constexpr (FUSED) commit_stage(0);
         lds_barrier();
         const int status = __builtin_amdgcn_readfirstlane(s_flag);   // uniform branch below
+        if constexpr (FUSED) commit_apply(b, hk, hg, h0, h);
         uint16_t* O = static_cast<uint16_t*>(a.o);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         u32x4 vfr[NB];                                // node 16t + l%16, columns col0 + 8(l/16)..+7
@@ -459,6 +685,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         // stores retire in order).  One program point for both paths, so no
         // register copy of a load in flight is needed where they meet.
         load_small(pf, more);
+        if constexpr (FUSED) commit_small(pf);
 #pragma unroll
         for (int g = 0; g < CG; ++g) load_s0(pf, g, more);
         if (!status) {
@@ -484,6 +711,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         // v landed: only the 8 * CG S0 loads issued last may still be in flight
         // (the explicit count lets them overlap the solve).
         wait_vmem_le<8 * CG>();
+        if constexpr (FUSED) commit_take_small();
         if (wave == NW - 1) write_tree_cache(b, h0, hk == 0 && hg == 0, status);
         // ---- 5. per wave: projection, blocked substitution, output ---------
         //   sb[g][cs]   S0 rows of group g (local row l%16): B operand of K S0^T, A
@@ -589,7 +817,12 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
             }
         }
         lds_barrier();                                      // k / q in LDS are free now
-        if (more) kq_dma(nxt);                                // the next item's k / q
+        if constexpr (FUSED) commit_row(pf);                  // ahead of the k / q rows
+        // the next item's k / q.  Fused: issued after the last item too, so that
+        // every path into the next item has the same loads in flight after the
+        // ancestor row (the wait for it then leaves the copies running)
+        if constexpr (FUSED) kq_dma(pf, more);
+        else if (more) kq_dma(nxt, true);
     }
 }
 
@@ -599,15 +832,15 @@ bool verify_tiled_supported(const VerifyArgs& a, int io) {
     return io == GDN_BF16 && a.dk == kD && a.dv == kD && a.N <= 128;
 }
 
-hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream) {
-    (void)io;
+template <bool FUSED>
+static hipError_t launch_tiled(const VerifyArgs& a, const CommitArgs& c, hipStream_t stream) {
     const int G = a.Hv / a.Hk;
     const int hpw = (G % 2 == 0) ? 2 : 1;
     const void* fn;
     if (a.N <= 64)
-        fn = hpw == 2 ? (const void*)verify_tiled_kernel<4, 2> : (const void*)verify_tiled_kernel<4, 1>;
+        fn = hpw == 2 ? (const void*)verify_tiled_kernel<4, 2, FUSED> : (const void*)verify_tiled_kernel<4, 1, FUSED>;
     else
-        fn = hpw == 2 ? (const void*)verify_tiled_kernel<8, 2> : (const void*)verify_tiled_kernel<8, 1>;
+        fn = hpw == 2 ? (const void*)verify_tiled_kernel<8, 2, FUSED> : (const void*)verify_tiled_kernel<8, 1, FUSED>;
     int nitems = a.B * a.Hk * (G / hpw);
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -615,9 +848,20 @@ hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream) 
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)(nitems < cus ? nitems : cus);
-    VerifyArgs copy = a;
-    void* args[] = {&copy, &nitems};
+    VerifyArgs va = a;
+    CommitArgs ca = c;
+    void* args[] = {&va, &ca, &nitems};
     return hipLaunchKernel(fn, dim3(grid), dim3(256 * hpw), args, 0, stream);
+}
+
+hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream) {
+    (void)io;
+    return launch_tiled<false>(a, CommitArgs{}, stream);
+}
+
+hipError_t launch_commit_verify_tiled(const VerifyArgs& a, const CommitArgs& c, int io, hipStream_t stream) {
+    (void)io;
+    return launch_tiled<true>(a, c, stream);
 }
 
 }  // namespace gdn
