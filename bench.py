@@ -4,17 +4,22 @@ A step is one decode iteration of the 36-layer stack: for every layer, verify
 all 64 draft trees (128 nodes, M = 8 wide, 16 deep; 16 key / 32 value heads,
 d = 128, bf16 q/k/v, fp32 state) and commit each sequence's accepted node.
 The committed states of step t are the prefix states of step t + 1, as in a
-decode loop.  All inputs are synthetic (workloads.py) and resident in HBM
+decode loop.  By default each layer is one launch of gdn_tree_commit_verify:
+the commit of the tree verified at the previous step, then this step's
+verification on the committed state (the tree verified before the first timed
+step is primed untimed).  --unfused times gdn_tree_verify + gdn_tree_commit
+per layer instead.  All inputs are synthetic (workloads.py) and resident in HBM
 before the timed region starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--unfused]
 
 Prints one JSON line.  value = B * N * layers * K / elapsed, i.e. nodes per
-second per layer (each layer call verifies B * N nodes).  The roofline block
-reports the dominant kernel (verification): algorithmic bytes per launch over
-its average launch time, measured here with HIP events on the launch stream.
-The cpu_baseline block times the fp64 oracle (path-walk mode) on a bounded
-sample of the same workload on the host cores.
+second per layer (each layer call verifies B * N nodes and commits B paths).
+The roofline block reports the dominant kernel (the fused launch, or the
+verification when unfused): algorithmic bytes per launch over its average
+launch time, measured here with HIP events on the launch stream.  The
+cpu_baseline block times the fp64 oracle (path-walk mode) on a bounded sample
+of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -278,8 +283,8 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
-    ap.add_argument("--fused", action="store_true",
-                    help="one launch per layer: commit the previous tree, verify the next")
+    ap.add_argument("--unfused", dest="fused", action="store_false",
+                    help="verify and commit as two launches per layer")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -326,7 +331,7 @@ def main():
             "workload": s.name, "batch": s.batch, "n_nodes": s.n_nodes, "layers": L,
             "tree": f"{s.width}-ary x depth {s.depth}" if s.tree == "mary" else s.tree,
             "h_k": s.h_k, "h_v": s.h_v, "d_k": s.d, "d_v": s.d, "io": s.io,
-            "state": "f32",
+            "state": "f32", "launches": "commit_verify" if args.fused else "verify+commit",
         },
         "roofline": {
             "bound": "hbm", "kernel": kernel, "achieved": achieved,
