@@ -8,14 +8,15 @@
 //  - tree_prep_kernel, one workgroup per sequence, validates the parent row
 //    and writes the strict-ancestor bit rows, depth and status to the cache;
 //  - verify_large_kernel, one workgroup per (sequence, value head, column
-//    slice), walks the 16-node block rows t in order.  For row t it computes
+//    slice), walks the 16-node block rows t in order.  For each row it computes
 //    only the Gram tiles (t, s) whose nodes have an ancestor pair (a tile
-//    occupancy taken from the ancestor rows), spread over the waves, stages the
-//    masked, decayed tiles in an LDS row buffer (two of them, alternating), and
-//    after one barrier every wave runs row t of the blocked substitution and the
-//    output stage for its 16 value columns, two node blocks per MFMA.
+//    occupancy taken from the ancestor rows), spread over the waves, into an
+//    LDS row buffer (two of them, alternating); every wave runs the row's
+//    blocked substitution and output stage for its 16 value columns, two node
+//    blocks per MFMA.  Row t + 1's tiles are computed while row t is solved, so
+//    one barrier per row separates them.
 // k / q rows are read from global memory (L2) straight into MFMA operand
-// registers; the next row's are requested before the current row's solve.
+// registers, a row ahead of their use.
 #include "gdn_common.hpp"
 #include "launch.hpp"
 #include "mfma_tiles.hpp"
@@ -42,11 +43,20 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
     if (threadIdx.x == 0) a.status[b] = status;
 }
 
-// The index of the k-th set bit (k >= 0) of a wave-uniform 64-bit mask.
-__device__ __forceinline__ int nth_bit64(uint64_t m, int k) {
-    for (int i = 0; i < k; ++i) m &= m - 1;
-    return __ffsll((unsigned long long)m) - 1;
+// x of lane k of each lane quad, to all four lanes (k a compile-time value
+// once the caller's loop is unrolled).
+__device__ __forceinline__ float quad_bcast(float x, int k) {
+    const int v = __float_as_int(x);
+    switch (k) {
+        case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false));
+        case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x55, 0xf, 0xf, false));
+        case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xaa, 0xf, 0xf, false));
+        default: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xff, 0xf, 0xf, false));
+    }
 }
+
+typedef __attribute__((address_space(1))) const void* kgptr_t;
+typedef __attribute__((address_space(3))) void* klptr_t;
 
 // A/B fragment of a 16-node block of k or q straight from global memory: lane
 // l gets row 16 blk + l % 16 (clamped to N - 1), columns 32 cs + 8 (l / 16)..+7.
@@ -57,11 +67,21 @@ __device__ __forceinline__ bf16x8 g_frag(const uint16_t* base, size_t row_stride
                                           base + (size_t)row * row_stride + 32 * cs + 8 * (lane >> 4)));
 }
 
-template <int NB, int NWV>
-__global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a, int csplit) {
+// Waves 0 .. NS-1 solve: wave w owns value columns col0 = 64 slice + 16 w.
+// Waves NS .. 2 NS-1 are Gram waves: they compute the next block row's tiles
+// and, for column group w - NS, its projections K_t S0^T and S0 Q_t^T into
+// LDS, while the solve waves run the current row; one barrier per row.  The
+// two roles run separate loops with the same barrier count, so neither
+// keeps the other's registers.
+template <int NB>
+__global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int csplit) {
     constexpr int NP = 16 * NB;                 // padded node count
-    constexpr int NT = 64 * NWV;
+    constexpr int NT = 512;
+    constexpr int NS = 4;                       // solve waves (= Gram waves)
     constexpr int NPR = NB / 2;                 // U pairs
+    constexpr int TPW = 4;                      // tiles per Gram wave requested a row ahead
+    constexpr int KC = 16;                      // node blocks whose k rows are cached in LDS
+    constexpr bool KALL = NB <= KC;             // every block cached: no k rows from L2 in the Gram
     // -X and Y tiles of one block row, by column block s, for rows of either
     // parity; a spare tile at the end (a pair read may run 512 bytes past the
     // last tile; those lanes are zeroed before use)
@@ -69,21 +89,29 @@ __global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a,
     __shared__ __attribute__((aligned(16))) uint16_t s_yrow[2][NB * 256 + 256];
     __shared__ __attribute__((aligned(16))) uint16_t s_dinv[2][256];
     __shared__ __attribute__((aligned(16))) float s_xd[2][256];
+    __shared__ __attribute__((aligned(16))) f32x4 s_pk[2][NS][64];   // K_t S0^T, accumulator layout
+    __shared__ __attribute__((aligned(16))) f32x4 s_pq[2][NS][64];   // S0 Q_t^T
     __shared__ __attribute__((aligned(16))) float s_lg[NP];
     __shared__ __attribute__((aligned(16))) float s_beta[NP];
     __shared__ __attribute__((aligned(16))) int32_t s_jump[NP];
     __shared__ unsigned long long s_occ[NB];    // bit s of row t: tile (t, s), s < t, not all zero
-    __shared__ int s_flag;
+    __shared__ uint8_t s_tcol[NB][NB];          // row t's tiles: t, then its occupied blocks s < t
+    // k rows of blocks 0 .. KC-1 in MFMA operand order: (block s, chunk cs) is
+    // 1 KB, lane l's 16 bytes at l * 16 (row 16 s + l % 16, columns 32 cs +
+    // 8 (l / 16) .. +7), so a fragment read is one conflict-free ds_read_b128
+    __shared__ __attribute__((aligned(16))) uint16_t s_kc[KC * 4 * 512];
 
     const int N = a.N, Hv = a.Hv, Hk = a.Hk, G = Hv / Hk;
     const int W = (N + 31) / 32;
     const int nblk = (N + 15) / 16;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool solver = wave < NS;
+    const int cg = solver ? wave : wave - NS;           // column group (solve, or projections)
     const int item = blockIdx.x;
     const int slice = item % csplit, bh = item / csplit;
     const int h = bh % Hv, b = bh / Hv, hk = h / G;
-    const int col0 = slice * (16 * NWV) + 16 * wave;   // this wave's 16 value columns
+    const int col0 = slice * (16 * NS) + 16 * cg;
     const size_t vo_row = (size_t)Hv * kD;
     const size_t vo_base = ((size_t)b * N * Hv + h) * kD;
     uint16_t* O = static_cast<uint16_t*>(a.o);
@@ -92,17 +120,34 @@ __global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a,
     const int status = a.status[b];
     if (status) {                                       // invalid tree: NaN outputs
         const float qnan = __uint_as_float(0x7fc00000u);
-        for (int x = lane; x < N * 16; x += 64) {
-            const int i = x / 16, c = col0 + x % 16;
-            O[vo_base + (size_t)i * vo_row + c] = 0x7fc0;
-            Ug[(size_t)i * kD + c] = qnan;
-        }
+        if (solver)
+            for (int x = lane; x < N * 16; x += 64) {
+                const int i = x / 16, c = col0 + x % 16;
+                O[vo_base + (size_t)i * vo_row + c] = 0x7fc0;
+                Ug[(size_t)i * kD + c] = qnan;
+            }
         if (slice == 0)
             for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = qnan;
         return;
     }
 
+    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + ((size_t)b * N * Hk + hk) * kD;
+    const size_t kq_row = (size_t)Hk * kD;
+    // k rows of the cached blocks straight into LDS (direct-to-LDS loads, one
+    // 1 KB chunk per instruction), landing while the tree's gates are summed
+    {
+        const int ncb = min(nblk, KC);
+        for (int x = wave; x < ncb * 4; x += NT / 64) {
+            const int sblk = x >> 2, cs = x & 3;
+            const int row = min(16 * sblk + ln, N - 1);
+            __builtin_amdgcn_global_load_lds((kgptr_t)(Kb + (size_t)row * kq_row + 32 * cs + 8 * lq),
+                                             (klptr_t)(s_kc + x * 512), 16, 0, 0);
+        }
+    }
+
     // ---- path log-gates G (synchronous pointer doubling), beta, occupancy ----
+    const uint32_t* gmask = a.anc_mask + (size_t)b * N * W;
     for (int i = tid; i < NP; i += NT) {
         const bool v = i < N;
         s_jump[i] = v ? a.parent[(size_t)b * N + i] : -1;
@@ -111,10 +156,26 @@ __global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a,
     }
     for (int t = tid; t < NB; t += NT) s_occ[t] = 0ull;
     __syncthreads();
+    {
+        // occupancy: OR of the ancestor words of block t's rows, word w covering
+        // column blocks 2w and 2w + 1 (the 16 row loads issued together)
+        for (int x = tid; x < nblk * W; x += NT) {
+            const int t = x / W, w = x % W;
+            uint32_t r[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) r[i] = gmask[(size_t)min(16 * t + i, N - 1) * W + w];
+            uint32_t acc = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc |= r[i];
+            const unsigned long long bits = ((acc & 0xffffu) ? 1ull << (2 * w) : 0ull) |
+                                            ((acc >> 16) ? 1ull << (2 * w + 1) : 0ull);
+            if (bits) atomicOr(&s_occ[t], bits);
+        }
+    }
     for (;;) {
-        int nn[NP / NT > 0 ? NP / NT : 1];
-        float gj[NP / NT > 0 ? NP / NT : 1];
         constexpr int PER = NP / NT > 0 ? NP / NT : 1;
+        int nn[PER];
+        float gj[PER];
         bool act = false;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
@@ -137,153 +198,243 @@ __global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a,
     }
     if (slice == 0)
         for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
-    {
-        // occupancy: OR of the ancestor words of block t's rows, word w covering
-        // column blocks 2w and 2w + 1
-        const uint32_t* gm = a.anc_mask + (size_t)b * N * W;
-        for (int x = tid; x < nblk * W; x += NT) {
-            const int t = x / W, w = x % W;
-            uint32_t acc = 0;
-            for (int i = 16 * t; i < min(16 * t + 16, N); ++i) acc |= gm[(size_t)i * W + w];
-            const unsigned long long bits = ((acc & 0xffffu) ? 1ull << (2 * w) : 0ull) |
-                                            ((acc >> 16) ? 1ull << (2 * w + 1) : 0ull);
-            if (bits) atomicOr(&s_occ[t], bits);
+
+    for (int t = tid; t < nblk; t += NT) {              // tile lists (occupancy complete)
+        unsigned long long occ = s_occ[t] & ((1ull << t) - 1ull);
+        s_tcol[t][0] = (uint8_t)t;
+        for (int m = 1; occ; ++m) {
+            s_tcol[t][m] = (uint8_t)(__ffsll((unsigned long long)occ) - 1);
+            occ &= occ - 1ull;
         }
     }
-
-    // this wave's S0 rows (value columns col0 + l%16) as bf16 B / A operands
-    bf16x8 sb[4];
-    {
-        const float* p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(col0 + ln) * kD + 8 * lq;
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs)
-            sb[cs] = to_bf16x8(*reinterpret_cast<const float4*>(p + 32 * cs),
-                               *reinterpret_cast<const float4*>(p + 32 * cs + 4));
-    }
+    wait_vmem_all();                                    // the cached k rows have landed
     __syncthreads();
-
-    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
-    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + ((size_t)b * N * Hk + hk) * kD;
-    const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + vo_base + col0 + 4 * lq;
-    const size_t kq_row = (size_t)Hk * kD;
-    const uint32_t* gmask = a.anc_mask + (size_t)b * N * W;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const s16x4 zero4 = {0, 0, 0, 0};
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    auto row_occ = [&](int t) __attribute__((always_inline)) {
+        // (readfirstlane returns a signed int: widen through uint32_t, and keep
+        // only column blocks 0 .. t - 1)
+        return (((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(s_occ[t] >> 32)) << 32) |
+                (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)s_occ[t])) &
+               ((1ull << t) - 1ull);
+    };
+
+    if (!solver) {
+        // ================= Gram waves =================
+        const int gw = cg;
+        // this wave's column group's S0 rows as bf16 B / A operands
+        bf16x8 sb[4];
+        {
+            const float* p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(col0 + ln) * kD + 8 * lq;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs)
+                sb[cs] = to_bf16x8(*reinterpret_cast<const float4*>(p + 32 * cs),
+                                   *reinterpret_cast<const float4*>(p + 32 * cs + 4));
+        }
+        // k / q fragment of node block blk, column chunk cs, from global memory
+        // (L2): the block's base is uniform, the lane's row / column a 32-bit
+        // offset (rows clamped to N - 1)
+        const uint32_t lane_col = 16u * lq;                 // bytes: 8 bf16 per lane group
+        auto frag = [&](const uint16_t* base, int blk, int cs) __attribute__((always_inline)) {
+            const uint32_t row = (uint32_t)min(16 * blk + ln, N - 1);
+            const uint32_t off = row * (uint32_t)(kq_row * 2) + lane_col + 64u * cs;
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                  reinterpret_cast<const char*>(base) + off));
+        };
+        // Gram products of tile (t, s): A = K_s K_t^T, C = K_s Q_t^T (node j of
+        // block s in rows, node i of block t in columns)
+        auto tile_products = [&](const bf16x8 (&kt)[4], const bf16x8 (&qt)[4], const bf16x8 (&ks)[4],
+                                 f32x4& A, f32x4& C) __attribute__((always_inline)) {
+            A = z;
+            C = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) {
+                A = mfma32(ks[cs], kt[cs], A);
+                C = mfma32(ks[cs], qt[cs], C);
+            }
+        };
+        // the products masked and decayed into -X / Y (bf16, tile layout) in the
+        // row buffers of parity t & 1; for s == t the diagonal X block in fp32,
+        // transposed, for the inversion
+        auto tile_store = [&](int t, int s, f32x4 A, f32x4 C, uint32_t mword) __attribute__((always_inline)) {
+            const int par = t & 1;
+            const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
+            const uint32_t bits = i < N ? (mword >> (j0 & 31)) & 15u : 0u;
+            const float lgi = s_lg[i], bei = s_beta[i];
+            const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[j0]);
+            const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
+            float xv[4];
+            uint16_t yv[4], nxv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool anc = (bits >> e) & 1u;
+                const bool self = (j0 + e == i) && i < N;
+                const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
+                xv[e] = anc ? bei * d * A[e] : 0.f;
+                yv[e] = bf16_rne(d * C[e]);
+                nxv[e] = bf16_rne(-xv[e]);
+            }
+            const int tp = a32_pos(ln, 4 * lq);
+            *reinterpret_cast<uint2*>(&s_yrow[par][s * 256 + tp]) =
+                make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
+            if (s < t) {
+                *reinterpret_cast<uint2*>(&s_xrow[par][s * 256 + tp]) =
+                    make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s_xd[par][(4 * lq + e) * 16 + ln] = xv[e];   // [col][row]
+            }
+        };
+        // D = (I + X_tt)^-1 in fp32 by right-looking substitution, four lanes
+        // per column: lane 4c + q holds rows 4q .. 4q+3 of column c; step m
+        // broadcasts y_m from its owner within the lane quad and updates the
+        // rows below it
+        auto diag_inverse = [&](int t) __attribute__((always_inline)) {
+            const int par = t & 1;
+            const int c = lane >> 2, qd = lane & 3;
+            float acc[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = (4 * qd + e == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < 15; ++m) {
+                const float4 xc = *reinterpret_cast<const float4*>(&s_xd[par][m * 16 + 4 * qd]);
+                const float ym = quad_bcast(acc[m & 3], m >> 2);
+                const float xr[4] = {xc.x, xc.y, xc.z, xc.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {                     // rows below m only
+                    const float upd = fmaf(-xr[e], ym, acc[e]);
+                    acc[e] = 4 * qd + e > m ? upd : acc[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_dinv[par][a32_pos(4 * qd + e, c)] = bf16_rne(acc[e]);
+        };
+        // Row t's tiles: the diagonal tile first, then the occupied column
+        // blocks s < t in order; Gram wave gw computes tiles gw, gw + NS, ...
+        auto tile_col = [&](int t, unsigned long long occ, int m) __attribute__((always_inline)) {
+            (void)occ;
+            return __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]);
+        };
+        // k / q fragments of a row (two sets, alternating by row) and, refilled
+        // once their products are issued, the k rows and ancestor words of this
+        // wave's first TPW tiles of the next row
+        struct RowOps {
+            bf16x8 k[4], q[4];
+        };
+        bf16x8 kp[TPW][4];
+        uint32_t wp[TPW];
+        auto load_kq = [&](RowOps& o, int t) __attribute__((always_inline)) {
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) {
+                o.k[cs] = frag(Kb, t, cs);
+                o.q[cs] = frag(Qb, t, cs);
+            }
+        };
+        // (blocks past the LDS cache only: a cached block's slot reads one
+        // line, the same for every lane)
+        auto load_tile = [&](int i, int t, unsigned long long occ, int ntile) __attribute__((always_inline)) {
+            const int m = gw + i * NS;
+            const int sc = m < ntile ? tile_col(t, occ, m) : t;
+            if constexpr (!KALL) {
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs)
+                    kp[i][cs] = sc >= KC ? frag(Kb, sc, cs) : *reinterpret_cast<const bf16x8*>(Kb);
+            }
+            wp[i] = gmask[(size_t)min(16 * t + ln, N - 1) * W + ((16 * sc + 4 * lq) >> 5)];
+        };
+        auto kc_frag = [&](int sblk, int cs) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8*>(s_kc + (min(sblk, KC - 1) * 4 + cs) * 512 + lane * 8);
+        };
+        // step t: row t + 1's tiles and projections (operands in cur, its first
+        // tiles' k rows in kp), requesting row t + 2's operands into nxt and kp;
+        // the last rows re-read the last row (harmless).  The first TPW tiles'
+        // products are issued together (independent chains), then their k
+        // registers are refilled, then they are masked and stored.
+        auto gstep = [&](int t, const RowOps& cur, RowOps& nxt) __attribute__((always_inline)) {
+            if (t + 1 < nblk) {
+                const int tr = t + 1, tn = min(t + 2, nblk - 1);
+                load_kq(nxt, tn);
+                const unsigned long long occ = row_occ(tr), occn = row_occ(tn);
+                const int ntile = __popcll(occ) + 1, ntn = __popcll(occn) + 1;
+                f32x4 Ap[TPW], Cp[TPW];
+                uint32_t wc[TPW];
+#pragma unroll
+                for (int i = 0; i < TPW; ++i) {
+                    const int m = gw + i * NS;
+                    const int sc = m < ntile ? tile_col(tr, occ, m) : tr;    // (unused slot: a valid tile)
+                    bf16x8 ks[4];
+#pragma unroll
+                    for (int cs = 0; cs < 4; ++cs) {
+                        if constexpr (KALL) ks[cs] = kc_frag(sc, cs);
+                        else ks[cs] = sc < KC ? kc_frag(sc, cs) : kp[i][cs];
+                    }
+                    tile_products(cur.k, cur.q, ks, Ap[i], Cp[i]);
+                    wc[i] = wp[i];
+                }
+#pragma unroll
+                for (int i = 0; i < TPW; ++i) load_tile(i, tn, occn, ntn);
+#pragma unroll
+                for (int i = 0; i < TPW; ++i) {
+                    const int m = gw + i * NS;
+                    if (m < ntile) tile_store(tr, tile_col(tr, occ, m), Ap[i], Cp[i], wc[i]);
+                }
+                const int ii = min(16 * tr + ln, N - 1);
+                for (int m = gw + TPW * NS; m < ntile; m += NS) {
+                    const int sc = tile_col(tr, occ, m);
+                    bf16x8 k0[4];
+#pragma unroll
+                    for (int cs = 0; cs < 4; ++cs) k0[cs] = sc < KC ? kc_frag(sc, cs) : frag(Kb, sc, cs);
+                    f32x4 A0, C0;
+                    tile_products(cur.k, cur.q, k0, A0, C0);
+                    tile_store(tr, sc, A0, C0, gmask[(size_t)ii * W + ((16 * sc + 4 * lq) >> 5)]);
+                }
+                // projections of row t + 1 for column group gw
+                f32x4 pk = z, pq = z;
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) {
+                    pk = mfma32(cur.k[cs], sb[cs], pk);         // [node][r]
+                    pq = mfma32(sb[cs], cur.q[cs], pq);         // [r][node]
+                }
+                s_pk[tr & 1][gw][lane] = pk;
+                s_pq[tr & 1][gw][lane] = pq;
+                if (gw == 0) diag_inverse(tr);                  // the diagonal tile is this wave's first
+            }
+            lds_barrier();
+        };
+        RowOps A, B;
+        load_kq(A, 0);
+        {
+            const unsigned long long occ0 = row_occ(0);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) load_tile(i, 0, occ0, __popcll(occ0) + 1);
+        }
+        gstep(-1, A, B);                                // row 0; requests row 1
+        for (int t = 0; t < nblk; t += 2) {
+            gstep(t, B, A);
+            if (t + 1 < nblk) gstep(t + 1, A, B);
+        }
+        return;
+    }
+
+    // ================= solve waves =================
+    const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + vo_base + col0 + 4 * lq;
+    const s16x4 zero4 = {0, 0, 0, 0};
     const bool hi_half = lq >= 2;
     s16x4 ident;
 #pragma unroll
     for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
-
     bf16x8 up[NPR];                                     // [U_2p; U_2p+1] as 16x16x32 B operands
 #pragma unroll
     for (int p = 0; p < NPR; ++p) up[p] = zero8;
 
-    // one Gram tile (t, s): masked, decayed -X / Y (bf16, tile layout) into the
-    // row buffers of parity par; for s == t the diagonal X block in fp32 and its
-    // inverse (16 lanes of this wave, column ln each)
-    auto gram_tile = [&](int t, int s, const bf16x8 (&kt)[4], const bf16x8 (&qt)[4],
-                         const bf16x8 (&ks)[4], uint32_t mword) {
+    // row t of the blocked substitution and the output stage, this wave's 16
+    // columns, from the published tiles and projections of row t (parity t & 1)
+    auto solve_row = [&](int t, uint2 vt) __attribute__((always_inline)) {
         const int par = t & 1;
-        f32x4 A = z, C = z;
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-            A = mfma32(ks[cs], kt[cs], A);
-            C = mfma32(ks[cs], qt[cs], C);
-        }
-        const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
-        const uint32_t bits = i < N ? (mword >> (j0 & 31)) & 15u : 0u;
-        const float lgi = s_lg[i], bei = s_beta[i];
-        const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[j0]);
-        const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
-        float xv[4];
-        uint16_t yv[4], nxv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool anc = (bits >> e) & 1u;
-            const bool self = (j0 + e == i) && i < N;
-            const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
-            xv[e] = anc ? bei * d * A[e] : 0.f;
-            yv[e] = bf16_rne(d * C[e]);
-            nxv[e] = bf16_rne(-xv[e]);
-        }
-        const int tp = a32_pos(ln, 4 * lq);
-        *reinterpret_cast<uint2*>(&s_yrow[par][s * 256 + tp]) =
-            make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
-        if (s < t) {
-            *reinterpret_cast<uint2*>(&s_xrow[par][s * 256 + tp]) =
-                make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
-        } else {
-            *reinterpret_cast<float4*>(&s_xd[par][ln * 16 + 4 * lq]) = make_float4(xv[0], xv[1], xv[2], xv[3]);
-            // (I + X_tt)^-1 by forward substitution, one column per lane; the
-            // wave reads its own LDS writes (in order within a wave)
-            if (lane < 16) {
-                const float* xd = s_xd[par];
-                float y[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float acc = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-                    for (int m = 0; m < r; ++m) acc = fmaf(-xd[r * 16 + m], y[m], acc);
-                    y[r] = acc;
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s_dinv[par][a32_pos(r, ln)] = bf16_rne(y[r]);
-            }
-        }
-    };
-
-    // one block row: Gram tiles, barrier, then this wave's substitution and
-    // outputs.  kt / qt / vt are row t's operands (requested a row earlier);
-    // kn / qn / vn receive row t + 1's.
-    auto do_row = [&](int t, const bf16x8 (&kt)[4], const bf16x8 (&qt)[4], uint2 vt,
-                      bf16x8 (&kn)[4], bf16x8 (&qn)[4], uint2& vn) {
-        const int par = t & 1;
-        // (readfirstlane returns a signed int: widen through uint32_t, and keep
-        // only column blocks 0 .. t)
-        const unsigned long long occ =
-            (((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(s_occ[t] >> 32)) << 32) |
-             (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)s_occ[t])) &
-            ((2ull << t) - 1ull);
-        const unsigned long long full = occ | (1ull << t);
-        const int ntile = __popcll(full);
-        // this wave's tiles of the row, two at a time (both tiles' k rows and
-        // ancestor words requested before either is computed)
-        for (int m = wave; m < ntile; m += 2 * NWV) {
-            const int s0 = nth_bit64(full, m);
-            const bool two = m + NWV < ntile;
-            const int s1 = two ? nth_bit64(full, m + NWV) : s0;
-            bf16x8 k0[4], k1[4];
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs) {
-                k0[cs] = g_frag(Kb, kq_row, s0, cs, lane, N);
-                k1[cs] = g_frag(Kb, kq_row, s1, cs, lane, N);
-            }
-            const int ii = min(16 * t + ln, N - 1);
-            const uint32_t w0 = gmask[(size_t)ii * W + ((16 * s0 + 4 * lq) >> 5)];
-            const uint32_t w1 = gmask[(size_t)ii * W + ((16 * s1 + 4 * lq) >> 5)];
-            gram_tile(t, s0, kt, qt, k0, w0);
-            if (two) gram_tile(t, s1, kt, qt, k1, w1);
-        }
-        lds_barrier();                                  // row t's tiles and inverse are published
-        // row t + 1's operands (the last row re-reads its own: harmless)
-        const int tn = min(t + 1, nblk - 1);
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-            kn[cs] = g_frag(Kb, kq_row, tn, cs, lane, N);
-            qn[cs] = g_frag(Qb, kq_row, tn, cs, lane, N);
-        }
-        vn = *reinterpret_cast<const uint2*>(Vp + (size_t)min(16 * tn + ln, N - 1) * vo_row);
-
-        // ---- substitution and outputs for row t, this wave's 16 columns ----
+        const unsigned long long occ = row_occ(t);
         const uint16_t* xr = s_xrow[par];
         const uint16_t* yr = s_yrow[par];
-        f32x4 pk = z, pqT = z;
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-            pk = mfma32(kt[cs], sb[cs], pk);            // [node][r]
-            pqT = mfma32(sb[cs], qt[cs], pqT);          // [r][node]
-        }
+        const f32x4 pk = s_pk[par][wave][lane], pqT = s_pq[par][wave][lane];
         f32x4 R;
         {
             const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vt), ident, z);
@@ -293,7 +444,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a,
                 R[m] = s_beta[i] * (vd[m] - __expf(s_lg[i]) * pk[m]);
             }
         }
-        // R_t += sum_{s<t} (-X_ts) U_s over occupied tiles, two blocks per MFMA
+        // R_t += sum_{s<t} (-X_ts) U_s over occupied tiles, two blocks per MFMA,
+        // even and odd pairs in two accumulators (two independent chains)
+        f32x4 R2 = z;
 #pragma unroll
         for (int p = 0; p < NPR; ++p) {
             const int s = 2 * p;
@@ -303,10 +456,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a,
                 if (o0 || o1) {
                     bf16x8 nx = *reinterpret_cast<const bf16x8*>(xr + s * 256 + lane * 8);
                     if (!(hi_half ? o1 : o0)) nx = zero8;
-                    R = mfma32(nx, up[p], R);
+                    if (p & 1) R2 = mfma32(nx, up[p], R2);
+                    else R = mfma32(nx, up[p], R);
                 }
             }
         }
+        R += R2;
         const bf16x8 di = *reinterpret_cast<const bf16x8*>(s_dinv[par] + (ln + 16 * (lq & 1)) * 8);
         s16x4 rh, rl;
         split4(R, rh, rl);
@@ -327,7 +482,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a,
         const int node = 16 * t + ln;
         if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 4 * lq) = UT;
         // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T over occupied tiles
-        f32x4 Oc = z;
+        f32x4 Oc = z, Oc2 = z;
 #pragma unroll
         for (int p = 0; p < NPR; ++p) {
             const int s = 2 * p;
@@ -337,10 +492,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a,
                 if (o0 || o1) {
                     bf16x8 yt = *reinterpret_cast<const bf16x8*>(yr + s * 256 + lane * 8);
                     if (!(hi_half ? o1 : o0)) yt = zero8;
-                    Oc = mfma32(up[p], yt, Oc);
+                    if (p & 1) Oc2 = mfma32(up[p], yt, Oc2);
+                    else Oc = mfma32(up[p], yt, Oc);
                 }
             }
         }
+        Oc += Oc2;
         if (node < N) {
             const float egn = __expf(s_lg[node]);
             f32x4 OT;
@@ -351,19 +508,22 @@ __global__ __launch_bounds__(64 * NWV, 1) void verify_large_kernel(VerifyArgs a,
             *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + col0 + 4 * lq) = make_uint2(lo, hi);
         }
     };
-
-    // rows in pairs, the operand registers alternating (no copies of loads in flight)
-    bf16x8 ka[4], qa[4], kb2[4], qb2[4];
-    uint2 va, vb;
-#pragma unroll
-    for (int cs = 0; cs < 4; ++cs) {
-        ka[cs] = g_frag(Kb, kq_row, 0, cs, lane, N);
-        qa[cs] = g_frag(Qb, kq_row, 0, cs, lane, N);
-    }
-    va = *reinterpret_cast<const uint2*>(Vp + (size_t)min(ln, N - 1) * vo_row);
+    // v of row t + 1 is requested before row t's stores (loads and stores
+    // retire in order, so waiting for it never waits for those stores)
+    auto load_v = [&](int t) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint2*>(Vp + (size_t)min(16 * t + ln, N - 1) * vo_row);
+    };
+    uint2 va = load_v(0), vb;
+    lds_barrier();
     for (int t = 0; t < nblk; t += 2) {
-        do_row(t, ka, qa, va, kb2, qb2, vb);
-        if (t + 1 < nblk) do_row(t + 1, kb2, qb2, vb, ka, qa, va);
+        vb = load_v(min(t + 1, nblk - 1));
+        solve_row(t, va);
+        lds_barrier();
+        if (t + 1 < nblk) {
+            va = load_v(min(t + 2, nblk - 1));
+            solve_row(t + 1, vb);
+            lds_barrier();
+        }
     }
 }
 
@@ -384,9 +544,9 @@ hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream) 
     // waves each: a wave holds up to 32 stacked U pairs and may use the whole
     // register file of its SIMD
     int csplit = 2;
-    const void* fn = a.N <= 256 ? (const void*)verify_large_kernel<16, 4> : (const void*)verify_large_kernel<32, 4>;
+    const void* fn = a.N <= 256 ? (const void*)verify_large_kernel<16> : (const void*)verify_large_kernel<32>;
     void* args[] = {&copy, &csplit};
-    return hipLaunchKernel(fn, dim3((unsigned)(a.B * a.Hv * csplit)), dim3(256), args, 0, stream);
+    return hipLaunchKernel(fn, dim3((unsigned)(a.B * a.Hv * csplit)), dim3(512), args, 0, stream);
 }
 
 }  // namespace gdn
