@@ -223,39 +223,43 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_d128(CommitArgs a) {
 // c, columns: value row r),
 //     D_out = e^(G_a) D_in + K_P^T (diag(w) U_P),
 // K_P (|P| x 128) the path's k rows and U_P (|P| x 128, fp32) its u rows.
-// Four waves; wave w owns the value-row tiles 2w, 2w + 1 of D and all eight
-// key-column tiles: 16 accumulator tiles whose lanes hold 4 consecutive key
-// columns of one value row, i.e. 16 contiguous bytes of S, so S_in loads and
-// S_out stores stay row-major.  The path is consumed 32 nodes at a time: its k
-// rows and its weighted u rows (split into bf16 hi + lo, about 16 mantissa
-// bits, so the update keeps fp32-level accuracy) are staged transposed in
-// LDS, each MFMA operand one 16-byte read.
+// Two workgroups per (sequence, value head), one per half of the value rows
+// (the update of a row needs only that row's u entries); four waves, wave w
+// owns value-row tile w of its half and all eight key-column tiles: 8
+// accumulator tiles whose lanes hold 4 consecutive key columns of one value
+// row, i.e. 16 contiguous bytes of S, so S_in loads and S_out stores stay
+// row-major.  The path is consumed 32 nodes at a time: its k rows and its
+// weighted u rows (split into bf16 hi + lo, about 16 mantissa bits, so the
+// update keeps fp32-level accuracy) are staged transposed in LDS, each MFMA
+// operand one 16-byte read, the next chunk's loads issued before the current
+// chunk's products.
 constexpr int kMfmaChunk = 32;
+constexpr int kMfmaHalves = 2;                       // value-row halves per (b, h)
+constexpr int kHalfRows = kFastD / kMfmaHalves;
 
 __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    __shared__ __attribute__((aligned(16))) uint16_t s_kT[kFastD * kMfmaChunk];    // [c][j]
-    __shared__ __attribute__((aligned(16))) uint16_t s_uhT[kFastD * kMfmaChunk];   // [r][j], hi
-    __shared__ __attribute__((aligned(16))) uint16_t s_ulT[kFastD * kMfmaChunk];   // [r][j], lo
+    __shared__ __attribute__((aligned(16))) uint16_t s_kT[kFastD * kMfmaChunk];      // [c][j]
+    __shared__ __attribute__((aligned(16))) uint16_t s_uhT[kHalfRows * kMfmaChunk];  // [r][j], hi
+    __shared__ __attribute__((aligned(16))) uint16_t s_ulT[kHalfRows * kMfmaChunk];  // [r][j], lo
     __shared__ int s_idx[kMaxNodes];
 
     const int N = a.N, W = (N + 31) / 32;
-    const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
+    const int half = blockIdx.x % kMfmaHalves, bh = blockIdx.x / kMfmaHalves;
+    const int b = bh / a.Hv, h = bh % a.Hv;
     const int hk = h / (a.Hv / a.Hk);
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lq = lane >> 4, wave = tid >> 6;
+    const int r0 = half * kHalfRows;                  // this workgroup's first value row
 
     const int acc_node = a.accepted[b];
     const int status = a.status[b];
     const size_t sbase = ((size_t)b * a.Hv + h) * kFastD * kFastD;
-    f32x4 D[2][8];                                     // [value-row tile 2w + i][key-column tile]
+    const size_t srow = sbase + (size_t)(r0 + 16 * wave + ln) * kFastD + 4 * lq;
+    f32x4 D[8];                                       // [key-column tile], value-row tile `wave`
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int tc = 0; tc < 8; ++tc)
-            D[i][tc] = *reinterpret_cast<const f32x4*>(a.S_in + sbase + (size_t)(16 * (2 * wave + i) + ln) * kFastD +
-                                                       16 * tc + 4 * lq);
+    for (int tc = 0; tc < 8; ++tc) D[tc] = *reinterpret_cast<const f32x4*>(a.S_in + srow + 16 * tc);
 
     const bool valid = status == 0 && acc_node >= -1 && acc_node < N;
     const uint32_t* row = a.anc_mask + ((size_t)b * N + (acc_node < 0 ? 0 : acc_node)) * W;
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
         if (tid == 0) s_idx[plen - 1] = acc_node;
     }
     __syncthreads();
-    if (h == 0) {
+    if (h == 0 && half == 0) {
         int32_t* pb = a.path + (size_t)b * N;
         for (int m = tid; m < N; m += kThreads) pb[m] = m < plen ? s_idx[m] : -1;
         if (tid == 0) a.path_len[b] = plen;
@@ -286,24 +290,24 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
         const float ga = lg[acc_node];
         const float dec = __expf(ga);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int tc = 0; tc < 8; ++tc) D[i][tc] *= dec;
-        const int m = tid >> 3, seg = (tid & 7) * 16;  // staging: path node m, 16 columns from seg
+        for (int tc = 0; tc < 8; ++tc) D[tc] *= dec;
+        // staging: path node m of the chunk, key columns kseg .. +15 and value
+        // rows useg .. +7 of this half
+        const int m = tid >> 3, kseg = (tid & 7) * 16, useg = (tid & 7) * 8;
         // chunk loads, unconditional (rows past the path re-read its last node
         // with weight 0), issued one chunk ahead of their use
         u32x4 k0, k1;
-        float4 u4[4];
+        float4 u4[2];
         float lgj;
         auto load_chunk = [&](int p0) {
             const int pn = min(kMfmaChunk, plen - p0);
             const int j = s_idx[p0 + min(m, pn - 1)];
-            const uint16_t* kr = K + (((size_t)b * N + j) * a.Hk + hk) * kFastD + seg;
+            const uint16_t* kr = K + (((size_t)b * N + j) * a.Hk + hk) * kFastD + kseg;
             k0 = *reinterpret_cast<const u32x4*>(kr);
             k1 = *reinterpret_cast<const u32x4*>(kr + 8);
-            const float* ur = U + (size_t)j * kFastD + seg;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) u4[e] = *reinterpret_cast<const float4*>(ur + 4 * e);
+            const float* ur = U + (size_t)j * kFastD + r0 + useg;
+            u4[0] = *reinterpret_cast<const float4*>(ur);
+            u4[1] = *reinterpret_cast<const float4*>(ur + 4);
             lgj = lg[j];
         };
         load_chunk(0);
@@ -311,48 +315,39 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
             lds_barrier();                             // the previous chunk's operands are consumed
             {
                 const float w = m < plen - p0 ? __expf(ga - lgj) : 0.f;
-                const float uv[16] = {u4[0].x, u4[0].y, u4[0].z, u4[0].w, u4[1].x, u4[1].y, u4[1].z, u4[1].w,
-                                      u4[2].x, u4[2].y, u4[2].z, u4[2].w, u4[3].x, u4[3].y, u4[3].z, u4[3].w};
+                const float uv[8] = {u4[0].x, u4[0].y, u4[0].z, u4[0].w, u4[1].x, u4[1].y, u4[1].z, u4[1].w};
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const uint32_t kw = (e < 8 ? k0[e >> 1] : k1[(e - 8) >> 1]) >> (16 * (e & 1));
+                    s_kT[(kseg + e) * kMfmaChunk + m] = (uint16_t)(kw & 0xffffu);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
                     const float x = w * uv[e];
                     const uint16_t hi = __builtin_bit_cast(uint16_t, (__bf16)x);
                     const uint16_t lo = __builtin_bit_cast(uint16_t, (__bf16)(x - __uint_as_float((uint32_t)hi << 16)));
-                    s_kT[(seg + e) * kMfmaChunk + m] = (uint16_t)(kw & 0xffffu);
-                    s_uhT[(seg + e) * kMfmaChunk + m] = hi;
-                    s_ulT[(seg + e) * kMfmaChunk + m] = lo;
+                    s_uhT[(useg + e) * kMfmaChunk + m] = hi;
+                    s_ulT[(useg + e) * kMfmaChunk + m] = lo;
                 }
             }
             // (LDS-only barriers: the loads just issued stay in flight over them)
             if (p0 + kMfmaChunk < plen) load_chunk(p0 + kMfmaChunk);
             lds_barrier();
-            bf16x8 bh[2], bl[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int off = (16 * (2 * wave + i) + ln) * kMfmaChunk + 8 * lq;
-                bh[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_uhT + off));
-                bl[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_ulT + off));
-            }
+            const int off = (16 * wave + ln) * kMfmaChunk + 8 * lq;
+            const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_uhT + off));
+            const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_ulT + off));
 #pragma unroll
             for (int tc = 0; tc < 8; ++tc) {
                 const bf16x8 ak = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(s_kT + (16 * tc + ln) * kMfmaChunk + 8 * lq));
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    D[i][tc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bh[i], D[i][tc], 0, 0, 0);
-                    D[i][tc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bl[i], D[i][tc], 0, 0, 0);
-                }
+                D[tc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bh, D[tc], 0, 0, 0);
+                D[tc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bl, D[tc], 0, 0, 0);
             }
         }
     }
     if (plen > 0 || a.S_in != a.S_out) {               // nothing accepted (or invalid): S_out = S_in
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int tc = 0; tc < 8; ++tc)
-                *reinterpret_cast<f32x4*>(a.S_out + sbase + (size_t)(16 * (2 * wave + i) + ln) * kFastD + 16 * tc +
-                                          4 * lq) = D[i][tc];
+        for (int tc = 0; tc < 8; ++tc) *reinterpret_cast<f32x4*>(a.S_out + srow + 16 * tc) = D[tc];
     }
 }
 
@@ -366,7 +361,8 @@ hipError_t launch_commit(const CommitArgs& a, int io, hipStream_t stream) {
         const void* fn = io != GDN_BF16 ? (const void*)commit_kernel_d128<GDN_F32>
                          : a.N <= 128   ? (const void*)commit_kernel_d128<GDN_BF16>
                                         : (const void*)commit_kernel_mfma;
-        return hipLaunchKernel(fn, dim3((unsigned)(a.B * a.Hv)), dim3(kThreads), args, 0, stream);
+        const unsigned grid = (unsigned)(a.B * a.Hv) * (fn == (const void*)commit_kernel_mfma ? kMfmaHalves : 1);
+        return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
     }
     const void* fn = io == GDN_BF16 ? (const void*)commit_kernel<GDN_BF16>
                                     : (const void*)commit_kernel<GDN_F32>;
