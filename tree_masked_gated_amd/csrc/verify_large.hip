@@ -67,19 +67,23 @@ __device__ __forceinline__ bf16x8 g_frag(const uint16_t* base, size_t row_stride
                                           base + (size_t)row * row_stride + 32 * cs + 8 * (lane >> 4)));
 }
 
-// Waves 0 .. NS-1 solve: wave w owns value columns col0 = 64 slice + 16 w.
-// Waves NS .. 2 NS-1 are Gram waves: they compute the next block row's tiles
-// and, for column group w - NS, its projections K_t S0^T and S0 Q_t^T into
-// LDS, while the solve waves run the current row; one barrier per row.  The
-// two roles run separate loops with the same barrier count, so neither
-// keeps the other's registers.
+// Waves 0 .. NS-1 solve: wave w owns value columns 64 slice + 32 w .. +31 as
+// two 16-column groups (two independent MFMA chains per product).  Waves NS ..
+// NS+NG-1 are Gram waves: they compute the next block row's tiles and (the
+// last NCG of them, one 16-column group each) its projections K_t S0^T and
+// S0 Q_t^T into LDS, while the solve waves run the current row; one barrier
+// per row.  The two roles run separate loops with the same barrier count, so
+// neither keeps the other's registers.
 template <int NB>
 __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int csplit) {
     constexpr int NP = 16 * NB;                 // padded node count
     constexpr int NT = 512;
-    constexpr int NS = 4;                       // solve waves (= Gram waves)
+    constexpr int NS = 2;                       // solve waves, 32 value columns each
+    constexpr int NG = 6;                       // Gram waves
+    constexpr int NCG = 4;                      // 16-column groups per workgroup
+    constexpr int CG = 2;                       // groups per solve wave
     constexpr int NPR = NB / 2;                 // U pairs
-    constexpr int TPW = 4;                      // tiles per Gram wave requested a row ahead
+    constexpr int TPW = 3;                      // tiles per Gram wave requested a row ahead
     constexpr int KC = 16;                      // node blocks whose k rows are cached in LDS
     constexpr bool KALL = NB <= KC;             // every block cached: no k rows from L2 in the Gram
     // -X and Y tiles of one block row, by column block s, for rows of either
@@ -89,8 +93,8 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     __shared__ __attribute__((aligned(16))) uint16_t s_yrow[2][NB * 256 + 256];
     __shared__ __attribute__((aligned(16))) uint16_t s_dinv[2][256];
     __shared__ __attribute__((aligned(16))) float s_xd[2][256];
-    __shared__ __attribute__((aligned(16))) f32x4 s_pk[2][NS][64];   // K_t S0^T, accumulator layout
-    __shared__ __attribute__((aligned(16))) f32x4 s_pq[2][NS][64];   // S0 Q_t^T
+    __shared__ __attribute__((aligned(16))) f32x4 s_pk[2][NCG][64];   // K_t S0^T, accumulator layout
+    __shared__ __attribute__((aligned(16))) f32x4 s_pq[2][NCG][64];   // S0 Q_t^T
     __shared__ __attribute__((aligned(16))) float s_lg[NP];
     __shared__ __attribute__((aligned(16))) float s_beta[NP];
     __shared__ __attribute__((aligned(16))) int32_t s_jump[NP];
@@ -107,11 +111,10 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool solver = wave < NS;
-    const int cg = solver ? wave : wave - NS;           // column group (solve, or projections)
     const int item = blockIdx.x;
     const int slice = item % csplit, bh = item / csplit;
     const int h = bh % Hv, b = bh / Hv, hk = h / G;
-    const int col0 = slice * (16 * NS) + 16 * cg;
+    const int cbase = slice * (16 * NCG);               // the workgroup's first value column
     const size_t vo_row = (size_t)Hv * kD;
     const size_t vo_base = ((size_t)b * N * Hv + h) * kD;
     uint16_t* O = static_cast<uint16_t*>(a.o);
@@ -121,8 +124,8 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     if (status) {                                       // invalid tree: NaN outputs
         const float qnan = __uint_as_float(0x7fc00000u);
         if (solver)
-            for (int x = lane; x < N * 16; x += 64) {
-                const int i = x / 16, c = col0 + x % 16;
+            for (int x = lane; x < N * 32; x += 64) {
+                const int i = x / 32, c = cbase + 32 * wave + x % 32;
                 O[vo_base + (size_t)i * vo_row + c] = 0x7fc0;
                 Ug[(size_t)i * kD + c] = qnan;
             }
@@ -221,10 +224,12 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
 
     if (!solver) {
         // ================= Gram waves =================
-        const int gw = cg;
-        // this wave's column group's S0 rows as bf16 B / A operands
+        const int gw = wave - NS;
+        const int pg = gw - (NG - NCG);                 // projection column group (>= 0: this wave's)
+        // the projection group's S0 rows as bf16 B / A operands
         bf16x8 sb[4];
         {
+            const int col0 = cbase + 16 * max(pg, 0);
             const float* p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(col0 + ln) * kD + 8 * lq;
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs)
@@ -310,7 +315,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             for (int e = 0; e < 4; ++e) s_dinv[par][a32_pos(4 * qd + e, c)] = bf16_rne(acc[e]);
         };
         // Row t's tiles: the diagonal tile first, then the occupied column
-        // blocks s < t in order; Gram wave gw computes tiles gw, gw + NS, ...
+        // blocks s < t in order; Gram wave gw computes tiles gw, gw + NG, ...
         auto tile_col = [&](int t, unsigned long long occ, int m) __attribute__((always_inline)) {
             (void)occ;
             return __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]);
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         // (blocks past the LDS cache only: a cached block's slot reads one
         // line, the same for every lane)
         auto load_tile = [&](int i, int t, unsigned long long occ, int ntile) __attribute__((always_inline)) {
-            const int m = gw + i * NS;
+            const int m = gw + i * NG;
             const int sc = m < ntile ? tile_col(t, occ, m) : t;
             if constexpr (!KALL) {
 #pragma unroll
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 uint32_t wc[TPW];
 #pragma unroll
                 for (int i = 0; i < TPW; ++i) {
-                    const int m = gw + i * NS;
+                    const int m = gw + i * NG;
                     const int sc = m < ntile ? tile_col(tr, occ, m) : tr;    // (unused slot: a valid tile)
                     bf16x8 ks[4];
 #pragma unroll
@@ -375,11 +380,11 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 for (int i = 0; i < TPW; ++i) load_tile(i, tn, occn, ntn);
 #pragma unroll
                 for (int i = 0; i < TPW; ++i) {
-                    const int m = gw + i * NS;
+                    const int m = gw + i * NG;
                     if (m < ntile) tile_store(tr, tile_col(tr, occ, m), Ap[i], Cp[i], wc[i]);
                 }
                 const int ii = min(16 * tr + ln, N - 1);
-                for (int m = gw + TPW * NS; m < ntile; m += NS) {
+                for (int m = gw + TPW * NG; m < ntile; m += NG) {
                     const int sc = tile_col(tr, occ, m);
                     bf16x8 k0[4];
 #pragma unroll
@@ -388,15 +393,17 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                     tile_products(cur.k, cur.q, k0, A0, C0);
                     tile_store(tr, sc, A0, C0, gmask[(size_t)ii * W + ((16 * sc + 4 * lq) >> 5)]);
                 }
-                // projections of row t + 1 for column group gw
-                f32x4 pk = z, pq = z;
+                // projections of row t + 1 for column group pg
+                if (pg >= 0) {
+                    f32x4 pk = z, pq = z;
 #pragma unroll
-                for (int cs = 0; cs < 4; ++cs) {
-                    pk = mfma32(cur.k[cs], sb[cs], pk);         // [node][r]
-                    pq = mfma32(sb[cs], cur.q[cs], pq);         // [r][node]
+                    for (int cs = 0; cs < 4; ++cs) {
+                        pk = mfma32(cur.k[cs], sb[cs], pk);     // [node][r]
+                        pq = mfma32(sb[cs], cur.q[cs], pq);     // [r][node]
+                    }
+                    s_pk[tr & 1][pg][lane] = pk;
+                    s_pq[tr & 1][pg][lane] = pq;
                 }
-                s_pk[tr & 1][gw][lane] = pk;
-                s_pq[tr & 1][gw][lane] = pq;
                 if (gw == 0) diag_inverse(tr);                  // the diagonal tile is this wave's first
             }
             lds_barrier();
@@ -417,36 +424,39 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     }
 
     // ================= solve waves =================
-    const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + vo_base + col0 + 4 * lq;
+    const int c0 = cbase + 32 * wave;                   // this wave's first value column
     const s16x4 zero4 = {0, 0, 0, 0};
     const bool hi_half = lq >= 2;
     s16x4 ident;
 #pragma unroll
     for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
-    bf16x8 up[NPR];                                     // [U_2p; U_2p+1] as 16x16x32 B operands
+    bf16x8 up[CG][NPR];                                 // [U_2p; U_2p+1] as 16x16x32 B operands
 #pragma unroll
-    for (int p = 0; p < NPR; ++p) up[p] = zero8;
+    for (int g = 0; g < CG; ++g)
+#pragma unroll
+        for (int p = 0; p < NPR; ++p) up[g][p] = zero8;
 
-    // row t of the blocked substitution and the output stage, this wave's 16
-    // columns, from the published tiles and projections of row t (parity t & 1)
-    auto solve_row = [&](int t, uint2 vt) __attribute__((always_inline)) {
+    // row t of the blocked substitution and the output stage for this wave's
+    // two column groups, from the published tiles and projections of row t
+    // (parity t & 1); every tile read feeds both groups
+    auto solve_row = [&](int t, const uint2 (&vt)[CG]) __attribute__((always_inline)) {
         const int par = t & 1;
         const unsigned long long occ = row_occ(t);
         const uint16_t* xr = s_xrow[par];
         const uint16_t* yr = s_yrow[par];
-        const f32x4 pk = s_pk[par][wave][lane], pqT = s_pq[par][wave][lane];
-        f32x4 R;
-        {
-            const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vt), ident, z);
+        f32x4 R[CG], pqT[CG];
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+            const f32x4 pk = s_pk[par][2 * wave + g][lane];
+            pqT[g] = s_pq[par][2 * wave + g][lane];
+            const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vt[g]), ident, z);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int i = 16 * t + 4 * lq + m;
-                R[m] = s_beta[i] * (vd[m] - __expf(s_lg[i]) * pk[m]);
+                R[g][m] = s_beta[i] * (vd[m] - __expf(s_lg[i]) * pk[m]);
             }
         }
-        // R_t += sum_{s<t} (-X_ts) U_s over occupied tiles, two blocks per MFMA,
-        // even and odd pairs in two accumulators (two independent chains)
-        f32x4 R2 = z;
+        // R_t += sum_{s<t} (-X_ts) U_s over occupied tiles, two blocks per MFMA
 #pragma unroll
         for (int p = 0; p < NPR; ++p) {
             const int s = 2 * p;
@@ -456,33 +466,37 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 if (o0 || o1) {
                     bf16x8 nx = *reinterpret_cast<const bf16x8*>(xr + s * 256 + lane * 8);
                     if (!(hi_half ? o1 : o0)) nx = zero8;
-                    if (p & 1) R2 = mfma32(nx, up[p], R2);
-                    else R = mfma32(nx, up[p], R);
+#pragma unroll
+                    for (int g = 0; g < CG; ++g) R[g] = mfma32(nx, up[g][p], R[g]);
                 }
             }
         }
-        R += R2;
         const bf16x8 di = *reinterpret_cast<const bf16x8*>(s_dinv[par] + (ln + 16 * (lq & 1)) * 8);
-        s16x4 rh, rl;
-        split4(R, rh, rl);
-        const bf16x8 rr = stack_pair(rh, rl);
-        const f32x4 U = mfma32(di, rr, z);
-        const f32x4 UT = mfma32(rr, di, z);
-        const s16x4 ut = to_bf16x4(U);
-#pragma unroll
-        for (int p = 0; p < NPR; ++p) {
-            if (p == (t >> 1)) {
-                if (t & 1)
-                    up[p] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, up[p]) |
-                                                           __builtin_bit_cast(u32x4, stack_pair(zero4, ut)));
-                else
-                    up[p] = stack_pair(ut, zero4);
-            }
-        }
         const int node = 16 * t + ln;
-        if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 4 * lq) = UT;
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+            s16x4 rh, rl;
+            split4(R[g], rh, rl);
+            const bf16x8 rr = stack_pair(rh, rl);
+            const f32x4 U = mfma32(di, rr, z);
+            const f32x4 UT = mfma32(rr, di, z);
+            const s16x4 ut = to_bf16x4(U);
+#pragma unroll
+            for (int p = 0; p < NPR; ++p) {
+                if (p == (t >> 1)) {
+                    if (t & 1)
+                        up[g][p] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, up[g][p]) |
+                                                                  __builtin_bit_cast(u32x4, stack_pair(zero4, ut)));
+                    else
+                        up[g][p] = stack_pair(ut, zero4);
+                }
+            }
+            if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + c0 + 16 * g + 4 * lq) = UT;
+        }
         // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T over occupied tiles
-        f32x4 Oc = z, Oc2 = z;
+        f32x4 Oc[CG];
+#pragma unroll
+        for (int g = 0; g < CG; ++g) Oc[g] = z;
 #pragma unroll
         for (int p = 0; p < NPR; ++p) {
             const int s = 2 * p;
@@ -492,35 +506,42 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 if (o0 || o1) {
                     bf16x8 yt = *reinterpret_cast<const bf16x8*>(yr + s * 256 + lane * 8);
                     if (!(hi_half ? o1 : o0)) yt = zero8;
-                    if (p & 1) Oc2 = mfma32(up[p], yt, Oc2);
-                    else Oc = mfma32(up[p], yt, Oc);
+#pragma unroll
+                    for (int g = 0; g < CG; ++g) Oc[g] = mfma32(up[g][p], yt, Oc[g]);
                 }
             }
         }
-        Oc += Oc2;
         if (node < N) {
             const float egn = __expf(s_lg[node]);
-            f32x4 OT;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[m] + Oc[m];
-            const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
-            const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
-            *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + col0 + 4 * lq) = make_uint2(lo, hi);
+            for (int g = 0; g < CG; ++g) {
+                f32x4 OT;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[g][m] + Oc[g][m];
+                const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
+                const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
+                *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + c0 + 16 * g + 4 * lq) =
+                    make_uint2(lo, hi);
+            }
         }
     };
     // v of row t + 1 is requested before row t's stores (loads and stores
     // retire in order, so waiting for it never waits for those stores)
-    auto load_v = [&](int t) __attribute__((always_inline)) {
-        return *reinterpret_cast<const uint2*>(Vp + (size_t)min(16 * t + ln, N - 1) * vo_row);
+    const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + vo_base + c0 + 4 * lq;
+    auto load_v = [&](int t, uint2 (&v)[CG]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < CG; ++g)
+            v[g] = *reinterpret_cast<const uint2*>(Vp + (size_t)min(16 * t + ln, N - 1) * vo_row + 16 * g);
     };
-    uint2 va = load_v(0), vb;
+    uint2 va[CG], vb[CG];
+    load_v(0, va);
     lds_barrier();
     for (int t = 0; t < nblk; t += 2) {
-        vb = load_v(min(t + 1, nblk - 1));
+        load_v(min(t + 1, nblk - 1), vb);
         solve_row(t, va);
         lds_barrier();
         if (t + 1 < nblk) {
-            va = load_v(min(t + 2, nblk - 1));
+            load_v(min(t + 2, nblk - 1), va);
             solve_row(t + 1, vb);
             lds_barrier();
         }
