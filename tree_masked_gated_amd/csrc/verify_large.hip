@@ -55,9 +55,6 @@ __device__ __forceinline__ float quad_bcast(float x, int k) {
     }
 }
 
-typedef __attribute__((address_space(1))) const void* kgptr_t;
-typedef __attribute__((address_space(3))) void* klptr_t;
-
 // A/B fragment of a 16-node block of k or q straight from global memory: lane
 // l gets row 16 blk + l % 16 (clamped to N - 1), columns 32 cs + 8 (l / 16)..+7.
 __device__ __forceinline__ bf16x8 g_frag(const uint16_t* base, size_t row_stride, int blk,
@@ -137,18 +134,6 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
     const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + ((size_t)b * N * Hk + hk) * kD;
     const size_t kq_row = (size_t)Hk * kD;
-    // k rows of the cached blocks straight into LDS (direct-to-LDS loads, one
-    // 1 KB chunk per instruction), landing while the tree's gates are summed
-    {
-        const int ncb = min(nblk, KC);
-        for (int x = wave; x < ncb * 4; x += NT / 64) {
-            const int sblk = x >> 2, cs = x & 3;
-            const int row = min(16 * sblk + ln, N - 1);
-            __builtin_amdgcn_global_load_lds((kgptr_t)(Kb + (size_t)row * kq_row + 32 * cs + 8 * lq),
-                                             (klptr_t)(s_kc + x * 512), 16, 0, 0);
-        }
-    }
-
     // ---- path log-gates G (synchronous pointer doubling), beta, occupancy ----
     const uint32_t* gmask = a.anc_mask + (size_t)b * N * W;
     for (int i = tid; i < NP; i += NT) {
@@ -175,6 +160,19 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             if (bits) atomicOr(&s_occ[t], bits);
         }
     }
+    // k rows of the cached blocks into registers (1 KB unit wave + 8 r: block
+    // u / 4, chunk u % 4), written to LDS once the tree's gates are summed, so
+    // the loads overlap that work; issued after the loads waited on above
+    // (loads retire in order).  Rows clamped to N - 1.
+    constexpr int KCR = KC * 4 / (NT / 64);             // units per wave
+    u32x4 kcr[KCR];
+#pragma unroll
+    for (int r = 0; r < KCR; ++r) {
+        const int u = wave + (NT / 64) * r;
+        const int row = min(16 * (u >> 2) + ln, N - 1);
+        kcr[r] = *reinterpret_cast<const u32x4*>(Kb + (size_t)row * kq_row + 32 * (u & 3) + 8 * lq);
+    }
+
     for (;;) {
         constexpr int PER = NP / NT > 0 ? NP / NT : 1;
         int nn[PER];
@@ -210,7 +208,9 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             occ &= occ - 1ull;
         }
     }
-    wait_vmem_all();                                    // the cached k rows have landed
+#pragma unroll
+    for (int r = 0; r < KCR; ++r)
+        *reinterpret_cast<u32x4*>(s_kc + (wave + (NT / 64) * r) * 512 + lane * 8) = kcr[r];
     __syncthreads();
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
