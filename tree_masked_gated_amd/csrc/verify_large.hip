@@ -28,19 +28,71 @@ namespace {
 constexpr int kPrepMaxN = 512;       // largest tree of this path
 constexpr int kPrepThreads = 1024;
 
-// Ancestor rows, depth and status of one sequence's tree, into the cache.
+// Ancestor rows, depth and status of one sequence's tree, into the cache, by
+// synchronous pointer doubling over (node, word) pairs: node i keeps a covered
+// set C_i (itself and its nearest ancestors, a bit row) and nx_i, its nearest
+// ancestor outside C_i; a round adds C_(nx_i) and moves nx_i to nx_(nx_i),
+// every pair reading before any pair writes, so C_i doubles per round until
+// it is i with all its ancestors.  Two threads per node, eight row words
+// each (two 16-byte LDS accesses), so a round is a handful of LDS accesses
+// and two barriers.
 __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
-    __shared__ uint32_t s_mask[kPrepMaxN * (kPrepMaxN / 32)];
+    constexpr int WP = kPrepMaxN / 32;                  // row stride in LDS (words)
+    static_assert(kPrepThreads == 2 * kPrepMaxN && WP == 16, "two threads per node, 8 words each");
+    __shared__ __attribute__((aligned(16))) uint32_t s_mask[kPrepMaxN * WP];
     __shared__ int32_t s_jump[kPrepMaxN];
     __shared__ int s_flag;
-    const int b = blockIdx.x, N = a.N, W = (N + 31) / 32;
-    const int status = tree_build_lds(a.parent + (size_t)b * N, N, W, s_mask, s_jump, &s_flag);
+    const int b = blockIdx.x, N = a.N, W = (N + 31) / 32, tid = threadIdx.x;
+    const int i = tid >> 1, hh = tid & 1;               // node, half row (words 8 hh .. +7)
+    if (tid == 0) s_flag = 0x7fffffff;
     __syncthreads();
+    if (hh == 0 && i < N) {
+        const int p = a.parent[(size_t)b * N + i];
+        s_jump[i] = p;
+        if (p < -1 || p >= i) atomicMin(&s_flag, i);
+    }
+    uint4* row = reinterpret_cast<uint4*>(s_mask + i * WP + 8 * hh);
+    {
+        uint32_t w8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w8[e] = (i >> 5) == 8 * hh + e ? 1u << (i & 31) : 0u;
+        row[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+        row[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+    }
+    __syncthreads();
+    const int status = s_flag == 0x7fffffff ? 0 : s_flag + 1;
+    if (status == 0) {
+        for (;;) {
+            const int j = i < N ? s_jump[i] : -1;
+            uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
+            int nj = -1;
+            if (j >= 0) {
+                const uint4* rj = reinterpret_cast<const uint4*>(s_mask + j * WP + 8 * hh);
+                a0 = rj[0];
+                a1 = rj[1];
+                nj = s_jump[j];
+            }
+            __syncthreads();
+            if (j >= 0) {
+                uint4 r0 = row[0], r1 = row[1];
+                r0.x |= a0.x; r0.y |= a0.y; r0.z |= a0.z; r0.w |= a0.w;
+                r1.x |= a1.x; r1.y |= a1.y; r1.z |= a1.z; r1.w |= a1.w;
+                row[0] = r0;
+                row[1] = r1;
+                if (hh == 0) s_jump[i] = nj;
+            }
+            if (!__syncthreads_or(j >= 0 && nj >= 0)) break;
+        }
+    }
+    // strict rows (bit i cleared), zero for an invalid tree
     uint32_t* gm = a.anc_mask + (size_t)b * N * W;
-    for (int x = threadIdx.x; x < N * W; x += blockDim.x) gm[x] = s_mask[x];
-    for (int i = threadIdx.x; i < N; i += blockDim.x)
-        a.depth[(size_t)b * N + i] = status ? -1 : row_popc(s_mask + i * W, W);
-    if (threadIdx.x == 0) a.status[b] = status;
+    for (int x = tid; x < N * W; x += kPrepThreads) {
+        const int r = x / W, w = x - r * W;
+        gm[x] = status ? 0u : s_mask[r * WP + w] & ~((r >> 5) == w ? 1u << (r & 31) : 0u);
+    }
+    for (int r = tid; r < N; r += kPrepThreads)
+        a.depth[(size_t)b * N + r] = status ? -1 : row_popc(s_mask + r * WP, W) - 1;
+    if (tid == 0) a.status[b] = status;
 }
 
 // x of lane k of each lane quad, to all four lanes (k a compile-time value
