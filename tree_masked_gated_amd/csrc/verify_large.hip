@@ -148,7 +148,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     __shared__ __attribute__((aligned(16))) float s_beta[NP];
     __shared__ __attribute__((aligned(16))) int32_t s_jump[NP];
     __shared__ unsigned long long s_occ[NB];    // bit s of row t: tile (t, s), s < t, not all zero
-    __shared__ uint8_t s_tcol[NB][NB];          // row t's tiles: t, then its occupied blocks s < t
+    __shared__ uint8_t s_tcol[NB][NB];          // row t's tiles: t, then its occupied blocks s < t, descending
     // k rows of blocks 0 .. KC-1 in MFMA operand order: (block s, chunk cs) is
     // 1 KB, lane l's 16 bytes at l * 16 (row 16 s + l % 16, columns 32 cs +
     // 8 (l / 16) .. +7), so a fragment read is one conflict-free ds_read_b128
@@ -252,12 +252,16 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     if (slice == 0)
         for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
 
-    for (int t = tid; t < nblk; t += NT) {              // tile lists (occupancy complete)
+    // tile lists (occupancy complete): the diagonal, then the occupied blocks
+    // in descending order, so the blocks past the LDS k cache come first and
+    // get the prefetched slots
+    for (int t = tid; t < nblk; t += NT) {
         unsigned long long occ = s_occ[t] & ((1ull << t) - 1ull);
         s_tcol[t][0] = (uint8_t)t;
         for (int m = 1; occ; ++m) {
-            s_tcol[t][m] = (uint8_t)(__ffsll((unsigned long long)occ) - 1);
-            occ &= occ - 1ull;
+            const int hb = 63 - __clzll((long long)occ);
+            s_tcol[t][m] = (uint8_t)hb;
+            occ &= ~(1ull << hb);
         }
     }
 #pragma unroll
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             for (int e = 0; e < 4; ++e) s_dinv[par][a32_pos(4 * qd + e, c)] = bf16_rne(acc[e]);
         };
         // Row t's tiles: the diagonal tile first, then the occupied column
-        // blocks s < t in order; Gram wave gw computes tiles gw, gw + NG, ...
+        // blocks s < t, descending; Gram wave gw computes tiles gw, gw + NG, ...
         auto tile_col = [&](int t, unsigned long long occ, int m) __attribute__((always_inline)) {
             (void)occ;
             return __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]);
@@ -508,7 +512,11 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 R[g][m] = s_beta[i] * (vd[m] - __expf(s_lg[i]) * pk[m]);
             }
         }
-        // R_t += sum_{s<t} (-X_ts) U_s over occupied tiles, two blocks per MFMA
+        // R_t += sum_{s<t} (-X_ts) U_s over occupied tiles, two blocks per MFMA;
+        // even and odd pairs accumulate apart (four independent chains)
+        f32x4 R2[CG];
+#pragma unroll
+        for (int g = 0; g < CG; ++g) R2[g] = z;
 #pragma unroll
         for (int p = 0; p < NPR; ++p) {
             const int s = 2 * p;
@@ -519,10 +527,15 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                     bf16x8 nx = *reinterpret_cast<const bf16x8*>(xr + s * 256 + lane * 8);
                     if (!(hi_half ? o1 : o0)) nx = zero8;
 #pragma unroll
-                    for (int g = 0; g < CG; ++g) R[g] = mfma32(nx, up[g][p], R[g]);
+                    for (int g = 0; g < CG; ++g) {
+                        if (p & 1) R2[g] = mfma32(nx, up[g][p], R2[g]);
+                        else R[g] = mfma32(nx, up[g][p], R[g]);
+                    }
                 }
             }
         }
+#pragma unroll
+        for (int g = 0; g < CG; ++g) R[g] += R2[g];
         const bf16x8 di = *reinterpret_cast<const bf16x8*>(s_dinv[par] + (ln + 16 * (lq & 1)) * 8);
         const int node = 16 * t + ln;
 #pragma unroll
@@ -546,9 +559,9 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + c0 + 16 * g + 4 * lq) = UT;
         }
         // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T over occupied tiles
-        f32x4 Oc[CG];
+        f32x4 Oc[CG], Oc2[CG];
 #pragma unroll
-        for (int g = 0; g < CG; ++g) Oc[g] = z;
+        for (int g = 0; g < CG; ++g) Oc[g] = Oc2[g] = z;
 #pragma unroll
         for (int p = 0; p < NPR; ++p) {
             const int s = 2 * p;
@@ -559,10 +572,15 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                     bf16x8 yt = *reinterpret_cast<const bf16x8*>(yr + s * 256 + lane * 8);
                     if (!(hi_half ? o1 : o0)) yt = zero8;
 #pragma unroll
-                    for (int g = 0; g < CG; ++g) Oc[g] = mfma32(up[g][p], yt, Oc[g]);
+                    for (int g = 0; g < CG; ++g) {
+                        if (p & 1) Oc2[g] = mfma32(up[g][p], yt, Oc2[g]);
+                        else Oc[g] = mfma32(up[g][p], yt, Oc[g]);
+                    }
                 }
             }
         }
+#pragma unroll
+        for (int g = 0; g < CG; ++g) Oc[g] += Oc2[g];
         if (node < N) {
             const float egn = __expf(s_lg[node]);
 #pragma unroll
