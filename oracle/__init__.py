@@ -45,6 +45,8 @@ def _bind(path: str):
     lib.oracle_verify.argtypes = [ci] * 6 + [f64p] * 6 + [i32p, i32p, ci, ci] + \
         [f64p] * 4 + [i32p] * 3
     lib.oracle_verify.restype = ci
+    lib.oracle_accept.argtypes = [ci, ci] + [i32p] * 7
+    lib.oracle_accept.restype = ci
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ci
     return lib
@@ -81,6 +83,24 @@ def tree(parent: np.ndarray, lib=None):
     if rc:
         raise ValueError(f"oracle_tree failed: {rc}")
     return mask, depth, status
+
+
+def accept(parent, draft, target, target_root, lib=None):
+    """Greedy acceptance walk (see gdn_oracle.c): parent, draft, target [B][N]
+    int32, target_root [B] int32.  Returns (accepted, accept_len, next_token),
+    each [B] int32."""
+    lib = lib or load()
+    f = lambda a: np.ascontiguousarray(a, dtype=np.int32)
+    parent, draft, target, target_root = map(f, (parent, draft, target, target_root))
+    B, N = parent.shape
+    assert draft.shape == (B, N) == target.shape and target_root.shape == (B,)
+    acc = np.empty(B, np.int32)
+    alen = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    rc = lib.oracle_accept(B, N, parent, draft, target, target_root, acc, alen, nxt)
+    if rc:
+        raise ValueError(f"oracle_accept failed: {rc}")
+    return acc, alen, nxt
 
 
 def verify(S0, q, k, v, beta, g, parent, accepted, memo=False, nthreads=0, lib=None):

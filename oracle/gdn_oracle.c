@@ -113,6 +113,59 @@ int oracle_tree(int B, int N, const int32_t* parent, uint32_t* mask,
 
 /* ------------------------------------------------------------ recurrence */
 
+/*
+ * Greedy acceptance walk over one tree per sequence (page "Trees from
+ * Marginals", the speculative-decoding item: the drafter guesses, the verifier
+ * checks the guesses and keeps the ones that are right; section 3: the state
+ * is committed once the accepted branch is known).  Reading taken: greedy
+ * verification of a token tree.  target_root[b] is the verifier's token after
+ * the prefix and target[b][i] its token after node i (the argmax of its
+ * logits at that position).  Starting at the prefix, the walk moves to the
+ * first child (lowest index) whose draft token equals the current prediction,
+ * and stops when no child matches:
+ *     accepted[b]   = the last node reached, -1 if no root node matched;
+ *     accept_len[b] = the number of nodes reached (its depth + 1, or 0);
+ *     next_token[b] = the prediction at that point (the verifier's token that
+ *                     follows the accepted tokens).
+ * An invalid parent row gives accepted = -1, accept_len = -1 and
+ * next_token = target_root[b].
+ */
+int oracle_accept(int B, int N, const int32_t* parent, const int32_t* draft,
+                  const int32_t* target, const int32_t* target_root, int32_t* accepted,
+                  int32_t* accept_len, int32_t* next_token)
+{
+    if (B < 0 || N < 1) return -1;
+    for (int b = 0; b < B; ++b) {
+        const int32_t* par = parent + (size_t)b * N;
+        const int32_t* dr = draft + (size_t)b * N;
+        const int32_t* tg = target + (size_t)b * N;
+        int want = target_root[b];
+        if (tree_check(N, par)) {
+            accepted[b] = -1;
+            accept_len[b] = -1;
+            next_token[b] = want;
+            continue;
+        }
+        int cur = -1, len = 0;
+        for (;;) {
+            int found = -1;
+            for (int i = 0; i < N; ++i)
+                if (par[i] == cur && dr[i] == want) {
+                    found = i;
+                    break;
+                }
+            if (found < 0) break;
+            cur = found;
+            want = tg[cur];
+            ++len;
+        }
+        accepted[b] = cur;
+        accept_len[b] = len;
+        next_token[b] = want;
+    }
+    return 0;
+}
+
 /* One gated delta step on S (dv x dk, row-major), in the fixed order above. */
 static void gdn_step(int dv, int dk, double* S, const double* k, const double* v,
                      double beta, double g, double* w)

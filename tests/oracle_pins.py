@@ -11,7 +11,9 @@ when the oracle disagrees with:
   * a boolean transitive closure of the parent relation (masks, depth, paths);
   * a dense numpy linear solve of the unrolled tree system (tests/wy_dense.py);
   * tree invariants: siblings, non-ancestors, topological relabelling, and the
-    conventions for invalid trees and accepted indices.
+    conventions for invalid trees and accepted indices;
+  * for the acceptance walk, a per-node restatement of greedy acceptance
+    checked node by node (tests/oracle_pins.py, accept_brute_force).
 The same battery runs against deliberately broken copies of the oracle
 (tests/test_oracle_mutants.py) to show that each plausible mistake trips a pin.
 """
@@ -336,10 +338,79 @@ def pin_conventions(lib):
         assert st[0] == first
 
 
+def accept_brute_force(parent, draft, target, target_root):
+    """Greedy acceptance restated per node: node i is reached iff every node j
+    on its root-to-node path carries the prediction of j's predecessor (the
+    prefix's for a root) and is the lowest-index sibling carrying it; the
+    accepted node is the deepest node reached (at most one per depth)."""
+    N = len(parent)
+    if any(not (-1 <= parent[i] < i) for i in range(N)):
+        return -1, -1, int(target_root)
+    pred = lambda j: int(target_root) if j < 0 else int(target[j])
+    best, best_len = -1, 0
+    for i in range(N):
+        path, j = [], i
+        while j >= 0:
+            path.append(j)
+            j = parent[j]
+        ok = True
+        for j in path:
+            want = pred(parent[j])
+            first = min(x for x in range(N) if parent[x] == parent[j] and draft[x] == want) \
+                if any(parent[x] == parent[j] and draft[x] == want for x in range(N)) else None
+            if draft[j] != want or first != j:
+                ok = False
+                break
+        if ok and len(path) > best_len:
+            best, best_len = i, len(path)
+    return best, best_len, pred(best)
+
+
+def pin_accept_brute_force(lib):
+    """The acceptance walk against the per-node restatement on random trees
+    with a three-token vocabulary (so siblings often tie and paths run deep)."""
+    rng = np.random.default_rng(31)
+    trees = []
+    for n in (1, 2, 7, 20, 45):
+        for _ in range(6):
+            trees.append(W.tree_random_recursive(rng, n))
+    trees += [W.tree_chain(30), W.tree_star(12), W.tree_mary(rng, 3, 5)]
+    for parent in trees:
+        N = len(parent)
+        draft = rng.integers(0, 3, size=N).astype(np.int32)
+        target = rng.integers(0, 3, size=N).astype(np.int32)
+        root = np.array([rng.integers(0, 3)], np.int32)
+        acc, alen, nxt = oracle.accept(parent[None], draft[None], target[None], root, lib=lib)
+        assert (acc[0], alen[0], nxt[0]) == accept_brute_force(parent, draft, target, root[0]), parent
+
+
+def pin_accept_conventions(lib):
+    """Whole chain accepted; nothing accepted; the lowest-index tie wins; an
+    invalid parent row."""
+    N = 9
+    chain = W.tree_chain(N)
+    target = np.arange(100, 100 + N, dtype=np.int32)
+    draft = np.concatenate([[7], target[:-1]]).astype(np.int32)
+    acc, alen, nxt = oracle.accept(chain[None], draft[None], target[None], np.array([7], np.int32), lib=lib)
+    assert (acc[0], alen[0], nxt[0]) == (N - 1, N, target[N - 1])
+    acc, alen, nxt = oracle.accept(chain[None], draft[None], target[None], np.array([8], np.int32), lib=lib)
+    assert (acc[0], alen[0], nxt[0]) == (-1, 0, 8)
+    # two roots with the predicted token, each with a matching child
+    par = np.array([-1, -1, 0, 1], np.int32)
+    dr = np.array([5, 5, 6, 6], np.int32)
+    tg = np.array([6, 6, 1, 2], np.int32)
+    acc, alen, nxt = oracle.accept(par[None], dr[None], tg[None], np.array([5], np.int32), lib=lib)
+    assert (acc[0], alen[0], nxt[0]) == (2, 2, 1)
+    bad = chain.copy()
+    bad[4] = 4
+    acc, alen, nxt = oracle.accept(bad[None], draft[None], target[None], np.array([7], np.int32), lib=lib)
+    assert (acc[0], alen[0], nxt[0]) == (-1, -1, 7)
+
+
 ALL_PINS = [
     pin_autograd_step, pin_hand_example, pin_beta_zero_pure_decay,
     pin_projector_writes_v, pin_chain_product_form, pin_chain_is_linear_scan,
     pin_masks_paths, pin_dense_solve, pin_grouped_heads, pin_siblings_share_parent,
     pin_non_ancestors_do_not_matter, pin_topological_relabel, pin_memo_equals_walk,
-    pin_conventions,
+    pin_conventions, pin_accept_brute_force, pin_accept_conventions,
 ]

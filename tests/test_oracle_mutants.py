@@ -56,6 +56,13 @@ MUTANTS = {
                      "const double* Sp = S0;"),
     # a parent equal to the node itself is accepted as valid
     "check_allows_self": ("par[i] >= i) return i + 1;", "par[i] > i) return i + 1;"),
+    # the acceptance walk takes the last matching child instead of the first
+    "accept_last_child": ("                    found = i;\n                    break;\n",
+                          "                    found = i;\n"),
+    # the acceptance walk compares against the child's own prediction
+    "accept_own_target": ("if (par[i] == cur && dr[i] == want) {", "if (par[i] == cur && dr[i] == tg[i]) {"),
+    # the accepted length counts the prefix as a node
+    "accept_len_off": ("        int cur = -1, len = 0;", "        int cur = -1, len = 1;"),
 }
 
 CHILD = r"""
