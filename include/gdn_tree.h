@@ -180,6 +180,33 @@ int gdn_tree_commit_verify(const gdn_tree_dims* dims, const float* S_prev, float
                            const int32_t* parent, void* o, const gdn_tree_cache* cache,
                            hipStream_t stream);
 
+/*
+ * Greedy acceptance walk over each sequence's draft tree, on the device (page
+ * "Trees from Marginals", the speculative-decoding item: the verifier keeps
+ * the drafter's guesses that are right; section 3: the state is committed
+ * once the accepted branch is known).  With it, the accepted node reaches
+ * gdn_tree_commit / gdn_tree_commit_verify without a host round trip.
+ *
+ *   parent      [B][N] int32  the tree, as for gdn_tree_verify
+ *   draft       [B][N] int32  each node's draft token
+ *   target      [B][N] int32  the verifier's token after each node (argmax of
+ *                             its logits at that node)
+ *   target_root [B]    int32  the verifier's token after the prefix
+ *   accepted    [B]    int32  out: the accepted node, -1 if none
+ *   accept_len  [B]    int32  out: nodes accepted (depth + 1), 0 if none,
+ *                             -1 for an invalid parent row
+ *   next_token  [B]    int32  out: the verifier's token after the accepted
+ *                             tokens (target_root if none)
+ *
+ * From the prefix, the walk moves to the lowest-index child whose draft token
+ * equals the current prediction and stops where no child matches.  Only
+ * dims->batch and dims->n_nodes are used (the other fields are checked as for
+ * the other calls).  An invalid parent row gives accepted = -1.
+ */
+int gdn_tree_accept(const gdn_tree_dims* dims, const int32_t* parent, const int32_t* draft,
+                    const int32_t* target, const int32_t* target_root, int32_t* accepted,
+                    int32_t* accept_len, int32_t* next_token, hipStream_t stream);
+
 /* Static description of a gdn_status value. */
 const char* gdn_tree_strerror(int status);
 

@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["gdn_tree_cache_bytes", "gdn_tree_commit", "gdn_tree_commit_verify",
-                     "gdn_tree_strerror", "gdn_tree_verify"]
+    assert names == ["gdn_tree_accept", "gdn_tree_cache_bytes", "gdn_tree_commit",
+                     "gdn_tree_commit_verify", "gdn_tree_strerror", "gdn_tree_verify"]
     out = subprocess.run(["nm", "-D", "--defined-only", T.lib_path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)", out))
@@ -103,6 +103,14 @@ def test_error_codes():
     assert CV(good, ok3, other, ok10,
               T.Cache(FAKE, FAKE, FAKE, FAKE + 1280, FAKE)) == -6
     assert CV(T.dims(0, 7, 1, 2, 16, 16, 0), [None] * 3, None, [None] * 10, None) == 0
+    # acceptance walk
+    AC = lambda d, p: T._lib.gdn_tree_accept(ctypes.byref(d) if d is not None else None, *p, None)
+    ok7 = [FAKE] * 7
+    assert AC(None, ok7) == -1
+    assert AC(good, ok7[:2] + [None] + ok7[3:]) == -1
+    assert AC(good, ok7[:6] + [ODD]) == -5
+    assert AC(T.dims(2, 2000, 1, 2, 16, 16, 0), ok7) == -2
+    assert AC(T.dims(0, 7, 1, 2, 16, 16, 0), [None] * 7) == 0
 
 
 def test_strerror_and_cache_bytes():

@@ -17,6 +17,7 @@ from typing import Dict, Optional
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "Dims", "Cache", "lib_path", "dims",
     "gdn_tree_cache_bytes", "gdn_tree_verify", "gdn_tree_commit", "gdn_tree_commit_verify",
+    "gdn_tree_accept",
     "gdn_tree_strerror", "TreeCache",
 ]
 
@@ -59,6 +60,8 @@ _lib.gdn_tree_commit.restype = _i
 _lib.gdn_tree_commit_verify.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 3 + [ctypes.POINTER(Cache)] + \
     [_vp] * 10 + [ctypes.POINTER(Cache), _vp]
 _lib.gdn_tree_commit_verify.restype = _i
+_lib.gdn_tree_accept.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 7 + [_vp]
+_lib.gdn_tree_accept.restype = _i
 _lib.gdn_tree_strerror.argtypes = [_i]
 _lib.gdn_tree_strerror.restype = ctypes.c_char_p
 
@@ -237,6 +240,25 @@ def gdn_tree_commit_verify(d: Dims, S_prev, S_new, k_prev, cache_prev, accepted_
                                      *mid, ctypes.byref(_cache_struct(cache)), _stream(stream))
     if rc:
         raise GdnError(rc, "gdn_tree_commit_verify")
+
+
+def gdn_tree_accept(d: Dims, parent, draft, target, target_root, accepted, accept_len, next_token,
+                    stream=None) -> None:
+    """Enqueue the greedy acceptance walk (see gdn_tree.h)."""
+    torch = _torch()
+    B, N = d.batch, d.n_nodes
+    ptrs = [
+        _ptr(parent, (B, N), torch.int32, "parent"),
+        _ptr(draft, (B, N), torch.int32, "draft"),
+        _ptr(target, (B, N), torch.int32, "target"),
+        _ptr(target_root, (B,), torch.int32, "target_root"),
+        _ptr(accepted, (B,), torch.int32, "accepted"),
+        _ptr(accept_len, (B,), torch.int32, "accept_len"),
+        _ptr(next_token, (B,), torch.int32, "next_token"),
+    ]
+    rc = _lib.gdn_tree_accept(ctypes.byref(d), *ptrs, _stream(stream))
+    if rc:
+        raise GdnError(rc, "gdn_tree_accept")
 
 
 def _check_cache(c: TreeCache, d: Dims):

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdntree.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.hip", "verify_generic.hip", "verify_tiled.hip", "verify_large.hip", "commit.hip"]
+SOURCES = ["abi.hip", "verify_generic.hip", "verify_tiled.hip", "verify_large.hip", "commit.hip",
+           "accept.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}",

@@ -144,6 +144,22 @@ int gdn_tree_commit_verify(const gdn_tree_dims* dims, const float* S_prev, float
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+int gdn_tree_accept(const gdn_tree_dims* dims, const int32_t* parent, const int32_t* draft,
+                    const int32_t* target, const int32_t* target_root, int32_t* accepted,
+                    int32_t* accept_len, int32_t* next_token, hipStream_t stream) {
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (dims->batch == 0) return GDN_OK;
+    if (!parent || !draft || !target || !target_root || !accepted || !accept_len || !next_token)
+        return GDN_ERR_NULL;
+    if (misaligned(parent) || misaligned(draft) || misaligned(target) || misaligned(target_root) ||
+        misaligned(accepted) || misaligned(accept_len) || misaligned(next_token))
+        return GDN_ERR_ALIGN;
+    AcceptArgs a{dims->batch, dims->n_nodes, parent, draft, target, target_root,
+                 accepted, accept_len, next_token};
+    return launch_accept(a, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 const char* gdn_tree_strerror(int status) {
     switch (status) {
         case GDN_OK: return "ok";

@@ -25,4 +25,17 @@ hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream);
 // Deferred commit of the accepted node's state.
 hipError_t launch_commit(const CommitArgs& a, int io, hipStream_t stream);
 
+// Greedy acceptance walk, one wave per sequence.
+struct AcceptArgs {
+    int B, N;
+    const int32_t* parent;
+    const int32_t* draft;
+    const int32_t* target;
+    const int32_t* target_root;
+    int32_t* accepted;
+    int32_t* accept_len;
+    int32_t* next_token;
+};
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+
 }  // namespace gdn
