@@ -2,7 +2,9 @@
 
 A step is one decode iteration of the 36-layer stack: for every layer, verify
 all 64 draft trees (128 nodes, M = 8 wide, 16 deep; 16 key / 32 value heads,
-d = 128, bf16 q/k/v, fp32 state) and commit each sequence's accepted node.
+d = 128, bf16 q/k/v, fp32 state) and commit each sequence's accepted node,
+found on the device by the greedy acceptance walk over synthetic draft and
+verifier tokens (once per step; the tokens make it accept a random leaf).
 The committed states of step t are the prefix states of step t + 1, as in a
 decode loop.  By default each layer is one launch of gdn_tree_commit_verify:
 the commit of the tree verified at the previous step, then this step's
@@ -101,7 +103,12 @@ def run_gpu(args, s):
     log(f"generated and uploaded in {time.time() - t0:.1f} s")
     dims = T.dims(s.batch, s.n_nodes, s.h_k, s.h_v, s.d, s.d, s.io)
     par = W.to_device(parent, device=dev)
-    acc = W.to_device(accepted, device=dev)
+    # the acceptance walk runs on the device each step and writes acc; the
+    # synthetic tokens make it accept the workload's chosen leaf
+    draft, target, troot = (W.to_device(x, device=dev) for x in W.make_tokens(s, parent, accepted))
+    acc = torch.empty((s.batch,), dtype=torch.int32, device=dev)
+    alen = torch.empty((s.batch,), dtype=torch.int32, device=dev)
+    nxt = torch.empty((s.batch,), dtype=torch.int32, device=dev)
     # two caches per layer: the fused step reads the previous tree's while it
     # writes the new tree's
     caches2 = [[T.TreeCache(dims, dev), T.TreeCache(dims, dev) if args.fused else None]
@@ -133,21 +140,29 @@ def run_gpu(args, s):
                                  caches2[l][cur[0]], acc, path, plen, x["q"], x["k"], x["v"],
                                  x["beta"], x["g"], par, o[l], caches2[l][1 - cur[0]], sptr)
 
+    def accept(_l=0):
+        T.gdn_tree_accept(dims, par, draft, target, troot, acc, alen, nxt, sptr)
+
     def step():
         if args.fused:
-            # commit of the tree verified last step, then this step's tree
+            # commit of the tree verified last step, then this step's tree,
+            # then its acceptance walk (read by the next step's commits)
             for l in range(L):
                 commit_verify(l)
+            accept()
             cur[0] ^= 1
         else:
             for l in range(L):
                 verify(l)
+            accept()
+            for l in range(L):
                 commit(l)
         phase[0] ^= 1
 
     if args.fused:
         for l in range(L):            # the first tree has no commit before it
             verify(l)
+    accept()
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
@@ -182,12 +197,15 @@ def run_gpu(args, s):
     fused_ms = timed(commit_verify) if args.fused else None
     verify_ms = timed(verify)
     commit_ms = timed(commit)
+    accept_ms = timed(accept)
     log(f"verify {verify_ms * 1e3:.1f} us/launch, commit {commit_ms * 1e3:.1f} us/launch"
-        + (f", commit+verify {fused_ms * 1e3:.1f} us/launch" if args.fused else ""))
+        + (f", commit+verify {fused_ms * 1e3:.1f} us/launch" if args.fused else "")
+        + f", accept {accept_ms * 1e3:.1f} us/launch")
     path_lens = plen.cpu().numpy()
+    assert np.array_equal(acc.cpu().numpy(), accepted), "the acceptance walk missed the chosen leaf"
     return {
         "total_ms": total_ms, "verify_ms": verify_ms, "commit_ms": commit_ms,
-        "fused_ms": fused_ms,
+        "fused_ms": fused_ms, "accept_ms": accept_ms,
         "verify_bytes": verify_bytes(s, e), "commit_bytes": commit_bytes(s, e, path_lens),
         "path_lens": path_lens, "parent": parent, "accepted": accepted,
     }
@@ -349,6 +367,7 @@ def main():
             "launch_us": r["commit_ms"] * 1e3, "alg_bytes_per_launch": r["commit_bytes"],
             "achieved_GBs": r["commit_bytes"] / (r["commit_ms"] * 1e-3) / 1e9,
         },
+        "accept": {"launch_us": r["accept_ms"] * 1e3, "per": "step"},
         "cpu_baseline": base,
     }
     print(json.dumps(out), flush=True)

@@ -2,6 +2,7 @@
 import hashlib
 
 import numpy as np
+import pytest
 import torch
 
 import workloads as W
@@ -60,3 +61,17 @@ def test_tree_shapes():
     assert (acc == 255).all() and (par[:, 1:] == np.arange(255)).all()
     par, acc = W.make_trees(W.spec("tiny7"))
     assert par[0].tolist() == [-1, 0, 0, 1, 1, 2, 2] and acc[0] == 5
+
+
+@pytest.mark.parametrize("name", ["tiny7", "mary64_b32", "mary128_b64_l36", "chain256_b8", "rrt512_b8"])
+def test_tokens_accept_the_chosen_leaf(name):
+    """The benchmark's synthetic tokens make the oracle's acceptance walk stop
+    at the workload's chosen node, with the path length of that node."""
+    import oracle
+    s = W.spec(name)
+    parent, accepted = W.make_trees(s)
+    draft, target, root = W.make_tokens(s, parent, accepted)
+    acc, alen, _ = oracle.accept(parent, draft, target, root)
+    assert np.array_equal(acc, accepted)
+    _, depth, _ = oracle.tree(parent)
+    assert np.array_equal(alen, depth[np.arange(len(accepted)), accepted] + 1)

@@ -187,6 +187,27 @@ def make_trees(s: Spec):
     return parent, accepted
 
 
+def make_tokens(s: Spec, parent: np.ndarray, accepted: np.ndarray, vocab: int = 32000):
+    """Synthetic draft and verifier tokens under which greedy acceptance walks
+    exactly to `accepted`: (draft [B][N], target [B][N], target_root [B]),
+    int32.  A node on the accepted path carries its predecessor's verifier
+    token, every other node a different token."""
+    rng = np.random.default_rng(np.random.SeedSequence(s.seed).spawn(2)[1])
+    B, N = parent.shape
+    target = rng.integers(0, vocab, size=(B, N)).astype(np.int32)
+    root = rng.integers(0, vocab, size=B).astype(np.int32)
+    draft = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        on_path = np.zeros(N, dtype=bool)
+        j = int(accepted[b])
+        while j >= 0:
+            on_path[j] = True
+            j = int(parent[b, j])
+        pred = np.where(parent[b] < 0, root[b], target[b, np.maximum(parent[b], 0)])
+        draft[b] = np.where(on_path, pred, (pred + 1) % vocab)
+    return draft, target, root
+
+
 # ---------------------------------------------------------------- values
 
 def _normalise(x: np.ndarray) -> np.ndarray:
