@@ -4,12 +4,17 @@
 // factorized priors": the verifier keeps the drafter's guesses that are
 // right; section 3: the state is committed once the accepted branch is known).
 //
-// One wave per sequence.  Lane l holds parent, draft and target token of
-// nodes l + 64 k in registers.  Starting from the prefix, each step looks for
-// the lowest-index child of the current node whose draft token equals the
-// current prediction: a ballot per 64-node chunk, from the chunk holding the
-// current node + 1 (children follow their parent), stopping at the first
-// chunk with a match.  The walk is as long as the accepted path.
+// The walk (from the prefix, to the lowest-index child whose draft token is
+// the current prediction, until none is) is evaluated in parallel, one
+// workgroup per sequence:
+//  1. node i matches if its draft token equals its predecessor's verifier
+//     token (the prefix's for a root) and no lower-index sibling matches
+//     (an atomic minimum per parent);
+//  2. a node is on the walk iff it and all its ancestors match: synchronous
+//     pointer doubling carries, per node, the AND of the flags and the size of
+//     its covered path segment, log2(depth) + 1 rounds;
+//  3. at most one node per depth is on the walk, so the accepted node is the
+//     deepest one (a maximum over (depth, index) keys).
 #include <stdint.h>
 
 #include "gdn_common.hpp"
@@ -19,58 +24,110 @@ namespace gdn {
 
 namespace {
 
-constexpr int kAcceptChunks = kMaxNodes / 64;
+constexpr int kAcceptThreads = 256;
+constexpr int kAcceptPer = kMaxNodes / kAcceptThreads;
 
-__global__ __launch_bounds__(64) void accept_kernel(AcceptArgs a) {
-    const int b = blockIdx.x, lane = threadIdx.x, N = a.N;
-    const int nch = (N + 63) / 64;
+__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
+    __shared__ int32_t s_tg[kMaxNodes];
+    __shared__ int32_t s_first[kMaxNodes + 1];    // lowest matching child of parent p, at p + 1
+    __shared__ int32_t s_jump[kMaxNodes];
+    __shared__ int32_t s_cnt[kMaxNodes];
+    __shared__ int32_t s_ok[kMaxNodes];
+    __shared__ int s_bad, s_best;
+    const int b = blockIdx.x, tid = threadIdx.x, N = a.N;
     const int32_t* par = a.parent + (size_t)b * N;
     const int32_t* dr = a.draft + (size_t)b * N;
     const int32_t* tg = a.target + (size_t)b * N;
-    int pr[kAcceptChunks], dv[kAcceptChunks], tv[kAcceptChunks];
-#pragma unroll
-    for (int k = 0; k < kAcceptChunks; ++k) {          // unconditional, rows clamped
-        const int i = min(lane + 64 * k, N - 1);
-        pr[k] = par[i];
-        dv[k] = dr[i];
-        tv[k] = tg[i];
+    const int root = a.target_root[b];
+    if (tid == 0) {
+        s_bad = 0;
+        s_best = -1;
     }
-    int want = a.target_root[b];
+    int p[kAcceptPer], d[kAcceptPer];
+#pragma unroll
+    for (int k = 0; k < kAcceptPer; ++k) {
+        const int i = tid + kAcceptThreads * k;
+        const int ic = min(i, N - 1);
+        p[k] = par[ic];
+        d[k] = dr[ic];
+        if (i < N) s_tg[i] = tg[ic];
+        s_first[i] = 0x7fffffff;
+    }
+    if (tid == 0) s_first[kMaxNodes] = 0x7fffffff;
+    __syncthreads();
     bool bad = false;
 #pragma unroll
-    for (int k = 0; k < kAcceptChunks; ++k) {
-        const int i = lane + 64 * k;
-        bad |= __ballot(i < N && (pr[k] < -1 || pr[k] >= i)) != 0ull;
+    for (int k = 0; k < kAcceptPer; ++k) {
+        const int i = tid + kAcceptThreads * k;
+        bad |= i < N && (p[k] < -1 || p[k] >= i);
     }
-    int cur = -1, len = 0;
-    if (bad) {
-        len = -1;
-    } else {
-        for (;;) {
-            int found = -1, nwant = 0;
-            const int k0 = (cur + 1) >> 6;
+    if (bad) s_bad = 1;
+    __syncthreads();
+    const bool invalid = s_bad != 0;
+    if (!invalid) {
+        bool mt[kAcceptPer];
 #pragma unroll
-            for (int k = 0; k < kAcceptChunks; ++k) {
-                if (found < 0 && k >= k0 && k < nch) {
-                    const int i = lane + 64 * k;
-                    const unsigned long long m = __ballot(i < N && pr[k] == cur && dv[k] == want);
-                    if (m) {
-                        const int l = __ffsll(m) - 1;
-                        found = 64 * k + l;
-                        nwant = __builtin_amdgcn_readlane(tv[k], l);
-                    }
+        for (int k = 0; k < kAcceptPer; ++k) {           // 1. matches, lowest per parent
+            const int i = tid + kAcceptThreads * k;
+            const int pred = p[k] < 0 ? root : s_tg[p[k]];
+            mt[k] = i < N && d[k] == pred;
+            if (mt[k]) atomicMin(&s_first[p[k] + 1], i);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kAcceptPer; ++k) {
+            const int i = tid + kAcceptThreads * k;
+            if (i < N) {
+                s_ok[i] = mt[k] && s_first[p[k] + 1] == i;
+                s_cnt[i] = 1;
+                s_jump[i] = p[k];
+            }
+        }
+        __syncthreads();
+        for (;;) {                                       // 2. AND over the ancestors
+            int ok[kAcceptPer], cnt[kAcceptPer], nj[kAcceptPer];
+            bool act = false;
+#pragma unroll
+            for (int k = 0; k < kAcceptPer; ++k) {
+                const int i = tid + kAcceptThreads * k;
+                const int j = i < N ? s_jump[i] : -1;
+                ok[k] = 1;
+                cnt[k] = 0;
+                nj[k] = -1;
+                if (j >= 0) {
+                    ok[k] = s_ok[j];
+                    cnt[k] = s_cnt[j];
+                    nj[k] = s_jump[j];
+                    act = true;
                 }
             }
-            if (found < 0) break;
-            cur = found;
-            want = nwant;
-            ++len;
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < kAcceptPer; ++k) {
+                const int i = tid + kAcceptThreads * k;
+                if (i < N && s_jump[i] >= 0) {
+                    s_ok[i] &= ok[k];
+                    s_cnt[i] += cnt[k];
+                    s_jump[i] = nj[k];
+                }
+            }
+            if (!__syncthreads_or(act)) break;
         }
+        int best = -1;                                   // 3. the deepest node on the walk
+#pragma unroll
+        for (int k = 0; k < kAcceptPer; ++k) {
+            const int i = tid + kAcceptThreads * k;
+            if (i < N && s_ok[i]) best = max(best, s_cnt[i] * (kMaxNodes + 1) + i);
+        }
+        if (best >= 0) atomicMax(&s_best, best);
+        __syncthreads();
     }
-    if (lane == 0) {
-        a.accepted[b] = cur;
-        a.accept_len[b] = len;
-        a.next_token[b] = want;
+    if (tid == 0) {
+        const int key = s_best;
+        const int acc = key < 0 ? -1 : key % (kMaxNodes + 1);
+        a.accepted[b] = acc;
+        a.accept_len[b] = invalid ? -1 : (key < 0 ? 0 : key / (kMaxNodes + 1));
+        a.next_token[b] = acc < 0 ? root : s_tg[acc];
     }
 }
 
@@ -79,7 +136,8 @@ __global__ __launch_bounds__(64) void accept_kernel(AcceptArgs a) {
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream) {
     AcceptArgs copy = a;
     void* args[] = {&copy};
-    return hipLaunchKernel((const void*)accept_kernel, dim3((unsigned)a.B), dim3(64), args, 0, stream);
+    return hipLaunchKernel((const void*)accept_kernel, dim3((unsigned)a.B), dim3(kAcceptThreads), args, 0,
+                           stream);
 }
 
 }  // namespace gdn
