@@ -685,9 +685,13 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         // stores retire in order).  One program point for both paths, so no
         // register copy of a load in flight is needed where they meet.
         load_small(pf, more);
-        if constexpr (FUSED) commit_small(pf);
+        if constexpr (FUSED) {
+            commit_small(pf);
+            // (fused: the next item's S0 rows right here; spread over the solve
+            // they would meet the committed rows' stores less well)
 #pragma unroll
-        for (int g = 0; g < CG; ++g) load_s0(pf, g, more);
+            for (int g = 0; g < CG; ++g) load_s0(pf, g, more);
+        }
         if (!status) {
             // ---- 4. diagonal blocks: (I + X_tt)^-1 in fp32 ----------------------
             for (int blk = tid >> 4; blk < HPW * NB; blk += NT / 16) {
@@ -708,9 +712,10 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
             }
             lds_barrier();
         }
-        // v landed: only the 8 * CG S0 loads issued last may still be in flight
-        // (the explicit count lets them overlap the solve).
-        wait_vmem_le<8 * CG>();
+        // v landed: only the next item's small loads (and, fused, its S0 rows),
+        // issued after it, may still be in flight (the explicit count lets them
+        // overlap the solve).
+        wait_vmem_le<FUSED ? NSM + 2 + 8 * CG : NSM>();
         if constexpr (FUSED) commit_take_small();
         if (wave == NW - 1) write_tree_cache(b, h0, hk == 0 && hg == 0, status);
         // ---- 5. per wave: projection, blocked substitution, output ---------
@@ -738,6 +743,13 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         const int nsolve = status ? 0 : nblk;
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
+            // (not fused) the next item's S0 rows, one column group at a time,
+            // spread over the solve so that their reads share the HBM with its
+            // stores
+            if constexpr (!FUSED) {
+                if (t == NB / 4) load_s0(pf, 0, more);
+                if (t == NB / 2) load_s0(pf, 1, more);
+            }
             if (t >= nsolve) continue;                        // uniform
             f32x4 pk[CG], pqT[CG];
 #pragma unroll
