@@ -207,6 +207,62 @@ int gdn_tree_accept(const gdn_tree_dims* dims, const int32_t* parent, const int3
                     const int32_t* target, const int32_t* target_root, int32_t* accepted,
                     int32_t* accept_len, int32_t* next_token, hipStream_t stream);
 
+/*
+ * Ragged batches.  The trees of one batch may differ in size: the pages run
+ * draft budgets of 16 and 64 nodes (page "Technisches Resuemee: TreeFlash",
+ * experimental results) and leave batches of several sequences open (its
+ * limitations item), so a batch that mixes budgets is the serving case.  The
+ * *_ragged calls take the per-node arrays packed, sequence after sequence:
+ *
+ *   offsets [B + 1] int32, DEVICE: sequence b owns rows offsets[b] ..
+ *           offsets[b+1] - 1 of every per-node array, n_b = offsets[b+1] -
+ *           offsets[b] nodes (0 allowed), offsets[0] = 0, non-decreasing;
+ *           T = offsets[B] rows in all.  4-byte aligned (else GDN_ERR_ALIGN),
+ *           not NULL (else GDN_ERR_NULL).
+ *   dims->n_nodes = N, the largest tree allowed (every n_b <= N): the cache
+ *           keeps its [B][N] layout and sizes (gdn_tree_cache_bytes), the
+ *           kernels are chosen by N, and a tree of n_b < N nodes computes
+ *           only its own rows.
+ *
+ * Per-node arrays become [T][...]: q, k [T][H_k][d_k]; v, o [T][H_v][d_v];
+ * beta, g [T][H_v]; parent, draft, target, and a commit's path [T] (indices
+ * local to their tree: parent -1 or < i; path holds root..accepted, then -1,
+ * in the tree's own n_b slots).  Cache rows i >= n_b: anc_mask zero, depth
+ * -1, u and log_gamma unspecified.  The offsets are read on the device: a
+ * sequence with offsets[b] < 0 or n_b outside [0, N] gets tree_status -1,
+ * none of its rows is read or written, its commit gives path_len -1 and
+ * S_out = S_in, and its acceptance accepted = -1, accept_len = -1.  The
+ * caller guarantees that every array holds T rows.  An empty tree (n_b = 0)
+ * is valid: nothing to verify, and only accepted = -1 commits it.
+ * Otherwise each call behaves as its dense form on each tree alone.
+ */
+int gdn_tree_verify_ragged(const gdn_tree_dims* dims, const int32_t* offsets, const float* S0,
+                           const void* q, const void* k, const void* v, const float* beta,
+                           const float* g, const int32_t* parent, void* o,
+                           const gdn_tree_cache* cache, hipStream_t stream);
+
+/* offsets: the verified tree's, as given to gdn_tree_verify_ragged. */
+int gdn_tree_commit_ragged(const gdn_tree_dims* dims, const int32_t* offsets, const float* S_in,
+                           float* S_out, const void* k, const gdn_tree_cache* cache,
+                           const int32_t* accepted, int32_t* path, int32_t* path_len,
+                           hipStream_t stream);
+
+/* offsets_prev: the previous tree's (k_prev, path_prev); offsets: the new
+ * tree's (q, k, v, beta, g, parent, o).  Both trees have at most N nodes. */
+int gdn_tree_commit_verify_ragged(const gdn_tree_dims* dims, const int32_t* offsets_prev,
+                                  const float* S_prev, float* S_new, const void* k_prev,
+                                  const gdn_tree_cache* cache_prev, const int32_t* accepted_prev,
+                                  int32_t* path_prev, int32_t* path_len_prev,
+                                  const int32_t* offsets, const void* q, const void* k,
+                                  const void* v, const float* beta, const float* g,
+                                  const int32_t* parent, void* o, const gdn_tree_cache* cache,
+                                  hipStream_t stream);
+
+int gdn_tree_accept_ragged(const gdn_tree_dims* dims, const int32_t* offsets, const int32_t* parent,
+                           const int32_t* draft, const int32_t* target, const int32_t* target_root,
+                           int32_t* accepted, int32_t* accept_len, int32_t* next_token,
+                           hipStream_t stream);
+
 /* Static description of a gdn_status value. */
 const char* gdn_tree_strerror(int status);
 

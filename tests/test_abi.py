@@ -22,8 +22,10 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["gdn_tree_accept", "gdn_tree_cache_bytes", "gdn_tree_commit",
-                     "gdn_tree_commit_verify", "gdn_tree_strerror", "gdn_tree_verify"]
+    assert names == ["gdn_tree_accept", "gdn_tree_accept_ragged", "gdn_tree_cache_bytes",
+                     "gdn_tree_commit", "gdn_tree_commit_ragged", "gdn_tree_commit_verify",
+                     "gdn_tree_commit_verify_ragged", "gdn_tree_strerror", "gdn_tree_verify",
+                     "gdn_tree_verify_ragged"]
     out = subprocess.run(["nm", "-D", "--defined-only", T.lib_path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)", out))
@@ -111,6 +113,47 @@ def test_error_codes():
     assert AC(good, ok7[:6] + [ODD]) == -5
     assert AC(T.dims(2, 2000, 1, 2, 16, 16, 0), ok7) == -2
     assert AC(T.dims(0, 7, 1, 2, 16, 16, 0), [None] * 7) == 0
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="fake device pointers are only passed where no GPU exists")
+def test_ragged_error_codes():
+    """The ragged calls check their offsets pointer (NULL -1, not 4-byte aligned
+    -5) after the dims and before everything else, and otherwise run the dense
+    calls' checks."""
+    r = lambda c: ctypes.byref(c) if c is not None else None
+    good = T.dims(2, 7, 1, 2, 16, 16, "f32")
+    cache = T.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
+    other = T.Cache(FAKE + 256, FAKE + 512, FAKE + 768, FAKE + 1024, FAKE + 1280)
+    OFF, OFF_ODD = FAKE + 4, FAKE + 2       # int32 alignment suffices for offsets
+    VR = lambda d, off, p, c: T._lib.gdn_tree_verify_ragged(r(d), off, *p, r(c), None)
+    ok8 = [FAKE] * 8
+    assert VR(None, OFF, ok8, cache) == -1
+    assert VR(good, None, ok8, cache) == -1
+    assert VR(good, OFF_ODD, ok8, cache) == -5
+    assert VR(good, OFF, ok8[:7] + [None], cache) == -1
+    assert VR(good, OFF, ok8[:3] + [ODD] + ok8[4:], cache) == -5
+    assert VR(T.dims(2, 1025, 1, 2, 16, 16, 0), OFF, ok8, cache) == -2
+    assert VR(T.dims(0, 7, 1, 2, 16, 16, 0), None, [None] * 8, None) == 0
+    CR = lambda d, off, p, c, t: T._lib.gdn_tree_commit_ragged(r(d), off, *p, r(c), *t, None)
+    assert CR(good, None, [FAKE] * 3, cache, (FAKE,) * 3) == -1
+    assert CR(good, OFF_ODD, [FAKE] * 3, cache, (FAKE,) * 3) == -5
+    assert CR(good, OFF, [FAKE] * 3, cache, (FAKE, None, FAKE)) == -1
+    assert CR(T.dims(2, 7, 1, 2, 16, 16, 9), OFF, [FAKE] * 3, cache, (FAKE,) * 3) == -3
+    CVR = lambda d, op, head, cp, mid, c: T._lib.gdn_tree_commit_verify_ragged(
+        r(d), op, *head, r(cp), *mid, r(c), None)
+    mid = lambda off: [FAKE] * 3 + [off] + [FAKE] * 7
+    assert CVR(good, None, [FAKE] * 3, cache, mid(OFF), other) == -1
+    assert CVR(good, OFF, [FAKE] * 3, cache, mid(None), other) == -1
+    assert CVR(good, OFF, [FAKE] * 3, cache, mid(OFF_ODD), other) == -5
+    assert CVR(good, OFF, [FAKE] * 3, cache, mid(OFF), cache) == -6
+    assert CVR(T.dims(0, 7, 1, 2, 16, 16, 0), None, [None] * 3, None, [None] * 11, None) == 0
+    ACR = lambda d, off, p: T._lib.gdn_tree_accept_ragged(r(d), off, *p, None)
+    ok7 = [FAKE] * 7
+    assert ACR(good, None, ok7) == -1
+    assert ACR(good, OFF_ODD, ok7) == -5
+    assert ACR(good, OFF, ok7[:6] + [ODD]) == -5
+    assert ACR(T.dims(0, 7, 1, 2, 16, 16, 0), None, [None] * 7) == 0
 
 
 def test_strerror_and_cache_bytes():

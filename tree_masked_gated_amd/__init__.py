@@ -17,7 +17,8 @@ from typing import Dict, Optional
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "Dims", "Cache", "lib_path", "dims",
     "gdn_tree_cache_bytes", "gdn_tree_verify", "gdn_tree_commit", "gdn_tree_commit_verify",
-    "gdn_tree_accept",
+    "gdn_tree_accept", "gdn_tree_verify_ragged", "gdn_tree_commit_ragged",
+    "gdn_tree_commit_verify_ragged", "gdn_tree_accept_ragged", "check_offsets",
     "gdn_tree_strerror", "TreeCache",
 ]
 
@@ -62,6 +63,16 @@ _lib.gdn_tree_commit_verify.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 3 + [cty
 _lib.gdn_tree_commit_verify.restype = _i
 _lib.gdn_tree_accept.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 7 + [_vp]
 _lib.gdn_tree_accept.restype = _i
+_lib.gdn_tree_verify_ragged.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 9 + [ctypes.POINTER(Cache), _vp]
+_lib.gdn_tree_verify_ragged.restype = _i
+_lib.gdn_tree_commit_ragged.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 4 + \
+    [ctypes.POINTER(Cache)] + [_vp] * 3 + [_vp]
+_lib.gdn_tree_commit_ragged.restype = _i
+_lib.gdn_tree_commit_verify_ragged.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 4 + \
+    [ctypes.POINTER(Cache)] + [_vp] * 11 + [ctypes.POINTER(Cache), _vp]
+_lib.gdn_tree_commit_verify_ragged.restype = _i
+_lib.gdn_tree_accept_ragged.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 8 + [_vp]
+_lib.gdn_tree_accept_ragged.restype = _i
 _lib.gdn_tree_strerror.argtypes = [_i]
 _lib.gdn_tree_strerror.restype = ctypes.c_char_p
 
@@ -259,6 +270,143 @@ def gdn_tree_accept(d: Dims, parent, draft, target, target_root, accepted, accep
     rc = _lib.gdn_tree_accept(ctypes.byref(d), *ptrs, _stream(stream))
     if rc:
         raise GdnError(rc, "gdn_tree_accept")
+
+
+# ---------------------------------------------------------------- ragged batches
+# Per-node arrays packed sequence after sequence: T rows in all (the leading
+# extent of every per-node tensor, taken from the first one), sequence b owning
+# rows offsets[b] .. offsets[b+1] - 1 (offsets: int32 [B + 1] on the device).
+
+
+def check_offsets(offsets, d: Dims, T: int) -> None:
+    """Host-side check (copies offsets to the host and so synchronises) that
+    the offsets describe B trees of at most N nodes inside T rows.  The library
+    itself only checks each sequence's own count on the device; an offsets
+    array that points past T rows is the caller's error."""
+    o = offsets.cpu().tolist() if hasattr(offsets, "cpu") else list(offsets)
+    if len(o) != d.batch + 1 or o[0] != 0:
+        raise ValueError("offsets: expected B + 1 entries starting at 0")
+    if any(b < a or b - a > d.n_nodes for a, b in zip(o, o[1:])):
+        raise ValueError("offsets: non-decreasing, at most n_nodes rows per sequence")
+    if o[-1] > T:
+        raise ValueError(f"offsets: {o[-1]} rows, arrays hold {T}")
+
+
+def _rows(x, name):
+    if isinstance(x, int) or x is None:
+        raise TypeError(f"{name}: ragged calls take tensors (their leading extent is T)")
+    return int(x.shape[0])
+
+
+def gdn_tree_verify_ragged(d: Dims, offsets, S0, q, k, v, beta, g, parent, o, cache,
+                           stream=None) -> None:
+    """Enqueue verification of a batch of trees of different sizes (see
+    gdn_tree.h, ragged batches)."""
+    torch = _torch()
+    B, Hk, Hv, dk, dv = d.batch, d.h_k, d.h_v, d.d_k, d.d_v
+    T = _rows(q, "q")
+    io = _io_dtype(d)
+    if isinstance(cache, TreeCache):
+        _check_cache(cache, d)
+    args = [
+        _ptr(offsets, (B + 1,), torch.int32, "offsets"),
+        _ptr(S0, (B, Hv, dv, dk), torch.float32, "S0"),
+        _ptr(q, (T, Hk, dk), io, "q"),
+        _ptr(k, (T, Hk, dk), io, "k"),
+        _ptr(v, (T, Hv, dv), io, "v"),
+        _ptr(beta, (T, Hv), torch.float32, "beta"),
+        _ptr(g, (T, Hv), torch.float32, "g"),
+        _ptr(parent, (T,), torch.int32, "parent"),
+        _ptr(o, (T, Hv, dv), io, "o"),
+    ]
+    rc = _lib.gdn_tree_verify_ragged(ctypes.byref(d), *args, ctypes.byref(_cache_struct(cache)),
+                                     _stream(stream))
+    if rc:
+        raise GdnError(rc, "gdn_tree_verify_ragged")
+
+
+def gdn_tree_commit_ragged(d: Dims, offsets, S_in, S_out, k, cache, accepted, path, path_len,
+                           stream=None) -> None:
+    """Enqueue the commit of each sequence's accepted node, ragged layout."""
+    torch = _torch()
+    B, Hk, Hv, dk, dv = d.batch, d.h_k, d.h_v, d.d_k, d.d_v
+    T = _rows(k, "k")
+    if isinstance(cache, TreeCache):
+        _check_cache(cache, d)
+    args = [
+        _ptr(offsets, (B + 1,), torch.int32, "offsets"),
+        _ptr(S_in, (B, Hv, dv, dk), torch.float32, "S_in"),
+        _ptr(S_out, (B, Hv, dv, dk), torch.float32, "S_out"),
+        _ptr(k, (T, Hk, dk), _io_dtype(d), "k"),
+    ]
+    tail = [
+        _ptr(accepted, (B,), torch.int32, "accepted"),
+        _ptr(path, (T,), torch.int32, "path"),
+        _ptr(path_len, (B,), torch.int32, "path_len"),
+    ]
+    rc = _lib.gdn_tree_commit_ragged(ctypes.byref(d), *args, ctypes.byref(_cache_struct(cache)),
+                                     *tail, _stream(stream))
+    if rc:
+        raise GdnError(rc, "gdn_tree_commit_ragged")
+
+
+def gdn_tree_commit_verify_ragged(d: Dims, offsets_prev, S_prev, S_new, k_prev, cache_prev,
+                                  accepted_prev, path_prev, path_len_prev, offsets, q, k, v, beta,
+                                  g, parent, o, cache, stream=None) -> None:
+    """Enqueue the previous tree's commit and the new tree's verification as one
+    step, ragged layout (each tree its own offsets)."""
+    torch = _torch()
+    B, Hk, Hv, dk, dv = d.batch, d.h_k, d.h_v, d.d_k, d.d_v
+    Tp, T = _rows(k_prev, "k_prev"), _rows(q, "q")
+    io = _io_dtype(d)
+    for c in (cache_prev, cache):
+        if isinstance(c, TreeCache):
+            _check_cache(c, d)
+    head = [
+        _ptr(offsets_prev, (B + 1,), torch.int32, "offsets_prev"),
+        _ptr(S_prev, (B, Hv, dv, dk), torch.float32, "S_prev"),
+        _ptr(S_new, (B, Hv, dv, dk), torch.float32, "S_new"),
+        _ptr(k_prev, (Tp, Hk, dk), io, "k_prev"),
+    ]
+    mid = [
+        _ptr(accepted_prev, (B,), torch.int32, "accepted_prev"),
+        _ptr(path_prev, (Tp,), torch.int32, "path_prev"),
+        _ptr(path_len_prev, (B,), torch.int32, "path_len_prev"),
+        _ptr(offsets, (B + 1,), torch.int32, "offsets"),
+        _ptr(q, (T, Hk, dk), io, "q"),
+        _ptr(k, (T, Hk, dk), io, "k"),
+        _ptr(v, (T, Hv, dv), io, "v"),
+        _ptr(beta, (T, Hv), torch.float32, "beta"),
+        _ptr(g, (T, Hv), torch.float32, "g"),
+        _ptr(parent, (T,), torch.int32, "parent"),
+        _ptr(o, (T, Hv, dv), io, "o"),
+    ]
+    rc = _lib.gdn_tree_commit_verify_ragged(ctypes.byref(d), *head,
+                                            ctypes.byref(_cache_struct(cache_prev)), *mid,
+                                            ctypes.byref(_cache_struct(cache)), _stream(stream))
+    if rc:
+        raise GdnError(rc, "gdn_tree_commit_verify_ragged")
+
+
+def gdn_tree_accept_ragged(d: Dims, offsets, parent, draft, target, target_root, accepted,
+                           accept_len, next_token, stream=None) -> None:
+    """Enqueue the greedy acceptance walk, ragged layout."""
+    torch = _torch()
+    B = d.batch
+    T = _rows(parent, "parent")
+    ptrs = [
+        _ptr(offsets, (B + 1,), torch.int32, "offsets"),
+        _ptr(parent, (T,), torch.int32, "parent"),
+        _ptr(draft, (T,), torch.int32, "draft"),
+        _ptr(target, (T,), torch.int32, "target"),
+        _ptr(target_root, (B,), torch.int32, "target_root"),
+        _ptr(accepted, (B,), torch.int32, "accepted"),
+        _ptr(accept_len, (B,), torch.int32, "accept_len"),
+        _ptr(next_token, (B,), torch.int32, "next_token"),
+    ]
+    rc = _lib.gdn_tree_accept_ragged(ctypes.byref(d), *ptrs, _stream(stream))
+    if rc:
+        raise GdnError(rc, "gdn_tree_accept_ragged")
 
 
 def _check_cache(c: TreeCache, d: Dims):

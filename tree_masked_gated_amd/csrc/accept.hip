@@ -34,10 +34,12 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
     __shared__ int32_t s_cnt[kMaxNodes];
     __shared__ int32_t s_ok[kMaxNodes];
     __shared__ int s_bad, s_best;
-    const int b = blockIdx.x, tid = threadIdx.x, N = a.N;
-    const int32_t* par = a.parent + (size_t)b * N;
-    const int32_t* dr = a.draft + (size_t)b * N;
-    const int32_t* tg = a.target + (size_t)b * N;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const SeqRows rows = seq_rows(a.offsets, b, a.N);
+    const int N = max(rows.n, 0);                   // this tree's nodes
+    const int32_t* par = a.parent + rows.row0;
+    const int32_t* dr = a.draft + rows.row0;
+    const int32_t* tg = a.target + rows.row0;
     const int root = a.target_root[b];
     if (tid == 0) {
         s_bad = 0;
@@ -47,10 +49,9 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
 #pragma unroll
     for (int k = 0; k < kAcceptPer; ++k) {
         const int i = tid + kAcceptThreads * k;
-        const int ic = min(i, N - 1);
-        p[k] = par[ic];
-        d[k] = dr[ic];
-        if (i < N) s_tg[i] = tg[ic];
+        p[k] = i < N ? par[i] : -1;
+        d[k] = i < N ? dr[i] : 0;
+        if (i < N) s_tg[i] = tg[i];
         s_first[i] = 0x7fffffff;
     }
     if (tid == 0) s_first[kMaxNodes] = 0x7fffffff;
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
         const int i = tid + kAcceptThreads * k;
         bad |= i < N && (p[k] < -1 || p[k] >= i);
     }
-    if (bad) s_bad = 1;
+    if (bad || rows.n < 0) s_bad = 1;
     __syncthreads();
     const bool invalid = s_bad != 0;
     if (!invalid) {

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs a) {
     const int tid = threadIdx.x;
 
     const int acc = a.accepted[b];
-    const bool valid = a.status[b] == 0 && acc >= -1 && acc < N;
+    const SeqRows rows = seq_rows(a.offsets, b, N);
+    const bool valid = a.status[b] == 0 && rows.n >= 0 && acc >= -1 && acc < rows.n;
     const uint32_t* row = a.anc_mask + ((size_t)b * N + (acc < 0 ? 0 : acc)) * W;
     int plen = -1;
     if (valid) plen = acc < 0 ? 0 : row_popc(row, W) + 1;
@@ -60,8 +61,8 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs a) {
     }
     __syncthreads();
     if (h == 0 && blockIdx.y == 0) {
-        int32_t* pb = a.path + (size_t)b * N;
-        for (int m = tid; m < N; m += kThreads) pb[m] = m < plen ? s_idx[m] : -1;
+        int32_t* pb = a.path + rows.row0;
+        for (int m = tid; m < rows.n; m += kThreads) pb[m] = m < plen ? s_idx[m] : -1;
         if (tid == 0) a.path_len[b] = plen;
     }
 
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs a) {
         for (int x = tid; x < pn * dk; x += kThreads) {
             const int m = x / dk, c = x % dk;
             const int j = s_idx[p0 + m];
-            s_k[m * dk + c] = ld_io<IO>(a.k, (((size_t)b * N + j) * a.Hk + hk) * dk + c);
+            s_k[m * dk + c] = ld_io<IO>(a.k, ((rows.row0 + j) * a.Hk + hk) * dk + c);
         }
         for (int x = tid; x < pn * nrows; x += kThreads) {
             const int m = x / nrows, r = x % nrows;
@@ -147,7 +148,8 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_d128(CommitArgs a) {
 #pragma unroll
     for (int n = 0; n < 16; ++n) st[n] = Sin[(r0 + 8 * n) * (kFastD / 4) + (c4 >> 2)];
 
-    const bool valid = status == 0 && acc >= -1 && acc < N;
+    const SeqRows rows = seq_rows(a.offsets, b, N);
+    const bool valid = status == 0 && rows.n >= 0 && acc >= -1 && acc < rows.n;
     const uint32_t* row = a.anc_mask + ((size_t)b * N + (acc < 0 ? 0 : acc)) * W;
     int plen = -1;
     if (valid) plen = acc < 0 ? 0 : row_popc(row, W) + 1;
@@ -165,8 +167,8 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_d128(CommitArgs a) {
     }
     __syncthreads();
     if (h == 0) {
-        int32_t* pb = a.path + (size_t)b * N;
-        for (int m = tid; m < N; m += kThreads) pb[m] = m < plen ? s_idx[m] : -1;
+        int32_t* pb = a.path + rows.row0;
+        for (int m = tid; m < rows.n; m += kThreads) pb[m] = m < plen ? s_idx[m] : -1;
         if (tid == 0) a.path_len[b] = plen;
     }
     if (plen <= 0) {                       // nothing accepted (or invalid): S_out = S_in
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_d128(CommitArgs a) {
         for (int x = tid; x < pn * 32; x += kThreads) {
             const int m = x >> 5, c = (x & 31) * 4;
             const int j = s_idx[p0 + m];
-            const size_t kb = (((size_t)b * N + j) * a.Hk + hk) * kFastD + c;
+            const size_t kb = ((rows.row0 + j) * a.Hk + hk) * kFastD + c;
             *reinterpret_cast<float4*>(&s_k[m * kFastD + c]) =
                 make_float4(ld_io<IO>(a.k, kb), ld_io<IO>(a.k, kb + 1), ld_io<IO>(a.k, kb + 2),
                             ld_io<IO>(a.k, kb + 3));
@@ -261,7 +263,8 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
 #pragma unroll
     for (int tc = 0; tc < 8; ++tc) D[tc] = *reinterpret_cast<const f32x4*>(a.S_in + srow + 16 * tc);
 
-    const bool valid = status == 0 && acc_node >= -1 && acc_node < N;
+    const SeqRows rows = seq_rows(a.offsets, b, N);
+    const bool valid = status == 0 && rows.n >= 0 && acc_node >= -1 && acc_node < rows.n;
     const uint32_t* row = a.anc_mask + ((size_t)b * N + (acc_node < 0 ? 0 : acc_node)) * W;
     int plen = -1;
     if (valid) plen = acc_node < 0 ? 0 : row_popc(row, W) + 1;
@@ -279,8 +282,8 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
     }
     __syncthreads();
     if (h == 0 && half == 0) {
-        int32_t* pb = a.path + (size_t)b * N;
-        for (int m = tid; m < N; m += kThreads) pb[m] = m < plen ? s_idx[m] : -1;
+        int32_t* pb = a.path + rows.row0;
+        for (int m = tid; m < rows.n; m += kThreads) pb[m] = m < plen ? s_idx[m] : -1;
         if (tid == 0) a.path_len[b] = plen;
     }
     if (plen > 0) {
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
         auto load_chunk = [&](int p0) {
             const int pn = min(kMfmaChunk, plen - p0);
             const int j = s_idx[p0 + min(m, pn - 1)];
-            const uint16_t* kr = K + (((size_t)b * N + j) * a.Hk + hk) * kFastD + kseg;
+            const uint16_t* kr = K + ((rows.row0 + j) * a.Hk + hk) * kFastD + kseg;
             k0 = *reinterpret_cast<const u32x4*>(kr);
             k1 = *reinterpret_cast<const u32x4*>(kr + 8);
             const float* ur = U + (size_t)j * kFastD + r0 + useg;

@@ -29,6 +29,7 @@ struct VerifyArgs {
     float* u;
     float* log_gamma;
     int32_t* status;
+    const int32_t* offsets;   // ragged layout: [B + 1] first rows; nullptr = dense
 };
 
 struct CommitArgs {
@@ -43,7 +44,29 @@ struct CommitArgs {
     const int32_t* accepted;
     int32_t* path;
     int32_t* path_len;
+    const int32_t* offsets;   // ragged layout of k and path; nullptr = dense
 };
+
+// Rows of sequence b in the per-node arrays (q, k, v, o, beta, g, parent, the
+// acceptance tokens and a commit's path).  Dense layout (offsets = nullptr):
+// rows b N .. b N + N - 1.  Ragged layout: rows offsets[b] .. offsets[b+1] - 1,
+// N being the largest tree; n = -1 marks a sequence whose offsets are unusable
+// (a negative first row, or a node count outside [0, N]), and then nothing of
+// it is read.  b must be uniform over the wave: the two offsets are read
+// through the scalar cache, so waiting for them does not wait for the wave's
+// vector loads.
+struct SeqRows {
+    int64_t row0;
+    int n;
+};
+__device__ __forceinline__ SeqRows seq_rows(const int32_t* offsets, int b, int N) {
+    if (offsets == nullptr) return SeqRows{(int64_t)b * N, N};
+    typedef __attribute__((address_space(4))) const int32_t cint32;
+    const cint32* p = (const cint32*)offsets;
+    const int64_t o0 = p[b], n = (int64_t)p[b + 1] - o0;
+    if (o0 < 0 || n < 0 || n > N) return SeqRows{0, -1};
+    return SeqRows{o0, (int)n};
+}
 
 // ------------------------------------------------------------- element codecs
 

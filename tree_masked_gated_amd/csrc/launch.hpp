@@ -35,6 +35,7 @@ struct AcceptArgs {
     int32_t* accepted;
     int32_t* accept_len;
     int32_t* next_token;
+    const int32_t* offsets;   // ragged layout: [B + 1] first rows; nullptr = dense
 };
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
 

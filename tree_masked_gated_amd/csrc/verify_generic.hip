@@ -69,26 +69,30 @@ __global__ __launch_bounds__(kThreads) void verify_generic_kernel(VerifyArgs a) 
     const int hk = h / (a.Hv / a.Hk);
     const bool writer = (h == 0);   // one workgroup per tree publishes the tree
 
-    const int status = tree_build_lds(a.parent + (size_t)b * N, N, W, mask, jump, &s_flag);
+    // this tree's rows in the node arrays; the cache keeps N rows per tree
+    const SeqRows rows = seq_rows(a.offsets, b, N);
+    const int n = max(rows.n, 0);
+    int status = tree_build_lds(a.parent + rows.row0, n, W, mask, jump, &s_flag);
+    if (rows.n < 0) status = -1;
 
     // per-node base offsets in the documented layouts
-    auto qk_off = [&](int i) { return (((size_t)b * N + i) * a.Hk + hk) * dk; };
-    auto v_off = [&](int i) { return (((size_t)b * N + i) * a.Hv + h) * dv; };
-    auto bg_off = [&](int i) { return ((size_t)b * N + i) * a.Hv + h; };
+    auto qk_off = [&](int i) { return ((rows.row0 + i) * a.Hk + hk) * dk; };
+    auto v_off = [&](int i) { return ((rows.row0 + i) * a.Hv + h) * dv; };
+    auto bg_off = [&](int i) { return (rows.row0 + i) * a.Hv + h; };
     float* U = a.u + ((size_t)b * a.Hv + h) * (size_t)N * dv;
     const float* S0 = a.S0 + ((size_t)b * a.Hv + h) * (size_t)dv * dk;
 
     if (writer) {
         uint32_t* gm = a.anc_mask + (size_t)b * N * W;
-        for (int x = tid; x < N * W; x += kThreads) gm[x] = mask[x];
+        for (int x = tid; x < N * W; x += kThreads) gm[x] = x < n * W ? mask[x] : 0u;
         for (int i = tid; i < N; i += kThreads)
-            a.depth[(size_t)b * N + i] = status ? -1 : row_popc(mask + i * W, W);
+            a.depth[(size_t)b * N + i] = (status || i >= n) ? -1 : row_popc(mask + i * W, W);
         if (tid == 0) a.status[b] = status;
     }
     if (status) {
         const float qnan = __uint_as_float(0x7fc00000u);
         for (int x = tid; x < N * dv; x += kThreads) {
-            st_io<IO>(a.o, v_off(x / dv) + x % dv, qnan);
+            if (x < n * dv) st_io<IO>(a.o, v_off(x / dv) + x % dv, qnan);
             U[x] = qnan;
         }
         for (int i = tid; i < N; i += kThreads)
@@ -97,10 +101,10 @@ __global__ __launch_bounds__(kThreads) void verify_generic_kernel(VerifyArgs a) 
     }
 
     // ln g per node, then G_i = sum of ln g over ancestors (ascending) + own.
-    for (int i = tid; i < N; i += kThreads) lng[i] = logf(a.g[bg_off(i)]);
+    for (int i = tid; i < n; i += kThreads) lng[i] = logf(a.g[bg_off(i)]);
     if (tid == 0) s_maxdep = 0;
     __syncthreads();
-    for (int i = tid; i < N; i += kThreads) {
+    for (int i = tid; i < n; i += kThreads) {
         const uint32_t* row = mask + i * W;
         float s = 0.f;
         int d = 0;
@@ -125,12 +129,12 @@ __global__ __launch_bounds__(kThreads) void verify_generic_kernel(VerifyArgs a) 
     // own inputs and its ancestors' finished rows.
     for (int x = tid; x <= maxdep + 1; x += kThreads) lvl[x] = 0;
     __syncthreads();
-    for (int i = tid; i < N; i += kThreads) atomicAdd(&lvl[dep[i] + 1], 1);
+    for (int i = tid; i < n; i += kThreads) atomicAdd(&lvl[dep[i] + 1], 1);
     __syncthreads();
     block_inclusive_scan(lvl, maxdep + 2, s_part);       // lvl[l] = first slot of level l
     for (int x = tid; x <= maxdep; x += kThreads) jump[x] = lvl[x];
     __syncthreads();
-    for (int i = tid; i < N; i += kThreads) order[atomicAdd(&jump[dep[i]], 1)] = i;
+    for (int i = tid; i < n; i += kThreads) order[atomicAdd(&jump[dep[i]], 1)] = i;
     __syncthreads();
 
     // Two sweeps over the levels: pass 0 solves (I + X) U = R, pass 1 forms O.

@@ -43,11 +43,13 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
     __shared__ int32_t s_jump[kPrepMaxN];
     __shared__ int s_flag;
     const int b = blockIdx.x, N = a.N, W = (N + 31) / 32, tid = threadIdx.x;
+    const SeqRows rows = seq_rows(a.offsets, b, N);     // the cache keeps N rows per tree
+    const int n = max(rows.n, 0);
     const int i = tid >> 1, hh = tid & 1;               // node, half row (words 8 hh .. +7)
     if (tid == 0) s_flag = 0x7fffffff;
     __syncthreads();
-    if (hh == 0 && i < N) {
-        const int p = a.parent[(size_t)b * N + i];
+    if (hh == 0 && i < n) {
+        const int p = a.parent[rows.row0 + i];
         s_jump[i] = p;
         if (p < -1 || p >= i) atomicMin(&s_flag, i);
     }
@@ -60,10 +62,10 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
         row[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
     }
     __syncthreads();
-    const int status = s_flag == 0x7fffffff ? 0 : s_flag + 1;
+    const int status = rows.n < 0 ? -1 : s_flag == 0x7fffffff ? 0 : s_flag + 1;
     if (status == 0) {
         for (;;) {
-            const int j = i < N ? s_jump[i] : -1;
+            const int j = i < n ? s_jump[i] : -1;
             uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
             int nj = -1;
             if (j >= 0) {
@@ -88,10 +90,10 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
     uint32_t* gm = a.anc_mask + (size_t)b * N * W;
     for (int x = tid; x < N * W; x += kPrepThreads) {
         const int r = x / W, w = x - r * W;
-        gm[x] = status ? 0u : s_mask[r * WP + w] & ~((r >> 5) == w ? 1u << (r & 31) : 0u);
+        gm[x] = (status || r >= n) ? 0u : s_mask[r * WP + w] & ~((r >> 5) == w ? 1u << (r & 31) : 0u);
     }
     for (int r = tid; r < N; r += kPrepThreads)
-        a.depth[(size_t)b * N + r] = status ? -1 : row_popc(s_mask + r * WP, W) - 1;
+        a.depth[(size_t)b * N + r] = (status || r >= n) ? -1 : row_popc(s_mask + r * WP, W) - 1;
     if (tid == 0) a.status[b] = status;
 }
 
@@ -156,7 +158,6 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
 
     const int N = a.N, Hv = a.Hv, Hk = a.Hk, G = Hv / Hk;
     const int W = (N + 31) / 32;
-    const int nblk = (N + 15) / 16;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool solver = wave < NS;
@@ -164,8 +165,12 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     const int slice = item % csplit, bh = item / csplit;
     const int h = bh % Hv, b = bh / Hv, hk = h / G;
     const int cbase = slice * (16 * NCG);               // the workgroup's first value column
+    // this tree's rows in the node arrays (n nodes); the cache keeps N rows per tree
+    const SeqRows rows = seq_rows(a.offsets, b, N);
+    const int n = max(rows.n, 0);
+    const int nblk = (n + 15) / 16;
     const size_t vo_row = (size_t)Hv * kD;
-    const size_t vo_base = ((size_t)b * N * Hv + h) * kD;
+    const size_t vo_base = (rows.row0 * Hv + h) * kD;
     uint16_t* O = static_cast<uint16_t*>(a.o);
     float* Ug = a.u + ((size_t)b * Hv + h) * (size_t)N * kD;
 
@@ -175,24 +180,25 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         if (solver)
             for (int x = lane; x < N * 32; x += 64) {
                 const int i = x / 32, c = cbase + 32 * wave + x % 32;
-                O[vo_base + (size_t)i * vo_row + c] = 0x7fc0;
+                if (i < n) O[vo_base + (size_t)i * vo_row + c] = 0x7fc0;
                 Ug[(size_t)i * kD + c] = qnan;
             }
         if (slice == 0)
             for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = qnan;
         return;
     }
+    if (n == 0) return;                                 // an empty tree: nothing to verify
 
-    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
-    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + ((size_t)b * N * Hk + hk) * kD;
+    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + (rows.row0 * Hk + hk) * kD;
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + (rows.row0 * Hk + hk) * kD;
     const size_t kq_row = (size_t)Hk * kD;
     // ---- path log-gates G (synchronous pointer doubling), beta, occupancy ----
     const uint32_t* gmask = a.anc_mask + (size_t)b * N * W;
     for (int i = tid; i < NP; i += NT) {
-        const bool v = i < N;
-        s_jump[i] = v ? a.parent[(size_t)b * N + i] : -1;
-        s_lg[i] = v ? logf(a.g[((size_t)b * N + i) * Hv + h]) : 0.f;
-        s_beta[i] = v ? a.beta[((size_t)b * N + i) * Hv + h] : 0.f;
+        const bool v = i < n;
+        s_jump[i] = v ? a.parent[rows.row0 + i] : -1;
+        s_lg[i] = v ? logf(a.g[(rows.row0 + i) * Hv + h]) : 0.f;
+        s_beta[i] = v ? a.beta[(rows.row0 + i) * Hv + h] : 0.f;
     }
     for (int t = tid; t < NB; t += NT) s_occ[t] = 0ull;
     __syncthreads();
@@ -215,13 +221,13 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     // k rows of the cached blocks into registers (1 KB unit wave + 8 r: block
     // u / 4, chunk u % 4), written to LDS once the tree's gates are summed, so
     // the loads overlap that work; issued after the loads waited on above
-    // (loads retire in order).  Rows clamped to N - 1.
+    // (loads retire in order).  Rows clamped to n - 1.
     constexpr int KCR = KC * 4 / (NT / 64);             // units per wave
     u32x4 kcr[KCR];
 #pragma unroll
     for (int r = 0; r < KCR; ++r) {
         const int u = wave + (NT / 64) * r;
-        const int row = min(16 * (u >> 2) + ln, N - 1);
+        const int row = min(16 * (u >> 2) + ln, n - 1);
         kcr[r] = *reinterpret_cast<const u32x4*>(Kb + (size_t)row * kq_row + 32 * (u & 3) + 8 * lq);
     }
 
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         if (!__syncthreads_or(act)) break;
     }
     if (slice == 0)
-        for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
+        for (int i = tid; i < n; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
 
     // tile lists (occupancy complete): the diagonal, then the occupied blocks
     // in descending order, so the blocks past the LDS k cache come first and
@@ -294,10 +300,10 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         }
         // k / q fragment of node block blk, column chunk cs, from global memory
         // (L2): the block's base is uniform, the lane's row / column a 32-bit
-        // offset (rows clamped to N - 1)
+        // offset (rows clamped to n - 1)
         const uint32_t lane_col = 16u * lq;                 // bytes: 8 bf16 per lane group
         auto frag = [&](const uint16_t* base, int blk, int cs) __attribute__((always_inline)) {
-            const uint32_t row = (uint32_t)min(16 * blk + ln, N - 1);
+            const uint32_t row = (uint32_t)min(16 * blk + ln, n - 1);
             const uint32_t off = row * (uint32_t)(kq_row * 2) + lane_col + 64u * cs;
             return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                   reinterpret_cast<const char*>(base) + off));
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         auto tile_store = [&](int t, int s, f32x4 A, f32x4 C, uint32_t mword) __attribute__((always_inline)) {
             const int par = t & 1;
             const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
-            const uint32_t bits = i < N ? (mword >> (j0 & 31)) & 15u : 0u;
+            const uint32_t bits = i < n ? (mword >> (j0 & 31)) & 15u : 0u;
             const float lgi = s_lg[i], bei = s_beta[i];
             const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[j0]);
             const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bool anc = (bits >> e) & 1u;
-                const bool self = (j0 + e == i) && i < N;
+                const bool self = (j0 + e == i) && i < n;
                 const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
                 xv[e] = anc ? bei * d * A[e] : 0.f;
                 yv[e] = bf16_rne(d * C[e]);
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                     const int m = gw + i * NG;
                     if (m < ntile) tile_store(tr, tile_col(tr, occ, m), Ap[i], Cp[i], wc[i]);
                 }
-                const int ii = min(16 * tr + ln, N - 1);
+                const int ii = min(16 * tr + ln, n - 1);
                 for (int m = gw + TPW * NG; m < ntile; m += NG) {
                     const int sc = tile_col(tr, occ, m);
                     bf16x8 k0[4];
@@ -556,7 +562,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                         up[g][p] = stack_pair(ut, zero4);
                 }
             }
-            if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + c0 + 16 * g + 4 * lq) = UT;
+            if (node < n) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + c0 + 16 * g + 4 * lq) = UT;
         }
         // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T over occupied tiles
         f32x4 Oc[CG], Oc2[CG];
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         }
 #pragma unroll
         for (int g = 0; g < CG; ++g) Oc[g] += Oc2[g];
-        if (node < N) {
+        if (node < n) {
             const float egn = __expf(s_lg[node]);
 #pragma unroll
             for (int g = 0; g < CG; ++g) {
@@ -601,7 +607,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     auto load_v = [&](int t, uint2 (&v)[CG]) __attribute__((always_inline)) {
 #pragma unroll
         for (int g = 0; g < CG; ++g)
-            v[g] = *reinterpret_cast<const uint2*>(Vp + (size_t)min(16 * t + ln, N - 1) * vo_row + 16 * g);
+            v[g] = *reinterpret_cast<const uint2*>(Vp + (size_t)min(16 * t + ln, n - 1) * vo_row + 16 * g);
     };
     uint2 va[CG], vb[CG];
     load_v(0, va);

@@ -70,7 +70,11 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // FUSED: the kernel first commits the previous tree's accepted node (args c;
 // its state is this launch's S0, a.S0 = c.S_in) into the S0 rows each wave
 // holds, writes them to c.S_out and verifies with them (see the commit prologue).
-template <int NB, int HPW, bool FUSED>
+// RAGGED: per-node arrays in the ragged layout (a.offsets, and c.offsets for
+// the previous tree); a tree of n < N nodes runs only its ceil(n / 16) blocks.
+// Loads never leave a tree's rows: rows past n re-read row n - 1, and an empty
+// tree's loads read the first line of S0 instead.
+template <int NB, int HPW, bool FUSED, bool RAGGED>
 __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a, CommitArgs c, int nitems) {
     constexpr int WPH = 4;                      // waves per value head
     constexpr int CG = 2;                       // 16-column groups per wave
@@ -99,7 +103,6 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 
     const int N = a.N, Hv = a.Hv, Hk = a.Hk, G = Hv / Hk, GG = G / HPW;
     const int W = (N + 31) / 32;
-    const int nblk = (N + 15) / 16;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hp = wave / WPH, wc = wave % WPH;       // this wave: head h0+hp, cols 32wc..
     const int col0 = 32 * wc;
@@ -126,6 +129,15 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         hk = bh % Hk;
         b = bh / Hk;
     };
+    // rows of sequence b in the node arrays (dense: b N .., N nodes)
+    auto tree_rows = [&](const int32_t* offsets, int b) {
+        if constexpr (RAGGED) return seq_rows(offsets, b, N);
+        else return SeqRows{(int64_t)b * N, N};
+    };
+    // the current item's tree: node count (0 for unusable offsets) and whether
+    // its offsets are unusable
+    int tn = N;
+    bool tbad = false;
 
     // ---- prefetch helpers (registers / LDS written by loads in flight) ----
     // Per item, wave 0 needs parent and g of nodes lane + 64k (k < NPL), and the
@@ -142,13 +154,16 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         int b, hk, hg;
         decode(it, b, hk, hg);
         const int h0 = hk * G + hg * HPW;
-        const uint32_t* par = reinterpret_cast<const uint32_t*>(a.parent) + (size_t)b * N;
+        const SeqRows rw = tree_rows(a.offsets, b);
+        if (RAGGED && rw.n <= 0) real = false;
+        const uint32_t* par = reinterpret_cast<const uint32_t*>(a.parent) + rw.row0;
         const uint32_t* gg = reinterpret_cast<const uint32_t*>(wave == 0 ? a.g : a.beta) +
-                             (size_t)b * N * Hv + h0;
-        const int nb = real ? min(max(tid - 64, 0), N - 1) : 0;
+                             rw.row0 * Hv + h0;
+        if (RAGGED && !real) par = gg = reinterpret_cast<const uint32_t*>(a.S0);
+        const int nb = real ? min(max(tid - 64, 0), rw.n - 1) : 0;
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
-            const int i = real ? min(lane + 64 * k, N - 1) : 0;
+            const int i = real ? min(lane + 64 * k, rw.n - 1) : 0;
             sm[k] = par[i];
 #pragma unroll
             for (int p = 0; p < HPW; ++p)
@@ -157,20 +172,24 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     };
     // k and q rows of the item's tree into s_k / s_q: each wave instruction
     // fills 1 KB (4 rows) of LDS, lane l landing on row r0 + l/16, physical chunk
-    // l%16, which holds logical chunk (l%16) ^ (row & 15).  Rows past N copy
-    // row N-1 (finite values; masks and beta = 0 keep them out of every result).
+    // l%16, which holds logical chunk (l%16) ^ (row & 15).  Rows past the tree's
+    // n copy row n - 1 (finite values; masks and beta = 0 keep them out of every
+    // result).
     // (real = false: a placeholder after the last item, every lane reading one line)
     auto kq_dma = [&](int it, bool real) {
         int b, hk, hg;
         decode(it, b, hk, hg);
-        const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + ((size_t)b * N * Hk + hk) * kD;
-        const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + ((size_t)b * N * Hk + hk) * kD;
+        const SeqRows rw = tree_rows(a.offsets, b);
+        if (RAGGED && rw.n <= 0) real = false;
+        const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + (rw.row0 * Hk + hk) * kD;
+        const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + (rw.row0 * Hk + hk) * kD;
+        if (RAGGED && !real) Kb = reinterpret_cast<const uint16_t*>(a.S0);
 #pragma unroll
         for (int kk = 0; kk < KQ_INS / NW; ++kk) {      // compile-time count: a loop of
             const int ins = wave + kk * NW;            // loads would get a full wait ahead
             const int mat = ins / (NP / 4), r0 = (ins % (NP / 4)) * 4;
             const int row = r0 + (lane >> 4), pc = lane & 15;
-            const int srow = row < N ? row : N - 1;
+            const int srow = row < rw.n ? row : rw.n - 1;
             const uint16_t* src = real ? (mat ? Qb : Kb) + (size_t)srow * Hk * kD + ((pc ^ (row & 15)) << 3) : Kb;
             uint16_t* dst = (mat ? s_q : s_k) + r0 * kD;
             __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
@@ -213,16 +232,17 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 #pragma unroll
         for (int k = NPL - 1; k >= 0; --k) {                // lowest bad node wins
             const int i = lane + 64 * k, pi = (int)sm[k];
-            const uint64_t bad = __ballot(i < N && (pi < -1 || pi >= i));
+            const uint64_t bad = __ballot(i < tn && (pi < -1 || pi >= i));
             if (bad) status = 64 * k + __ffsll((unsigned long long)bad);
         }
+        if (tbad) status = -1;
         int nx[NPL];
         uint32_t m[NPL][MW];
         float gv[NPL][HPW];
 #pragma unroll
         for (int k = 0; k < NPL; ++k) {
             const int i = lane + 64 * k;
-            const bool valid = i < N && status == 0;
+            const bool valid = i < tn && status == 0;
             nx[k] = valid ? (int)sm[k] : -1;
 #pragma unroll
             for (int w = 0; w < MW; ++w) m[k][w] = (valid && (i >> 5) == w) ? 1u << (i & 31) : 0u;
@@ -294,7 +314,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
                     if (w < W) gm[(size_t)i * W + w] = x;
                     cnt += __popc(x);
                 }
-                a.depth[(size_t)b * N + i] = status ? -1 : cnt;
+                a.depth[(size_t)b * N + i] = (status || i >= tn) ? -1 : cnt;
             }
             if (status == 0) {
 #pragma unroll
@@ -334,6 +354,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     constexpr int UR = FUSED ? (HPW * PC * 32 + NT - 1) / NT : 0;   // u loads per thread
     int cm_acc_v = 0, cm_st_v = 0;              // loads in flight
     int cm_acc = 0, cm_st = 0;                  // the same, uniform
+    SeqRows prv{0, N};                          // this item: the previous tree's rows
     uint32_t cm_row_v[MW];
 #pragma unroll
     for (int w = 0; w < MW; ++w) cm_row_v[w] = 0u;
@@ -369,7 +390,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         for (int w = 0; w < MW; ++w) cm_row_v[w] = prow[min(w, W - 1)];
     };
     auto commit_path = [&]() {
-        const bool valid = cm_st == 0 && cm_acc >= -1 && cm_acc < N;
+        const bool valid = cm_st == 0 && cm_acc >= -1 && cm_acc < prv.n;
         int pc = 0;
 #pragma unroll
         for (int w = 0; w < MW; ++w) {
@@ -401,14 +422,18 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         return s < plen - 1 ? min(t, N - 1) : last;
     };
     auto commit_issue = [&](int b, int hk, int h0, int p0) {
-        const uint16_t* Kp = static_cast<const uint16_t*>(c.k) + (size_t)b * N * Hk * kD + hk * kD;
+        const uint16_t* Kp = static_cast<const uint16_t*>(c.k) + prv.row0 * Hk * kD + hk * kD;
+        // (path nodes lie below the accepted node; padding slots re-read its
+        // row, or, with nothing in the previous tree, the first line of S_in)
+        const int klast = RAGGED ? max(prv.n - 1, 0) : N - 1;
+        if (RAGGED && prv.n <= 0) Kp = reinterpret_cast<const uint16_t*>(c.S_in);
         const float* Up = c.u + ((size_t)b * Hv + h0) * (size_t)N * kD;
         const float* lgprev = c.log_gamma + ((size_t)b * Hv + h0) * N;
 #pragma unroll
         for (int r = 0; r < KR; ++r) {
             const int x = min(tid + r * NT, PC * 16 - 1);
             const int m = x % PC, ck = x / PC;
-            const int j = slot_node(p0 + m);
+            const int j = min(slot_node(p0 + m), klast);
             st_k[r] = *reinterpret_cast<const u32x4*>(Kp + (size_t)j * Hk * kD + 8 * ck);
         }
 #pragma unroll
@@ -458,7 +483,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
     };
     auto commit_apply = [&](int b, int hk, int hg, int h0, int h) {
         if (hk == 0 && hg == 0) {
-            for (int m = tid; m < N; m += NT) c.path[(size_t)b * N + m] = m < plen ? slot_node(m) : -1;
+            for (int m = tid; m < prv.n; m += NT) c.path[prv.row0 + m] = m < plen ? slot_node(m) : -1;
             if (tid == 0) c.path_len[b] = plen;
         }
         if (plen > 0) {
@@ -543,7 +568,12 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         decode(item, b, hk, hg);
         const int h0 = hk * G + hg * HPW;
         const int h = h0 + hp;
-        const size_t vo_base = ((size_t)b * N * Hv + h) * kD;     // node 0 of head h
+        const SeqRows rw = tree_rows(a.offsets, b);
+        tn = max(rw.n, 0);
+        tbad = rw.n < 0;
+        if constexpr (FUSED) prv = tree_rows(c.offsets, b);
+        const int tblk = (tn + 15) / 16;                      // this tree's node blocks
+        const size_t vo_base = (rw.row0 * Hv + h) * kD;       // node 0 of head h
         lds_barrier();                                        // LDS of the last item is free
         if constexpr (FUSED) {                                // the previous tree's path rows
             commit_path();
@@ -557,7 +587,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
             const int i = tid - 64;
 #pragma unroll
             for (int p = 0; p < HPW; ++p)
-                s_beta[p][i] = i < N ? __uint_as_float(sm[NPL + p]) : 0.f;
+                s_beta[p][i] = i < tn ? __uint_as_float(sm[NPL + p]) : 0.f;
         }
         // S0 rows (registers) and the direct-to-LDS k / q rows were issued before
         // anything still in flight: one wait covers both, the barrier publishes
@@ -581,25 +611,28 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
                 sb[g][cs] = to_bf16x8(s0raw[g][cs][0], s0raw[g][cs][1]);
                 asm volatile("" : "+v"(sb[g][cs]));
             }
-        if (status) {                                 // invalid tree: NaN outputs, no solve
-            const float qnan = __uint_as_float(0x7fc00000u);
+        const bool solve = status == 0 && tn > 0;          // (an empty tree: nothing to do)
+        if (!solve) {
+            if (status) {                             // invalid tree: NaN outputs, no solve
+                const float qnan = __uint_as_float(0x7fc00000u);
 #pragma unroll
-            for (int p = 0; p < HPW; ++p) {
-                const size_t ob = ((size_t)b * N * Hv + h0 + p) * kD;
-                float* Up = a.u + ((size_t)b * Hv + h0 + p) * (size_t)N * kD;
-                for (int x = tid; x < N * kD; x += NT) {
-                    O[ob + (size_t)(x / kD) * vo_row + x % kD] = 0x7fc0;
-                    Up[x] = qnan;
+                for (int p = 0; p < HPW; ++p) {
+                    const size_t ob = (rw.row0 * Hv + h0 + p) * kD;
+                    float* Up = a.u + ((size_t)b * Hv + h0 + p) * (size_t)N * kD;
+                    for (int x = tid; x < N * kD; x += NT) {
+                        if (x < tn * kD) O[ob + (size_t)(x / kD) * vo_row + x % kD] = 0x7fc0;
+                        Up[x] = qnan;
+                    }
+                    for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h0 + p) * N + i] = qnan;
                 }
-                for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h0 + p) * N + i] = qnan;
             }
         } else {
             // this item's v rows, needed only in the solve (unconditional: rows
-            // past N re-read row N - 1, and beta = 0 there)
+            // past n re-read row n - 1, and beta = 0 there)
             const uint16_t* V = static_cast<const uint16_t*>(a.v);
 #pragma unroll
             for (int t = 0; t < NB; ++t) {
-                const int i = min(16 * t + ln, N - 1);
+                const int i = min(16 * t + ln, tn - 1);
                 vfr[t] = *reinterpret_cast<const u32x4*>(V + vo_base + (size_t)i * vo_row + col0 + 8 * lq);
             }
             // ---- 3. Gram tiles -> masked, decayed X / Y tiles per head ----------
@@ -624,7 +657,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
                 }
 #pragma unroll
                 for (int c = 0; c < MAXC; ++c) {
-                    if (p0 + c >= p1 || t >= nblk) break;      // uniform
+                    if (p0 + c >= p1 || t >= tblk) break;      // uniform
                     f32x4 A = z, C = z;
 #pragma unroll
                     for (int cs = 0; cs < 4; ++cs) {
@@ -648,7 +681,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
                         for (int cs = 0; cs < 4; ++cs) fs[cs] = lds_frag(s_k, min(s, NB - 1), cs, lane);
                     }
                     const int i = 16 * tc + ln, j0 = 16 * sc + 4 * lq;
-                    const uint32_t bits = i < N ? (s_mask[i * MW + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
+                    const uint32_t bits = i < tn ? (s_mask[i * MW + (j0 >> 5)] >> (j0 & 31)) & 15u : 0u;
 #pragma unroll
                     for (int p = 0; p < HPW; ++p) {
                         const float lgi = s_lg[p][i], bei = s_beta[p][i];
@@ -659,7 +692,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const bool anc = (bits >> e) & 1u;
-                            const bool self = (j0 + e == i) && i < N;
+                            const bool self = (j0 + e == i) && i < tn;
                             const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
                             xv[e] = anc ? bei * d * A[e] : 0.f;
                             yv[e] = bf16_rne(d * C[e]);
@@ -692,11 +725,11 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 #pragma unroll
             for (int g = 0; g < CG; ++g) load_s0(pf, g, more);
         }
-        if (!status) {
+        if (solve) {
             // ---- 4. diagonal blocks: (I + X_tt)^-1 in fp32 ----------------------
             for (int blk = tid >> 4; blk < HPW * NB; blk += NT / 16) {
                 const int p = blk / NB, t = blk % NB;
-                if (t < nblk) {
+                if (t < tblk) {
                     const float* xd = s_xd[p] + t * 256;
                     float y[16];
 #pragma unroll
@@ -740,7 +773,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
         const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
         const bool hi_half = lq >= 2;                          // lanes of the pair's second block
         bf16x8 up[CG][(NB + 1) / 2];
-        const int nsolve = status ? 0 : nblk;
+        const int nsolve = solve ? tblk : 0;
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
             // (not fused) the next item's S0 rows, one column group at a time,
@@ -801,7 +834,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
                                                                   __builtin_bit_cast(u32x4, stack_pair(zero4, ut)));
                 else
                     up[g][t / 2] = stack_pair(ut, zero4);
-                if (node < N) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 8 * lq + 4 * g) = UT;
+                if (node < tn) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + col0 + 8 * lq + 4 * g) = UT;
             }
             // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T, two blocks per product
             f32x4 Oc[CG];
@@ -814,7 +847,7 @@ __global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a
 #pragma unroll
                 for (int g = 0; g < CG; ++g) Oc[g] = mfma32(up[g][s / 2], yt, Oc[g]);
             }
-            if (node < N) {
+            if (node < tn) {
                 const float egn = __expf(lgp[node]);
                 u32x4 ov;
 #pragma unroll
@@ -844,15 +877,23 @@ bool verify_tiled_supported(const VerifyArgs& a, int io) {
     return io == GDN_BF16 && a.dk == kD && a.dv == kD && a.N <= 128;
 }
 
+template <bool FUSED, bool RAGGED>
+static const void* tiled_kernel(int N, int hpw) {
+    if (N <= 64)
+        return hpw == 2 ? (const void*)verify_tiled_kernel<4, 2, FUSED, RAGGED>
+                        : (const void*)verify_tiled_kernel<4, 1, FUSED, RAGGED>;
+    return hpw == 2 ? (const void*)verify_tiled_kernel<8, 2, FUSED, RAGGED>
+                    : (const void*)verify_tiled_kernel<8, 1, FUSED, RAGGED>;
+}
+
 template <bool FUSED>
 static hipError_t launch_tiled(const VerifyArgs& a, const CommitArgs& c, hipStream_t stream) {
     const int G = a.Hv / a.Hk;
     const int hpw = (G % 2 == 0) ? 2 : 1;
-    const void* fn;
-    if (a.N <= 64)
-        fn = hpw == 2 ? (const void*)verify_tiled_kernel<4, 2, FUSED> : (const void*)verify_tiled_kernel<4, 1, FUSED>;
-    else
-        fn = hpw == 2 ? (const void*)verify_tiled_kernel<8, 2, FUSED> : (const void*)verify_tiled_kernel<8, 1, FUSED>;
+    // ragged: the new tree's offsets, and (fused) the previous tree's as well
+    const bool ragged = a.offsets != nullptr;
+    if (FUSED && ragged != (c.offsets != nullptr)) return hipErrorInvalidValue;
+    const void* fn = ragged ? tiled_kernel<FUSED, true>(a.N, hpw) : tiled_kernel<FUSED, false>(a.N, hpw);
     int nitems = a.B * a.Hk * (G / hpw);
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);

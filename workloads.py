@@ -265,6 +265,26 @@ def unit_slice(s: Spec, lay: dict, parent: np.ndarray, accepted: np.ndarray,
     }
 
 
+# ---------------------------------------------------------------- ragged batches
+
+def ragged_offsets(lens) -> np.ndarray:
+    """int32 [B + 1] first rows of B packed trees of sizes lens."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lens, dtype=np.int64))]).astype(np.int32)
+
+
+def pack_rows(dense: np.ndarray, lens) -> np.ndarray:
+    """Rows 0 .. lens[b] - 1 of every sequence b of a [B][N][...] array, packed
+    sequence after sequence into [sum(lens)][...]."""
+    parts = [dense[b, :n] for b, n in enumerate(lens)]
+    return np.ascontiguousarray(np.concatenate(parts, axis=0)) if parts else dense[:0, 0]
+
+
+def ragged_mary(rng: np.random.Generator, batch: int, width: int, depths) -> list:
+    """Per-sequence M-ary draft trees of equal width and per-sequence depth
+    (a batch that mixes draft budgets): list of parent arrays."""
+    return [tree_mary(rng, width, int(rng.choice(depths))) for _ in range(batch)]
+
+
 # ---------------------------------------------------------------- upload
 
 def to_device(arr: np.ndarray, io: str = "", device="cuda"):
