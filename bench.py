@@ -49,28 +49,34 @@ def log(msg):
 
 # ---------------------------------------------------------------- byte model
 
-def verify_bytes(s, e):
-    """Algorithmic HBM bytes of one verify launch: S0 read once, q/k read once
-    per key head, v read, beta/g/parent read, o written, the cache written
-    (u, Gamma, ancestor rows, depth, status)."""
-    B, N, Hk, Hv, d = s.batch, s.n_nodes, s.h_k, s.h_v, s.d
-    Wd = (N + 31) // 32
-    per_seq = (4 * Hv * d * d + 2 * N * Hk * d * e + N * Hv * d * e + 8 * N * Hv + 4 * N
-               + N * Hv * d * e + 4 * N * Hv * d + 4 * N * Hv + 4 * N * Wd + 4 * N + 4)
-    return B * per_seq
+def verify_bytes(s, e, sizes):
+    """Algorithmic HBM bytes of one verify launch, summed over the sequences (a
+    tree of n nodes): S0 read once, q/k read once per key head, v read,
+    beta/g/parent read, o written, the cache rows of the n nodes written (u,
+    Gamma, ancestor rows, depth) and the status; a ragged batch also reads its
+    two offsets per sequence."""
+    Hk, Hv, d = s.h_k, s.h_v, s.d
+    Wd = (s.n_nodes + 31) // 32
+    tot = 0
+    for n in sizes:
+        n = int(n)
+        tot += (4 * Hv * d * d + 2 * n * Hk * d * e + n * Hv * d * e + 8 * n * Hv + 4 * n
+                + n * Hv * d * e + 4 * n * Hv * d + 4 * n * Hv + 4 * n * Wd + 4 * n + 4
+                + (8 if s.depths else 0))
+    return tot
 
 
-def commit_bytes(s, e, path_lens):
+def commit_bytes(s, e, path_lens, sizes):
     """Algorithmic bytes of one commit launch: S in + out, and per path node its
     u row, k row and Gamma, plus the accepted row of the ancestor mask, the
-    path written and the small per-sequence scalars."""
-    Hk, Hv, d, N = s.h_k, s.h_v, s.d, s.n_nodes
-    Wd = (N + 31) // 32
+    path written (the tree's n slots) and the small per-sequence scalars."""
+    Hk, Hv, d = s.h_k, s.h_v, s.d
+    Wd = (s.n_nodes + 31) // 32
     tot = 0
-    for P in path_lens:
+    for P, n in zip(path_lens, sizes):
         P = max(int(P), 0)
         tot += (8 * Hv * d * d + P * (4 * Hv * d + Hk * d * e + 4 * Hv) + 4 * Hv
-                + 4 * Wd + 4 * N + 12)
+                + 4 * Wd + 4 * int(n) + 12 + (8 if s.depths else 0))
     return tot
 
 
@@ -83,6 +89,10 @@ def run_gpu(args, s):
     dev = torch.device("cuda:0")
     e = 2 if s.io == "bf16" else 4
     parent, accepted = W.make_trees(s)
+    sizes = W.tree_sizes(s)
+    ragged = bool(s.depths)
+    # a ragged batch: per-node arrays packed tree after tree, located by offsets
+    pack = (lambda a: W.pack_rows(a, sizes)) if ragged else (lambda a: a)
     L = s.layers
     log(f"generating {L} layers of {s.name} on the host")
     t0 = time.time()
@@ -91,6 +101,8 @@ def run_gpu(args, s):
         layers = []
         for l, f in enumerate(futs):
             lay = f.result()
+            if ragged:
+                lay.update({key: pack(lay[key]) for key in ("q", "k", "v", "beta", "g")})
             layers.append({
                 "q": W.to_device(lay["q"], s.io, dev), "k": W.to_device(lay["k"], s.io, dev),
                 "v": W.to_device(lay["v"], s.io, dev),
@@ -102,10 +114,14 @@ def run_gpu(args, s):
             del lay
     log(f"generated and uploaded in {time.time() - t0:.1f} s")
     dims = T.dims(s.batch, s.n_nodes, s.h_k, s.h_v, s.d, s.d, s.io)
-    par = W.to_device(parent, device=dev)
+    par = W.to_device(pack(parent), device=dev)
     # the acceptance walk runs on the device each step and writes acc; the
     # synthetic tokens make it accept the workload's chosen leaf
-    draft, target, troot = (W.to_device(x, device=dev) for x in W.make_tokens(s, parent, accepted))
+    draft, target, troot = W.make_tokens(s, parent, accepted)
+    draft, target, troot = (W.to_device(x, device=dev) for x in (pack(draft), pack(target), troot))
+    if ragged:
+        offs = W.to_device(W.ragged_offsets(sizes), device=dev)
+        T.check_offsets(offs, dims, int(sizes.sum()))
     acc = torch.empty((s.batch,), dtype=torch.int32, device=dev)
     alen = torch.empty((s.batch,), dtype=torch.int32, device=dev)
     nxt = torch.empty((s.batch,), dtype=torch.int32, device=dev)
@@ -114,34 +130,40 @@ def run_gpu(args, s):
     caches2 = [[T.TreeCache(dims, dev), T.TreeCache(dims, dev) if args.fused else None]
                for _ in range(L)]
     caches = [c[0] for c in caches2]
-    o = [torch.empty((s.batch, s.n_nodes, s.h_v, s.d), dtype=layers[0]["q"].dtype,
-                     device=dev) for _ in range(L)]
-    path = torch.empty((s.batch, s.n_nodes), dtype=torch.int32, device=dev)
+    rows = (int(sizes.sum()),) if ragged else (s.batch, s.n_nodes)
+    o = [torch.empty(rows + (s.h_v, s.d), dtype=layers[0]["q"].dtype, device=dev)
+         for _ in range(L)]
+    path = torch.empty(rows, dtype=torch.int32, device=dev)
     plen = torch.empty((s.batch,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     phase = [0]
+    # (ragged: the same trees every step, so the previous tree's offsets are
+    # this step's)
+    R = (lambda name: getattr(T, name + "_ragged")) if ragged else (lambda name: getattr(T, name))
+    O = (lambda: (offs,)) if ragged else (lambda: ())
 
     def verify(l):
         x = layers[l]
-        T.gdn_tree_verify(dims, x["S"][phase[0]], x["q"], x["k"], x["v"], x["beta"], x["g"],
-                          par, o[l], caches[l], sptr)
+        R("gdn_tree_verify")(dims, *O(), x["S"][phase[0]], x["q"], x["k"], x["v"], x["beta"],
+                             x["g"], par, o[l], caches[l], sptr)
 
     def commit(l):
         x = layers[l]
-        T.gdn_tree_commit(dims, x["S"][phase[0]], x["S"][1 - phase[0]], x["k"], caches[l],
-                          acc, path, plen, sptr)
+        R("gdn_tree_commit")(dims, *O(), x["S"][phase[0]], x["S"][1 - phase[0]], x["k"],
+                             caches[l], acc, path, plen, sptr)
 
     cur = [0]
 
     def commit_verify(l):
         x = layers[l]
-        T.gdn_tree_commit_verify(dims, x["S"][phase[0]], x["S"][1 - phase[0]], x["k"],
-                                 caches2[l][cur[0]], acc, path, plen, x["q"], x["k"], x["v"],
-                                 x["beta"], x["g"], par, o[l], caches2[l][1 - cur[0]], sptr)
+        R("gdn_tree_commit_verify")(dims, *O(), x["S"][phase[0]], x["S"][1 - phase[0]], x["k"],
+                                    caches2[l][cur[0]], acc, path, plen, *O(), x["q"], x["k"],
+                                    x["v"], x["beta"], x["g"], par, o[l], caches2[l][1 - cur[0]],
+                                    sptr)
 
     def accept(_l=0):
-        T.gdn_tree_accept(dims, par, draft, target, troot, acc, alen, nxt, sptr)
+        R("gdn_tree_accept")(dims, *O(), par, draft, target, troot, acc, alen, nxt, sptr)
 
     def step():
         if args.fused:
@@ -206,8 +228,9 @@ def run_gpu(args, s):
     return {
         "total_ms": total_ms, "verify_ms": verify_ms, "commit_ms": commit_ms,
         "fused_ms": fused_ms, "accept_ms": accept_ms,
-        "verify_bytes": verify_bytes(s, e), "commit_bytes": commit_bytes(s, e, path_lens),
-        "path_lens": path_lens, "parent": parent, "accepted": accepted,
+        "verify_bytes": verify_bytes(s, e, sizes),
+        "commit_bytes": commit_bytes(s, e, path_lens, sizes),
+        "path_lens": path_lens, "parent": parent, "accepted": accepted, "sizes": sizes,
     }
 
 
@@ -215,32 +238,39 @@ def run_gpu(args, s):
 
 def cpu_baseline(s, budget_s):
     """The fp64 oracle, path-walk mode, on the first sequences of layer 0 (all
-    value heads), growing the sample until it took about budget_s seconds."""
+    value heads), growing the sample until it took about budget_s seconds.  A
+    ragged batch's trees each run at their own size."""
     import oracle
     lib = oracle.load()
     parent, accepted = W.make_trees(s)
+    sizes = W.tree_sizes(s)
     lay = W.make_layer(s, 0)
     f = lambda a: W.io_to_f64(a, s.io)
-    nb, spent, done_nodes = 1, 0.0, 0
-    t_all = 0.0
+
+    def run(b0, b1, n):
+        sl = slice(b0, b1)
+        oracle.verify(lay["S0"][sl].astype(np.float64), f(lay["q"][sl, :n]), f(lay["k"][sl, :n]),
+                      f(lay["v"][sl, :n]), lay["beta"][sl, :n].astype(np.float64),
+                      lay["g"][sl, :n].astype(np.float64), parent[sl, :n], accepted[sl],
+                      memo=False, lib=lib)
+
+    nb = 1
     while True:
-        sl = slice(0, nb)
-        args = (lay["S0"][sl].astype(np.float64), f(lay["q"][sl]), f(lay["k"][sl]),
-                f(lay["v"][sl]), lay["beta"][sl].astype(np.float64),
-                lay["g"][sl].astype(np.float64), parent[sl], accepted[sl])
         t0 = time.perf_counter()
-        oracle.verify(*args, memo=False, lib=lib)
+        if s.depths:
+            for b in range(nb):
+                run(b, b + 1, int(sizes[b]))
+        else:
+            run(0, nb, s.n_nodes)
         dt = time.perf_counter() - t0
-        t_all += dt
         if dt >= budget_s / 4 or nb >= s.batch:
             break
         nb = min(s.batch, nb * 2)
-    # nodes/s/layer: a full layer has s.batch sequences; the sample had nb
-    value = (nb * s.n_nodes) / dt
-    return {"value": value, "unit": "nodes/s/layer", "cores": oracle.max_threads(lib),
+    nodes = int(sizes[:nb].sum())
+    return {"value": nodes / dt, "unit": "nodes/s/layer", "cores": oracle.max_threads(lib),
             "kind": "oracle",
             "sample": f"layer 0, sequences 0..{nb - 1} (all {s.h_v} value heads, "
-                      f"{nb * s.n_nodes} nodes), fp64 path walk, {dt:.2f} s"}
+                      f"{nodes} nodes), fp64 path walk, {dt:.2f} s"}
 
 
 # ---------------------------------------------------------------- copy
@@ -319,7 +349,7 @@ def main():
     s = W.spec(args.workload)
     r = run_gpu(args, s)
     L = s.layers
-    nodes = s.batch * s.n_nodes
+    nodes = int(r["sizes"].sum())
     value = nodes * L * args.steps / (r["total_ms"] * 1e-3)
     if args.fused:
         # the fused launch reads the state once for both halves
@@ -349,7 +379,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": s.name, "batch": s.batch, "n_nodes": s.n_nodes, "layers": L,
-            "tree": f"{s.width}-ary x depth {s.depth}" if s.tree == "mary" else s.tree,
+            "tree": (f"{s.width}-ary x depth {'/'.join(map(str, s.depths))} (ragged, "
+                     f"{nodes} nodes)" if s.depths else
+                     f"{s.width}-ary x depth {s.depth}" if s.tree == "mary" else s.tree),
             "h_k": s.h_k, "h_v": s.h_v, "d_k": s.d, "d_v": s.d, "io": s.io,
             "state": "f32", "launches": "commit_verify" if args.fused else "verify+commit",
         },

@@ -75,3 +75,23 @@ def test_tokens_accept_the_chosen_leaf(name):
     assert np.array_equal(acc, accepted)
     _, depth, _ = oracle.tree(parent)
     assert np.array_equal(alen, depth[np.arange(len(accepted)), accepted] + 1)
+
+
+def test_ragged_workload_packing():
+    """The ragged workload's tree sizes match the trees make_trees draws (entries
+    past a tree's size are -1), the offsets are their prefix sums, and packing
+    keeps each sequence's rows in order."""
+    import workloads as W
+    s = W.spec("maryragged_b64_l36")
+    parent, accepted = W.make_trees(s)
+    sizes = W.tree_sizes(s)
+    assert set(sizes.tolist()) <= {16, 32, 64, 128} and len(set(sizes.tolist())) > 1
+    for b, n in enumerate(sizes):
+        assert (parent[b, :n] < np.arange(n)).all() and (parent[b, n:] == -1).all()
+        assert 0 <= accepted[b] < n
+    off = W.ragged_offsets(sizes)
+    assert off[0] == 0 and off[-1] == sizes.sum() and (np.diff(off) == sizes).all()
+    x = np.arange(s.batch * s.n_nodes * 3).reshape(s.batch, s.n_nodes, 3)
+    p = W.pack_rows(x, sizes)
+    for b, n in enumerate(sizes):
+        assert np.array_equal(p[off[b]:off[b + 1]], x[b, :n])

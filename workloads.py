@@ -42,7 +42,7 @@ __all__ = [
     "Spec", "WORKLOADS", "spec", "bf16_bits", "bf16_to_f32", "io_to_f64",
     "tree_binary7", "tree_mary", "tree_chain", "tree_random_recursive",
     "tree_star", "leaves", "pick_leaf", "make_trees", "make_layer",
-    "draw_layer",
+    "draw_layer", "tree_sizes", "ragged_offsets", "pack_rows",
 ]
 
 
@@ -63,6 +63,7 @@ class Spec:
     depth: int = 0     # gamma for M-ary trees
     beta_mu: float = 0.0
     shared_tree: bool = False   # one tree per sequence shared by all layers
+    depths: tuple = ()          # ragged: each M-ary tree's depth drawn from these
 
     @property
     def group(self) -> int:
@@ -81,6 +82,11 @@ WORKLOADS: Dict[str, Spec] = {
     # 36 layers back to back, 64 sequences, 128-node M=8 trees shared by layers.
     "mary128_b64_l36": Spec("mary128_b64_l36", 64, 128, 16, 32, 128, "bf16", 36,
                             "mary", 3, width=8, depth=16, shared_tree=True),
+    # The 36-layer step with a ragged batch: 64 sequences whose M=8 trees have
+    # depth 2, 4, 8 or 16 (draft budgets of 16 .. 128 nodes), packed by offsets.
+    "maryragged_b64_l36": Spec("maryragged_b64_l36", 64, 128, 16, 32, 128, "bf16", 36,
+                               "mary", 6, width=8, depth=16, shared_tree=True,
+                               depths=(2, 4, 8, 16)),
     # 8 sequences, 16 heads, 256-node chain, beta pushed toward 1.
     "chain256_b8": Spec("chain256_b8", 8, 256, 16, 16, 128, "bf16", 1, "chain", 4,
                         beta_mu=2.0),
@@ -165,11 +171,18 @@ def pick_leaf(rng: np.random.Generator, parent: np.ndarray) -> int:
 
 
 def make_trees(s: Spec):
-    """(parent [B][N] int32, accepted [B] int32) for a workload."""
+    """(parent [B][N] int32, accepted [B] int32) for a workload.  A ragged
+    workload's sequence b fills its first tree_sizes(s)[b] entries; the rest
+    are -1 and belong to no tree."""
     rng = np.random.default_rng(s.seed)
-    parent = np.empty((s.batch, s.n_nodes), dtype=np.int32)
+    parent = np.full((s.batch, s.n_nodes), -1, dtype=np.int32)
     accepted = np.empty(s.batch, dtype=np.int32)
     for b in range(s.batch):
+        if s.depths:
+            p = tree_mary(rng, s.width, int(rng.choice(s.depths)))
+            parent[b, :len(p)] = p
+            accepted[b] = pick_leaf(rng, p)
+            continue
         if s.tree == "binary7":
             p, a = tree_binary7(), 5
         elif s.tree == "mary":
@@ -185,6 +198,20 @@ def make_trees(s: Spec):
         parent[b] = p
         accepted[b] = a
     return parent, accepted
+
+
+def tree_sizes(s: Spec) -> np.ndarray:
+    """Node count of each sequence's tree (n_nodes unless the workload is
+    ragged), int64 [B]."""
+    if not s.depths:
+        return np.full(s.batch, s.n_nodes, dtype=np.int64)
+    rng = np.random.default_rng(s.seed)
+    sizes = np.empty(s.batch, dtype=np.int64)
+    for b in range(s.batch):          # the same draws as make_trees
+        p = tree_mary(rng, s.width, int(rng.choice(s.depths)))
+        pick_leaf(rng, p)
+        sizes[b] = len(p)
+    return sizes
 
 
 def make_tokens(s: Spec, parent: np.ndarray, accepted: np.ndarray, vocab: int = 32000):
@@ -277,12 +304,6 @@ def pack_rows(dense: np.ndarray, lens) -> np.ndarray:
     sequence after sequence into [sum(lens)][...]."""
     parts = [dense[b, :n] for b, n in enumerate(lens)]
     return np.ascontiguousarray(np.concatenate(parts, axis=0)) if parts else dense[:0, 0]
-
-
-def ragged_mary(rng: np.random.Generator, batch: int, width: int, depths) -> list:
-    """Per-sequence M-ary draft trees of equal width and per-sequence depth
-    (a batch that mixes draft budgets): list of parent arrays."""
-    return [tree_mary(rng, width, int(rng.choice(depths))) for _ in range(batch)]
 
 
 # ---------------------------------------------------------------- upload
