@@ -47,6 +47,9 @@ def _bind(path: str):
     lib.oracle_verify.restype = ci
     lib.oracle_accept.argtypes = [ci, ci] + [i32p] * 7
     lib.oracle_accept.restype = ci
+    f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+    lib.oracle_build.argtypes = [ci, ci, ci, ci, f32p, i32p, i32p, i32p, f32p]
+    lib.oracle_build.restype = ci
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ci
     return lib
@@ -101,6 +104,25 @@ def accept(parent, draft, target, target_root, lib=None):
     if rc:
         raise ValueError(f"oracle_accept failed: {rc}")
     return acc, alen, nxt
+
+
+def build_tree(logp, tok, n_nodes, width, lib=None):
+    """Draft trees of n_nodes nodes built with `width` expansions per step from
+    synthetic drafter scores: logp [B][n_nodes + 1][K] float32 (row 0 the
+    prefix's K continuations, row 1 + i node i's), tok the same shape, int32.
+    Returns (parent, token, score), [B][n_nodes] each (score float32)."""
+    lib = lib or load()
+    logp = np.ascontiguousarray(logp, dtype=np.float32)
+    tok = np.ascontiguousarray(tok, dtype=np.int32)
+    B, R, K = logp.shape
+    assert R == n_nodes + 1 and tok.shape == logp.shape
+    parent = np.empty((B, n_nodes), np.int32)
+    token = np.empty((B, n_nodes), np.int32)
+    score = np.empty((B, n_nodes), np.float32)
+    rc = lib.oracle_build(B, n_nodes, K, width, logp, tok, parent, token, score)
+    if rc:
+        raise ValueError(f"oracle_build failed: {rc}")
+    return parent, token, score
 
 
 def verify(S0, q, k, v, beta, g, parent, accepted, memo=False, nthreads=0, lib=None):

@@ -166,6 +166,85 @@ int oracle_accept(int B, int N, const int32_t* parent, const int32_t* draft,
     return 0;
 }
 
+/*
+ * Draft-tree construction with w expansions per step (the pages' section 2,
+ * "tree construction": DySpec's best-first expansion, changed so that the w
+ * best candidates leave the candidate heap together and are expanded
+ * together, which builds a tree of N nodes in ceil(N / w) sequential steps).
+ * The drafter is replaced by synthetic scores given as input:
+ *   logp[b][r][c], tok[b][r][c], r = 0 .. N, c < K: row 0 holds the drafter's
+ *   K continuations of the prefix (log-probability, token), row 1 + i those of
+ *   node i (whatever node receives index i).
+ * A candidate is the continuation of rank c after a node p (p = -1: the
+ * prefix); its score is score(p) + logp[b][p + 1][c], with score(prefix) = 0,
+ * one fp32 addition (so the selections are decided in fp32, as the kernel
+ * decides them).  Candidates are ordered by score, higher first, then by p,
+ * then by c, lower first.  Each step takes the first m = min(w, N - n, number
+ * of candidates) of them, makes them nodes n, n + 1, ... in that order
+ * (parent p, token tok[b][p + 1][c], that score), removes them, and adds the K
+ * children of each.  Steps repeat until the tree has N nodes.
+ * Returns 0, or -1 for bad sizes, -2 when out of memory.
+ */
+typedef struct {
+    float s;
+    int32_t p, c;
+} cand_t;
+
+static int cand_cmp(const void* x, const void* y)
+{
+    const cand_t* a = (const cand_t*)x;
+    const cand_t* b = (const cand_t*)y;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    if (a->p != b->p) return a->p < b->p ? -1 : 1;
+    return a->c < b->c ? -1 : (a->c > b->c);
+}
+
+int oracle_build(int B, int N, int K, int w, const float* logp, const int32_t* tok,
+                 int32_t* parent, int32_t* token, float* score)
+{
+    if (B < 0 || N < 1 || K < 1 || w < 1) return -1;
+    cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)K * (N + 1));
+    if (!cand) return -2;
+    for (int b = 0; b < B; ++b) {
+        const float* lp = logp + (size_t)b * (N + 1) * K;
+        const int32_t* tk = tok + (size_t)b * (N + 1) * K;
+        int32_t* par = parent + (size_t)b * N;
+        int32_t* out_tok = token + (size_t)b * N;
+        float* sc = score + (size_t)b * N;
+        int nc = 0, n = 0;
+        for (int c = 0; c < K; ++c) {
+            cand[nc].s = 0.0f + lp[c];
+            cand[nc].p = -1;
+            cand[nc].c = c;
+            ++nc;
+        }
+        while (n < N) {
+            qsort(cand, (size_t)nc, sizeof(cand_t), cand_cmp);
+            int m = w;
+            if (m > N - n) m = N - n;
+            if (m > nc) m = nc;
+            const int first = n;
+            for (int t = 0; t < m; ++t, ++n) {
+                par[n] = cand[t].p;
+                out_tok[n] = tk[(size_t)(cand[t].p + 1) * K + cand[t].c];
+                sc[n] = cand[t].s;
+            }
+            memmove(cand, cand + m, sizeof(cand_t) * (size_t)(nc - m));
+            nc -= m;
+            for (int i = first; i < n; ++i)
+                for (int c = 0; c < K; ++c) {
+                    cand[nc].s = sc[i] + lp[(size_t)(i + 1) * K + c];
+                    cand[nc].p = i;
+                    cand[nc].c = c;
+                    ++nc;
+                }
+        }
+    }
+    free(cand);
+    return 0;
+}
+
 /* One gated delta step on S (dv x dk, row-major), in the fixed order above. */
 static void gdn_step(int dv, int dk, double* S, const double* k, const double* v,
                      double beta, double g, double* w)

@@ -13,7 +13,11 @@ when the oracle disagrees with:
   * tree invariants: siblings, non-ancestors, topological relabelling, and the
     conventions for invalid trees and accepted indices;
   * for the acceptance walk, a per-node restatement of greedy acceptance
-    checked node by node (tests/oracle_pins.py, accept_brute_force).
+    checked node by node (tests/oracle_pins.py, accept_brute_force);
+  * for the tree construction, a worked example derived by hand
+    (tests/golden/hand_build_k2_n5.json), the best path scores of an infinite
+    tree counted by convolution (width 1 is best-first expansion), and each
+    step of the output checked against the candidates open at that step.
 The same battery runs against deliberately broken copies of the oracle
 (tests/test_oracle_mutants.py) to show that each plausible mistake trips a pin.
 """
@@ -407,10 +411,97 @@ def pin_accept_conventions(lib):
     assert (acc[0], alen[0], nxt[0]) == (-1, -1, 7)
 
 
+def pin_build_hand_example(lib):
+    """Tree construction against the hand-worked example (widths 2, 1, 8)."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_build_k2_n5.json")))
+    lp = np.array(g["logp"], np.float32)[None]
+    tk = np.array(g["tok"], np.int32)[None]
+    for case in g["cases"]:
+        par, tok, sc = oracle.build_tree(lp, tk, g["n_nodes"], case["width"], lib=lib)
+        assert par[0].tolist() == case["parent"], case["width"]
+        assert tok[0].tolist() == case["token"], case["width"]
+        assert sc[0].tolist() == case["score"], case["width"]
+
+
+def top_path_scores(logp_row, n):
+    """The n highest path scores of the infinite tree in which every node has
+    the same K continuations (log-probabilities logp_row, all negative
+    multiples of 1/4): counts of paths by depth and score by convolution, then
+    the best n scores, each as often as it occurs."""
+    steps = [int(round(-4 * x)) for x in logp_row]           # score = -steps / 4
+    counts = {0: 1}                                          # depth 0: the prefix
+    best = {}
+    for _ in range(n):
+        nxt = {}
+        for s0, c0 in counts.items():
+            for st in steps:
+                nxt[s0 + st] = nxt.get(s0 + st, 0) + c0
+        counts = nxt
+        for s0, c0 in counts.items():
+            best[s0] = best.get(s0, 0) + c0
+    out = []
+    for s0 in sorted(best):
+        out += [-s0 / 4] * best[s0]
+        if len(out) >= n:
+            break
+    return out[:n]
+
+
+def pin_build_best_first_top_scores(lib):
+    """Width 1 is best-first expansion: when every node offers the same
+    continuations with negative log-probabilities, the tree holds the n best
+    paths of the infinite tree, so its scores are the n highest path scores
+    (counted independently, by convolution)."""
+    rng = np.random.default_rng(41)
+    for K, n in ((2, 9), (3, 20), (4, 33), (1, 6)):
+        row = -(rng.integers(1, 12, size=K) / 4.0)
+        lp = np.broadcast_to(row.astype(np.float32), (1, n + 1, K)).copy()
+        tk = np.arange((n + 1) * K, dtype=np.int32).reshape(1, n + 1, K)
+        par, tok, sc = oracle.build_tree(lp, tk, n, 1, lib=lib)
+        assert sorted(sc[0].tolist(), reverse=True) == top_path_scores(row, n), (K, n)
+
+
+def pin_build_steps_valid(lib):
+    """Each step's nodes, checked against the definition from the output alone:
+    the step sizes (min(w, nodes left, candidates)); every node's parent placed
+    in an earlier step; its token and score from its parent's row (score in
+    fp32); and the step's nodes are the best of the candidates open at that
+    step (score, then parent, then rank), in that order.  Scores are
+    quantised so that ties across parents and ranks occur."""
+    rng = np.random.default_rng(43)
+    for B, K, n, w in ((3, 4, 30, 4), (2, 2, 17, 3), (2, 5, 40, 8), (2, 3, 12, 1), (1, 1, 7, 3),
+                       (1, 8, 20, 64)):
+        lp = (-rng.integers(0, 6, size=(B, n + 1, K)) / 2.0).astype(np.float32)
+        tk = rng.permutation(B * (n + 1) * K).astype(np.int32).reshape(B, n + 1, K)
+        par, tok, sc = oracle.build_tree(lp, tk, n, w, lib=lib)
+        for b in range(B):
+            rank = {}
+            for i in range(n):
+                p = int(par[b, i])
+                row = p + 1
+                c = [x for x in range(K) if tk[b, row, x] == tok[b, i]]
+                assert len(c) == 1, (b, i)
+                rank[i] = c[0]
+                base = np.float32(0.0) if p < 0 else sc[b, p]
+                assert sc[b, i] == np.float32(base + lp[b, row, c[0]]), (b, i)
+            placed, open_ = 0, [(-1, x) for x in range(K)]
+            score_of = lambda pc: (np.float32(0.0) if pc[0] < 0 else sc[b, pc[0]]) + lp[b, pc[0] + 1, pc[1]]
+            while placed < n:
+                m = min(w, n - placed, len(open_))
+                ranked = sorted(open_, key=lambda pc: (-np.float32(score_of(pc)), pc[0], pc[1]))
+                step = [(int(par[b, i]), rank[i]) for i in range(placed, placed + m)]
+                assert step == ranked[:m], (b, placed)
+                for i in range(placed, placed + m):
+                    assert par[b, i] < placed, (b, i)
+                open_ = ranked[m:] + [(i, x) for i in range(placed, placed + m) for x in range(K)]
+                placed += m
+
+
 ALL_PINS = [
     pin_autograd_step, pin_hand_example, pin_beta_zero_pure_decay,
     pin_projector_writes_v, pin_chain_product_form, pin_chain_is_linear_scan,
     pin_masks_paths, pin_dense_solve, pin_grouped_heads, pin_siblings_share_parent,
     pin_non_ancestors_do_not_matter, pin_topological_relabel, pin_memo_equals_walk,
     pin_conventions, pin_accept_brute_force, pin_accept_conventions,
+    pin_build_hand_example, pin_build_best_first_top_scores, pin_build_steps_valid,
 ]

@@ -63,6 +63,22 @@ MUTANTS = {
     "accept_own_target": ("if (par[i] == cur && dr[i] == want) {", "if (par[i] == cur && dr[i] == tg[i]) {"),
     # the accepted length counts the prefix as a node
     "accept_len_off": ("        int cur = -1, len = 0;", "        int cur = -1, len = 1;"),
+    # tree construction expands one candidate per step whatever the width
+    "build_one_per_step": ("            int m = w;\n", "            int m = 1;\n"),
+    # equal scores after one parent go to the higher rank
+    "build_tie_rank": ("return a->c < b->c ? -1 : (a->c > b->c);", "return a->c > b->c ? -1 : (a->c < b->c);"),
+    # equal scores go to the higher parent index
+    "build_tie_parent": ("if (a->p != b->p) return a->p < b->p ? -1 : 1;",
+                         "if (a->p != b->p) return a->p > b->p ? -1 : 1;"),
+    # a node's children read the drafter row of the node before it
+    "build_row_off": ("cand[nc].s = sc[i] + lp[(size_t)(i + 1) * K + c];",
+                      "cand[nc].s = sc[i] + lp[(size_t)i * K + c];"),
+    # every node's token is read from the prefix's row
+    "build_token_row": ("out_tok[n] = tk[(size_t)(cand[t].p + 1) * K + cand[t].c];",
+                        "out_tok[n] = tk[cand[t].c];"),
+    # a child's score forgets its parent's score
+    "build_no_accumulate": ("cand[nc].s = sc[i] + lp[(size_t)(i + 1) * K + c];",
+                            "cand[nc].s = lp[(size_t)(i + 1) * K + c];"),
 }
 
 CHILD = r"""
