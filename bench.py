@@ -225,13 +225,45 @@ def run_gpu(args, s):
         + f", accept {accept_ms * 1e3:.1f} us/launch")
     path_lens = plen.cpu().numpy()
     assert np.array_equal(acc.cpu().numpy(), accepted), "the acceptance walk missed the chosen leaf"
+    build = time_tree_build(s, stream, reps)
     return {
         "total_ms": total_ms, "verify_ms": verify_ms, "commit_ms": commit_ms,
         "fused_ms": fused_ms, "accept_ms": accept_ms,
         "verify_bytes": verify_bytes(s, e, sizes),
         "commit_bytes": commit_bytes(s, e, path_lens, sizes),
         "path_lens": path_lens, "parent": parent, "accepted": accepted, "sizes": sizes,
+        "build": build,
     }
+
+
+def time_tree_build(s, stream, reps, topk=8):
+    """The step before verification: building the batch's draft trees from the
+    drafter's top-k continuations with w = M expansions per step (a tree of the
+    workload's largest size; synthetic drafter scores).  Timed with HIP events
+    on the launch stream, like the other kernels."""
+    import torch
+    import tree_masked_gated_amd as T
+    w = s.width or 8
+    N = s.n_nodes
+    lp, tk = W.draft_scores(np.random.default_rng(s.seed + 1000), s.batch, N, topk)
+    bd = T.build_dims(s.batch, N, topk, w)
+    lp_d, tk_d = W.to_device(lp), W.to_device(tk)
+    par = torch.empty((s.batch, N), dtype=torch.int32, device="cuda")
+    tok = torch.empty_like(par)
+    sc = torch.empty((s.batch, N), dtype=torch.float32, device="cuda")
+    sptr = stream.cuda_stream
+    T.gdn_tree_build(bd, lp_d, tk_d, par, tok, sc, sptr)     # untimed: code load
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        T.gdn_tree_build(bd, lp_d, tk_d, par, tok, sc, sptr)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    log(f"tree build {ms * 1e3:.1f} us/launch ({s.batch} trees of {N} nodes, k {topk}, w {w})")
+    return {"launch_us": ms * 1e3, "batch": s.batch, "n_nodes": N, "topk": topk, "width": w,
+            "steps": -(-N // w), "trees_per_s": s.batch / (ms * 1e-3)}
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -400,6 +432,7 @@ def main():
             "achieved_GBs": r["commit_bytes"] / (r["commit_ms"] * 1e-3) / 1e9,
         },
         "accept": {"launch_us": r["accept_ms"] * 1e3, "per": "step"},
+        "tree_build": r["build"],
         "cpu_baseline": base,
     }
     print(json.dumps(out), flush=True)

@@ -263,6 +263,42 @@ int gdn_tree_accept_ragged(const gdn_tree_dims* dims, const int32_t* offsets, co
                            int32_t* accepted, int32_t* accept_len, int32_t* next_token,
                            hipStream_t stream);
 
+/*
+ * Draft-tree construction with w expansions per step (page "Trees from
+ * Marginals", section 2, tree construction: best-first expansion as in
+ * DySpec, changed so that the w best candidates leave the candidate heap
+ * together and are expanded together, building a tree of N nodes in
+ * ceil(N / w) sequential steps).  The drafter itself is outside this library:
+ * its outputs are the input.
+ *
+ *   logp [B][N + 1][K] fp32   row 0: log-probabilities of the drafter's K
+ *                             continuations of the prefix; row 1 + i: those
+ *                             of node i (the node that receives index i)
+ *   tok  [B][N + 1][K] int32  the continuations' tokens, same layout
+ *   parent [B][N] int32  out: the tree, topologically ordered (parent[i] < i,
+ *                             -1 under the prefix): gdn_tree_verify's input
+ *   token  [B][N] int32  out: each node's token (its draft token for
+ *                             gdn_tree_accept)
+ *   score  [B][N] fp32   out: each node's score
+ *
+ * A candidate is the continuation of rank c after a node p already in the
+ * tree (p = -1: the prefix); its score is score(p) + logp[p + 1][c], one fp32
+ * addition, with score(prefix) = 0.  Each step takes the min(w, N - n, open
+ * candidates) best ones, ordered by score (higher first), then p, then c
+ * (lower first), makes them nodes n, n + 1, ... in that order, and opens the
+ * K continuations of each.  logp must hold no NaN.
+ *
+ * Sizes: 1 <= N <= 1024, 1 <= K <= 64, w >= 1, and the per-sequence working
+ * set, about 8 (2N + pow2(min(w, N) K)) + 4 (N + 1) K + 12 N bytes, within the
+ * 160 KiB of LDS (else GDN_ERR_DIMS).  batch = 0 launches nothing.
+ */
+typedef struct {
+    int32_t batch, n_nodes, topk, width;
+} gdn_tree_build_dims;
+
+int gdn_tree_build(const gdn_tree_build_dims* dims, const float* logp, const int32_t* tok,
+                   int32_t* parent, int32_t* token, float* score, hipStream_t stream);
+
 /* Static description of a gdn_status value. */
 const char* gdn_tree_strerror(int status);
 

@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["gdn_tree_accept", "gdn_tree_accept_ragged", "gdn_tree_cache_bytes",
+    assert names == ["gdn_tree_accept", "gdn_tree_accept_ragged", "gdn_tree_build",
+                     "gdn_tree_cache_bytes",
                      "gdn_tree_commit", "gdn_tree_commit_ragged", "gdn_tree_commit_verify",
                      "gdn_tree_commit_verify_ragged", "gdn_tree_strerror", "gdn_tree_verify",
                      "gdn_tree_verify_ragged"]
@@ -154,6 +155,24 @@ def test_ragged_error_codes():
     assert ACR(good, OFF_ODD, ok7) == -5
     assert ACR(good, OFF, ok7[:6] + [ODD]) == -5
     assert ACR(T.dims(0, 7, 1, 2, 16, 16, 0), None, [None] * 7) == 0
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="fake device pointers are only passed where no GPU exists")
+def test_build_error_codes():
+    """Tree construction: sizes (N in [1, 1024], K in [1, 64], w >= 1, the
+    working set within LDS), NULL and alignment, batch 0."""
+    r = lambda d: ctypes.byref(d) if d is not None else None
+    BD = lambda d, p: T._lib.gdn_tree_build(r(d), *p, None)
+    ok5 = [FAKE] * 5
+    assert BD(None, ok5) == -1
+    for bad in [(2, 0, 8, 8), (2, 1025, 8, 8), (2, 128, 0, 8), (2, 128, 65, 8), (2, 128, 8, 0),
+                (-1, 128, 8, 8), (2, 1024, 64, 8)]:
+        assert BD(T.build_dims(*bad), ok5) == -2, bad
+    good = T.build_dims(2, 128, 8, 8)
+    assert BD(good, ok5[:2] + [None] + ok5[3:]) == -1
+    assert BD(good, ok5[:4] + [ODD]) == -5
+    assert BD(T.build_dims(0, 128, 8, 8), [None] * 5) == 0
 
 
 def test_strerror_and_cache_bytes():

@@ -19,6 +19,7 @@ __all__ = [
     "gdn_tree_cache_bytes", "gdn_tree_verify", "gdn_tree_commit", "gdn_tree_commit_verify",
     "gdn_tree_accept", "gdn_tree_verify_ragged", "gdn_tree_commit_ragged",
     "gdn_tree_commit_verify_ragged", "gdn_tree_accept_ragged", "check_offsets",
+    "BuildDims", "build_dims", "gdn_tree_build",
     "gdn_tree_strerror", "TreeCache",
 ]
 
@@ -35,6 +36,10 @@ if not os.path.exists(lib_path):
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "n_nodes", "h_k", "h_v", "d_k", "d_v", "io_dtype")]
+
+
+class BuildDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "n_nodes", "topk", "width")]
 
 
 class Cache(ctypes.Structure):
@@ -73,6 +78,8 @@ _lib.gdn_tree_commit_verify_ragged.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 4
 _lib.gdn_tree_commit_verify_ragged.restype = _i
 _lib.gdn_tree_accept_ragged.argtypes = [ctypes.POINTER(Dims)] + [_vp] * 8 + [_vp]
 _lib.gdn_tree_accept_ragged.restype = _i
+_lib.gdn_tree_build.argtypes = [ctypes.POINTER(BuildDims)] + [_vp] * 5 + [_vp]
+_lib.gdn_tree_build.restype = _i
 _lib.gdn_tree_strerror.argtypes = [_i]
 _lib.gdn_tree_strerror.restype = ctypes.c_char_p
 
@@ -407,6 +414,29 @@ def gdn_tree_accept_ragged(d: Dims, offsets, parent, draft, target, target_root,
     rc = _lib.gdn_tree_accept_ragged(ctypes.byref(d), *ptrs, _stream(stream))
     if rc:
         raise GdnError(rc, "gdn_tree_accept_ragged")
+
+
+# ---------------------------------------------------------------- tree construction
+
+def build_dims(batch, n_nodes, topk, width) -> BuildDims:
+    return BuildDims(batch, n_nodes, topk, width)
+
+
+def gdn_tree_build(bd: BuildDims, logp, tok, parent, token, score, stream=None) -> None:
+    """Enqueue draft-tree construction with `width` expansions per step from the
+    drafter's top-k continuations (see gdn_tree.h)."""
+    torch = _torch()
+    B, N, K = bd.batch, bd.n_nodes, bd.topk
+    ptrs = [
+        _ptr(logp, (B, N + 1, K), torch.float32, "logp"),
+        _ptr(tok, (B, N + 1, K), torch.int32, "tok"),
+        _ptr(parent, (B, N), torch.int32, "parent"),
+        _ptr(token, (B, N), torch.int32, "token"),
+        _ptr(score, (B, N), torch.float32, "score"),
+    ]
+    rc = _lib.gdn_tree_build(ctypes.byref(bd), *ptrs, _stream(stream))
+    if rc:
+        raise GdnError(rc, "gdn_tree_build")
 
 
 def _check_cache(c: TreeCache, d: Dims):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdntree.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.hip", "verify_generic.hip", "verify_tiled.hip", "verify_large.hip", "commit.hip",
+SOURCES = ["abi.hip", "verify_generic.hip", "verify_tiled.hip", "verify_large.hip", "commit.hip", "build.hip",
            "accept.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

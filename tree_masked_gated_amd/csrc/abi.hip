@@ -256,6 +256,23 @@ int gdn_tree_accept_ragged(const gdn_tree_dims* dims, const int32_t* offsets, co
                        next_token, stream);
 }
 
+int gdn_tree_build(const gdn_tree_build_dims* dims, const float* logp, const int32_t* tok,
+                   int32_t* parent, int32_t* token, float* score, hipStream_t stream) {
+    if (!dims) return GDN_ERR_NULL;
+    if (dims->batch < 0 || dims->n_nodes < 1 || dims->n_nodes > kMaxNodes || dims->topk < 1 ||
+        dims->topk > kMaxBuildTopk || dims->width < 1)
+        return GDN_ERR_DIMS;
+    if (tree_build_lds_bytes(dims->n_nodes, dims->topk, dims->width) > (size_t)kMaxLds)
+        return GDN_ERR_DIMS;
+    if (dims->batch == 0) return GDN_OK;
+    if (!logp || !tok || !parent || !token || !score) return GDN_ERR_NULL;
+    if (misaligned(logp) || misaligned(tok) || misaligned(parent) || misaligned(token) ||
+        misaligned(score))
+        return GDN_ERR_ALIGN;
+    BuildArgs a{dims->batch, dims->n_nodes, dims->topk, dims->width, logp, tok, parent, token, score};
+    return launch_tree_build(a, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 const char* gdn_tree_strerror(int status) {
     switch (status) {
         case GDN_OK: return "ok";

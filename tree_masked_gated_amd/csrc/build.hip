@@ -1,0 +1,194 @@
+// build.hip -- draft-tree construction with w expansions per step, on the
+// device (page "Trees from Marginals: Autoregressive drafting with factorized
+// priors", section 2, tree construction: DySpec's best-first expansion, changed
+// so that the w best candidates leave the candidate heap together and are
+// expanded together; a tree of N nodes takes ceil(N / w) sequential steps).
+// The drafter's outputs are inputs here: for the prefix (row 0) and for every
+// node index i (row 1 + i), its K continuations as log-probabilities and
+// tokens.  A candidate is the continuation of rank c after a placed node p
+// (p = -1: the prefix), scored score(p) + logp[p + 1][c] in fp32 with
+// score(prefix) = 0; a step takes the min(w, nodes left, candidates) best,
+// ordered by score, then parent, then rank, as nodes n, n + 1, ...
+//
+// One wave per sequence.  The sequence's log-probability table is staged in
+// LDS once.  A candidate is one 64-bit key whose unsigned order is the
+// selection order (order-preserving score bits, then 0xffff - (p + 1), then
+// 0xffff - c); keys are distinct, so no tie needs a rule of its own.  The
+// open candidates are one list sorted in descending key order.  A step's new
+// children are bitonic-sorted and merged into the list by rank (each key's
+// place is its index in its own list plus the number of larger keys in the
+// other, a binary search), and the list is cut to the nodes still to place:
+// a candidate with that many better ones can never be chosen.
+#include "gdn_common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kBuildThreads = 64;
+
+// order-preserving 32-bit image of a finite (or infinite) float; -0 counts as +0
+__device__ __forceinline__ uint32_t score_bits(float s) {
+    const uint32_t u = __float_as_uint(s);
+    if ((u & 0x7fffffffu) == 0u) return 0x80000000u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float bits_score(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ uint64_t cand_key(float s, int p, int c) {
+    return ((uint64_t)score_bits(s) << 32) | ((uint64_t)(0xffffu - (uint32_t)(p + 1)) << 16) |
+           (uint64_t)(0xffffu - (uint32_t)c);
+}
+__device__ __forceinline__ int key_parent(uint64_t k) { return (int)(0xffffu - ((uint32_t)(k >> 16) & 0xffffu)) - 1; }
+__device__ __forceinline__ int key_rank(uint64_t k) { return (int)(0xffffu - ((uint32_t)k & 0xffffu)); }
+
+// number of keys of x[0 .. n) (descending, distinct) larger than key
+__device__ __forceinline__ int count_larger(const uint64_t* x, int n, uint64_t key) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (x[mid] > key) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+struct BuildLds {
+    int N, K, P;              // nodes, continuations per row, child keys per step (power of 2)
+    __host__ __device__ BuildLds(int n, int k, int p) : N(n), K(k), P(p) {}
+    // byte offsets: two lists of N keys, P child keys, then the table and per-node words
+    __host__ __device__ size_t list(int i) const { return (size_t)i * N * 8; }
+    __host__ __device__ size_t child() const { return list(2); }
+    __host__ __device__ size_t table() const { return child() + (size_t)P * 8; }
+    __host__ __device__ size_t score() const { return table() + (size_t)(N + 1) * K * 4; }
+    __host__ __device__ size_t parent() const { return score() + (size_t)N * 4; }
+    __host__ __device__ size_t rank() const { return parent() + (size_t)N * 4; }
+    __host__ __device__ size_t bytes() const { return rank() + (size_t)N * 4; }
+};
+
+__host__ __device__ inline int pow2_at_least(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+__global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int N = a.N, K = a.K, w = a.w;
+    const int wn = w < N ? w : N;
+    const BuildLds L(N, K, pow2_at_least(wn * K));
+    uint64_t* lists[2] = {reinterpret_cast<uint64_t*>(smem + L.list(0)),
+                          reinterpret_cast<uint64_t*>(smem + L.list(1))};
+    uint64_t* ck = reinterpret_cast<uint64_t*>(smem + L.child());
+    float* lp = reinterpret_cast<float*>(smem + L.table());
+    float* sc = reinterpret_cast<float*>(smem + L.score());
+    int32_t* par = reinterpret_cast<int32_t*>(smem + L.parent());
+    int32_t* rk = reinterpret_cast<int32_t*>(smem + L.rank());
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const size_t rows = (size_t)(N + 1) * K;
+
+    const float* g_lp = a.logp + (size_t)b * rows;
+    for (size_t x = lane; x < rows; x += kBuildThreads) lp[x] = g_lp[x];
+    for (int i = lane; i < N; i += kBuildThreads) {
+        par[i] = -1;
+        rk[i] = 0;
+        sc[i] = 0.0f;
+    }
+    __syncthreads();
+
+    int cur = 0, head = 0, len = 0;        // open candidates: lists[cur][head .. len)
+    int n = 0, e0 = -1, ne = 1;            // the nodes to expand: e0 .. e0 + ne - 1 (-1: the prefix)
+    for (;;) {
+        // 1. the expanded nodes' children, as keys, sorted descending
+        const int nc = ne * K, P = pow2_at_least(nc);
+        for (int x = lane; x < P; x += kBuildThreads) {
+            uint64_t key = 0;              // padding: below every candidate
+            if (x < nc) {
+                const int t = x / K, c = x - t * K;
+                const int p = e0 < 0 ? -1 : e0 + t;
+                const float base = p < 0 ? 0.0f : sc[p];
+                key = cand_key(base + lp[(size_t)(p + 1) * K + c], p, c);
+            }
+            ck[x] = key;
+        }
+        __syncthreads();
+        for (int k = 2; k <= P; k <<= 1)
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = lane; i < P; i += kBuildThreads) {
+                    const int ij = i ^ j;
+                    if (ij > i) {
+                        const uint64_t x = ck[i], y = ck[ij];
+                        const bool desc = (i & k) == 0;
+                        if (desc ? x < y : x > y) {
+                            ck[i] = y;
+                            ck[ij] = x;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        // 2. merge into the open list, keeping the best N - n
+        const int R = N - n;
+        const uint64_t* A = lists[cur] + head;
+        const int na = len - head;
+        uint64_t* out = lists[cur ^ 1];
+        for (int x = lane; x < na; x += kBuildThreads) {
+            const int pos = x + count_larger(ck, nc, A[x]);
+            if (pos < R) out[pos] = A[x];
+        }
+        for (int x = lane; x < nc; x += kBuildThreads) {
+            const int pos = x + count_larger(A, na, ck[x]);
+            if (pos < R) out[pos] = ck[x];
+        }
+        cur ^= 1;
+        head = 0;
+        len = min(na + nc, R);
+        __syncthreads();
+        // 3. the step: the best m open candidates become nodes n .. n + m - 1
+        const int m = min(min(w, R), len);
+        if (m == 0) break;                 // (never: every step adds K >= 1 candidates)
+        for (int t = lane; t < m; t += kBuildThreads) {
+            const uint64_t key = lists[cur][t];
+            sc[n + t] = bits_score((uint32_t)(key >> 32));
+            par[n + t] = key_parent(key);
+            rk[n + t] = key_rank(key);
+        }
+        __syncthreads();
+        e0 = n;
+        ne = m;
+        head = m;
+        n += m;
+        if (n >= N) break;
+    }
+    // the tree, with each node's token from its parent's row
+    const int32_t* g_tok = a.tok + (size_t)b * rows;
+    for (int i = lane; i < N; i += kBuildThreads) {
+        const int p = par[i];
+        a.parent[(size_t)b * N + i] = p;
+        a.token[(size_t)b * N + i] = g_tok[(size_t)(p + 1) * K + rk[i]];
+        a.score[(size_t)b * N + i] = sc[i];
+    }
+}
+
+}  // namespace
+
+size_t tree_build_lds_bytes(int N, int K, int w) {
+    const int wn = w < N ? w : N;
+    return BuildLds(N, K, pow2_at_least(wn * K)).bytes();
+}
+
+hipError_t launch_tree_build(const BuildArgs& a, hipStream_t stream) {
+    const size_t lds = tree_build_lds_bytes(a.N, a.K, a.w);
+    if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute((const void*)tree_build_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    BuildArgs copy = a;
+    void* args[] = {&copy};
+    return hipLaunchKernel((const void*)tree_build_kernel, dim3((unsigned)a.B), dim3(kBuildThreads),
+                           args, lds, stream);
+}
+
+}  // namespace gdn

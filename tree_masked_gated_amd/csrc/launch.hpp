@@ -39,4 +39,17 @@ struct AcceptArgs {
 };
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
 
+// Draft-tree construction with w expansions per step, one wave per sequence.
+constexpr int kMaxBuildTopk = 64;   // continuations per drafter row
+struct BuildArgs {
+    int B, N, K, w;
+    const float* logp;        // [B][N + 1][K]
+    const int32_t* tok;       // [B][N + 1][K]
+    int32_t* parent;          // [B][N]
+    int32_t* token;           // [B][N]
+    float* score;             // [B][N]
+};
+size_t tree_build_lds_bytes(int N, int K, int w);
+hipError_t launch_tree_build(const BuildArgs& a, hipStream_t stream);
+
 }  // namespace gdn

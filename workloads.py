@@ -42,7 +42,7 @@ __all__ = [
     "Spec", "WORKLOADS", "spec", "bf16_bits", "bf16_to_f32", "io_to_f64",
     "tree_binary7", "tree_mary", "tree_chain", "tree_random_recursive",
     "tree_star", "leaves", "pick_leaf", "make_trees", "make_layer",
-    "draw_layer", "tree_sizes", "ragged_offsets", "pack_rows",
+    "draw_layer", "tree_sizes", "ragged_offsets", "pack_rows", "draft_scores",
 ]
 
 
@@ -304,6 +304,28 @@ def pack_rows(dense: np.ndarray, lens) -> np.ndarray:
     sequence after sequence into [sum(lens)][...]."""
     parts = [dense[b, :n] for b, n in enumerate(lens)]
     return np.ascontiguousarray(np.concatenate(parts, axis=0)) if parts else dense[:0, 0]
+
+
+# ---------------------------------------------------------------- drafter scores
+
+def draft_scores(rng: np.random.Generator, batch: int, n: int, k: int, vocab: int = 32000,
+                 sigma: float = 2.0):
+    """Synthetic drafter outputs for tree construction: for the prefix and each
+    of n node indices, the top-k continuations of a distribution over `vocab`
+    tokens whose k candidates have logits ln(vocab) + N(0, sigma^2) and whose
+    other vocab - k tokens have logit 0 (so the candidates hold most of the
+    mass, the best one typically well over half, as a confident drafter's
+    would).  Returns (logp [batch][n + 1][k] float32, descending per row; tok
+    [batch][n + 1][k] int32, distinct per row)."""
+    z = np.log(vocab) + rng.standard_normal((batch, n + 1, k)) * sigma
+    zmax = np.maximum(z.max(axis=-1, keepdims=True), 0.0)
+    denom = np.exp(z - zmax).sum(axis=-1, keepdims=True) + (vocab - k) * np.exp(-zmax)
+    logp = np.sort(z - zmax - np.log(denom), axis=-1)[..., ::-1].astype(np.float32)
+    tok = np.empty((batch, n + 1, k), dtype=np.int32)
+    for b in range(batch):
+        for r in range(n + 1):
+            tok[b, r] = rng.choice(vocab, size=k, replace=False)
+    return np.ascontiguousarray(logp), tok
 
 
 # ---------------------------------------------------------------- upload
