@@ -42,11 +42,13 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t s_mask[kPrepMaxN * WP];
     __shared__ int32_t s_jump[kPrepMaxN];
     __shared__ int s_flag;
+    __shared__ int s_more[3];                           // per-round "a link is left" flags, round r uses r % 3
     const int b = blockIdx.x, N = a.N, W = (N + 31) / 32, tid = threadIdx.x;
     const SeqRows rows = seq_rows(a.offsets, b, N);     // the cache keeps N rows per tree
     const int n = max(rows.n, 0);
     const int i = tid >> 1, hh = tid & 1;               // node, half row (words 8 hh .. +7)
     if (tid == 0) s_flag = 0x7fffffff;
+    if (tid < 3) s_more[tid] = 0;
     __syncthreads();
     if (hh == 0 && i < n) {
         const int p = a.parent[rows.row0 + i];
@@ -64,7 +66,11 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
     __syncthreads();
     const int status = rows.n < 0 ? -1 : s_flag == 0x7fffffff ? 0 : s_flag + 1;
     if (status == 0) {
-        for (;;) {
+        // Round r raises flag r % 3 while some node still has a link to follow
+        // and clears flag (r + 1) % 3 before its first barrier (the last
+        // readers of that flag finished two rounds earlier): two LDS-only
+        // barriers per round, no workgroup reduction.
+        for (int rd = 0;; ++rd) {
             const int j = i < n ? s_jump[i] : -1;
             uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
             int nj = -1;
@@ -74,7 +80,8 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
                 a1 = rj[1];
                 nj = s_jump[j];
             }
-            __syncthreads();
+            if (tid == 0) s_more[(rd + 1) % 3] = 0;
+            lds_barrier();
             if (j >= 0) {
                 uint4 r0 = row[0], r1 = row[1];
                 r0.x |= a0.x; r0.y |= a0.y; r0.z |= a0.z; r0.w |= a0.w;
@@ -83,7 +90,9 @@ __global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
                 row[1] = r1;
                 if (hh == 0) s_jump[i] = nj;
             }
-            if (!__syncthreads_or(j >= 0 && nj >= 0)) break;
+            if (j >= 0 && nj >= 0) s_more[rd % 3] = 1;
+            lds_barrier();
+            if (!s_more[rd % 3]) break;
         }
     }
     // strict rows (bit i cleared), zero for an invalid tree
@@ -151,6 +160,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     __shared__ __attribute__((aligned(16))) int32_t s_jump[NP];
     __shared__ unsigned long long s_occ[NB];    // bit s of row t: tile (t, s), s < t, not all zero
     __shared__ uint8_t s_tcol[NB][NB];          // row t's tiles: t, then its occupied blocks s < t, descending
+    __shared__ int s_more[3];                   // per-round "a link is left" flags of the gate doubling
     // k rows of blocks 0 .. KC-1 in MFMA operand order: (block s, chunk cs) is
     // 1 KB, lane l's 16 bytes at l * 16 (row 16 s + l % 16, columns 32 cs +
     // 8 (l / 16) .. +7), so a fragment read is one conflict-free ds_read_b128
@@ -201,6 +211,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         s_beta[i] = v ? a.beta[(rows.row0 + i) * Hv + h] : 0.f;
     }
     for (int t = tid; t < NB; t += NT) s_occ[t] = 0ull;
+    if (tid < 3) s_more[tid] = 0;
     __syncthreads();
     {
         // occupancy: OR of the ancestor words of block t's rows, word w covering
@@ -231,20 +242,25 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         kcr[r] = *reinterpret_cast<const u32x4*>(Kb + (size_t)row * kq_row + 32 * (u & 3) + 8 * lq);
     }
 
-    for (;;) {
+    // path log-gates by synchronous pointer doubling (each node adds its
+    // link's sum and jumps to the link's link); round r raises flag r % 3
+    // while a node still has a link to follow and clears flag (r + 1) % 3
+    // before its first barrier: two LDS-only barriers per round
+    for (int rd = 0;; ++rd) {
         constexpr int PER = NP / NT > 0 ? NP / NT : 1;
         int nn[PER];
         float gj[PER];
-        bool act = false;
+        bool more = false;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + k * NT;
             const int j = i < NP ? s_jump[i] : -1;
             nn[k] = j >= 0 ? s_jump[j] : -1;
             gj[k] = j >= 0 ? s_lg[j] : 0.f;
-            act |= j >= 0;
+            more |= nn[k] >= 0;
         }
-        __syncthreads();
+        if (tid == 0) s_more[(rd + 1) % 3] = 0;
+        lds_barrier();
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + k * NT;
@@ -253,7 +269,9 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 s_jump[i] = nn[k];
             }
         }
-        if (!__syncthreads_or(act)) break;
+        if (more) s_more[rd % 3] = 1;
+        lds_barrier();
+        if (!s_more[rd % 3]) break;
     }
     if (slice == 0)
         for (int i = tid; i < n; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
