@@ -78,6 +78,37 @@ def test_ragged_sizes(N):
     check_case(parent, accepted, lay, "bf16", 2, 4, name=f"ragged N={N}")
 
 
+def tree_of_depth(rng, n, depth):
+    """n nodes whose deepest node has exactly `depth` strict ancestors: a chain
+    of depth + 1 nodes, then each further node under a uniformly drawn
+    earlier node of depth < `depth` (depth 0: every node under the prefix)."""
+    parent = np.full(n, -1, np.int32)
+    dep = np.zeros(n, np.int64)
+    for i in range(1, n):
+        if i <= depth:
+            parent[i] = i - 1
+        else:
+            cand = np.flatnonzero(dep[:i] < depth)
+            parent[i] = rng.choice(cand) if depth > 0 else -1
+        dep[i] = dep[parent[i]] + 1 if parent[i] >= 0 else 0
+    assert dep.max() == min(depth, n - 1)
+    return parent
+
+
+@pytest.mark.parametrize("N", [200, 300])
+def test_large_tree_depths(N):
+    """The larger-tree path (a separate tree launch and a solve launch, both
+    building by pointer doubling whose round count follows the deepest
+    path) at depths on either side of powers of two, up to a chain."""
+    rng = np.random.default_rng(900 + N)
+    depths = [0, 1, 2, 3, 4, 7, 8, 9, 15, 16, 17, 63, 64, 65, 128, N - 1]
+    parents = [tree_of_depth(rng, N, dd) for dd in depths]
+    parent, lay = custom(901 + N, parents, 1, 2, 128)
+    # accept node `depth`, the end of the chain: the longest committed path
+    accepted = np.array(depths, np.int32)
+    check_case(parent, accepted, lay, "bf16", 1, 2, name=f"depths N={N}")
+
+
 @pytest.mark.parametrize("d,io", [(16, "f32"), (16, "bf16"), (128, "f32"), (64, "bf16"),
                                   (32, "f32")])
 def test_head_sizes(d, io):
