@@ -34,6 +34,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
     __shared__ int32_t s_cnt[kMaxNodes];
     __shared__ int32_t s_ok[kMaxNodes];
     __shared__ int s_bad, s_best;
+    __shared__ int s_more[3];                     // per-round "a link is left" flags, round r uses r % 3
     const int b = blockIdx.x, tid = threadIdx.x;
     const SeqRows rows = seq_rows(a.offsets, b, a.N);
     const int N = max(rows.n, 0);                   // this tree's nodes
@@ -45,6 +46,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
         s_bad = 0;
         s_best = -1;
     }
+    if (tid < 3) s_more[tid] = 0;
     int p[kAcceptPer], d[kAcceptPer];
 #pragma unroll
     for (int k = 0; k < kAcceptPer; ++k) {
@@ -85,9 +87,13 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
             }
         }
         __syncthreads();
-        for (;;) {                                       // 2. AND over the ancestors
+        // 2. AND over the ancestors.  Round r raises flag r % 3 while some node
+        // still has a link to follow and clears flag (r + 1) % 3 before its
+        // first barrier (the last readers of that flag finished two rounds
+        // earlier): two LDS-only barriers per round, no workgroup reduction.
+        for (int rd = 0;; ++rd) {
             int ok[kAcceptPer], cnt[kAcceptPer], nj[kAcceptPer];
-            bool act = false;
+            bool more = false;
 #pragma unroll
             for (int k = 0; k < kAcceptPer; ++k) {
                 const int i = tid + kAcceptThreads * k;
@@ -99,10 +105,11 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
                     ok[k] = s_ok[j];
                     cnt[k] = s_cnt[j];
                     nj[k] = s_jump[j];
-                    act = true;
+                    more |= nj[k] >= 0;
                 }
             }
-            __syncthreads();
+            if (tid == 0) s_more[(rd + 1) % 3] = 0;
+            lds_barrier();
 #pragma unroll
             for (int k = 0; k < kAcceptPer; ++k) {
                 const int i = tid + kAcceptThreads * k;
@@ -112,7 +119,9 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(AcceptArgs a) {
                     s_jump[i] = nj[k];
                 }
             }
-            if (!__syncthreads_or(act)) break;
+            if (more) s_more[rd % 3] = 1;
+            lds_barrier();
+            if (!s_more[rd % 3]) break;
         }
         int best = -1;                                   // 3. the deepest node on the walk
 #pragma unroll
