@@ -203,3 +203,17 @@ def test_fused_other_sizes(N, d, io):
     accs = [[W.pick_leaf(rng, p[0]), N - 1] for p in ps]
     steps = chain_steps(98 + N, ps, accs, 1, 2, d, io)
     run_case(f"other N={N} d={d}", steps, io, 1, 2)
+
+
+def test_fused_full_batch_shape():
+    """The benchmark's launch configuration: 64 sequences of 8-ary, 16-deep
+    trees (128 nodes), 16 key / 32 value heads, d = 128, so that the persistent
+    fused launch takes four items per workgroup and every item hand-off (the
+    next item's S rows, k / q rows and previous-tree path read ahead) runs.
+    Three decode steps, every (sequence, value head) unit compared."""
+    rng = np.random.default_rng(97)
+    B, M, depth = 64, 8, 16
+    ps = [[W.tree_mary(rng, M, depth) for _ in range(B)] for _ in range(3)]
+    accs = [[W.pick_leaf(rng, p) for p in pp] for pp in ps]
+    steps = chain_steps(98, ps, accs, 16, 32, 128)
+    run_case("full batch", steps, "bf16", 16, 32)
