@@ -287,17 +287,30 @@ def test_ragged_fused_decode_loop():
     """Three decode steps whose trees change size from step to step, each step
     one fused commit (previous tree) + verify (new tree) call, against the
     oracle chained per sequence; and against the same loop as two calls."""
+    fused_loop_case(360, 128, 1, 2, 128,
+                    [[128, 64, 0, 33, 100], [16, 128, 77, 0, 1], [64, 64, 64, 64, 64]])
+
+
+def test_ragged_fused_full_batch():
+    """The same loop in the ragged benchmark's launch configuration: 64
+    sequences with trees of 16 .. 128 nodes, 16 key / 32 value heads, so the
+    persistent fused launch takes several items per workgroup."""
+    rng = np.random.default_rng(365)
+    sizes = [[int(x) for x in rng.integers(16, 129, 64)] for _ in range(3)]
+    fused_loop_case(366, 128, 16, 32, 128, sizes)
+
+
+def fused_loop_case(seed, N, Hk, Hv, d, sizes):
     import torch
     import oracle
     import tree_masked_gated_amd as T
-    rng = np.random.default_rng(360)
-    N, Hk, Hv, d, B = 128, 1, 2, 128, 5
-    sizes = [[128, 64, 0, 33, 100], [16, 128, 77, 0, 1], [64, 64, 64, 64, 64]]
+    rng = np.random.default_rng(seed)
+    B = len(sizes[0])
     steps = []
     for st, sz in enumerate(sizes):
         trees = mixed_trees(rng, N, sz)
         acc = [W.pick_leaf(rng, p) if len(p) else -1 for p in trees]
-        steps.append(build_case(370 + st, trees, N, Hk, Hv, d, accepted=acc, extra_rows=1))
+        steps.append(build_case(seed + 10 + st, trees, N, Hk, Hv, d, accepted=acc, extra_rows=1))
     # every step starts from the first step's S0, carried forward
     dims = T.dims(B, N, Hk, Hv, d, d, "bf16")
     dev = lambda a, x="": W.to_device(a, x)
