@@ -295,8 +295,12 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
 #pragma unroll
         for (int tc = 0; tc < 8; ++tc) D[tc] *= dec;
         // staging: path node m of the chunk, key columns kseg .. +15 and value
-        // rows useg .. +7 of this half
-        const int m = tid >> 3, kseg = (tid & 7) * 16, useg = (tid & 7) * 8;
+        // rows useg .. +7 of this half.  Consecutive lanes take consecutive
+        // nodes, so each transposed 2-byte store of a wave covers one 64-byte
+        // run of a row (and a second row's run) rather than eight rows that
+        // share one LDS bank.
+        const int m = tid & 31, kseg = (tid >> 5) * 16, useg = (tid >> 5) * 8;
+        static_assert(kThreads == 32 * 8 && kMfmaChunk == 32, "32 nodes x 8 column segments");
         // chunk loads, unconditional (rows past the path re-read its last node
         // with weight 0), issued one chunk ahead of their use
         u32x4 k0, k1;
