@@ -230,12 +230,13 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_d128(CommitArgs a) {
 // owns value-row tile w of its half and all eight key-column tiles: 8
 // accumulator tiles whose lanes hold 4 consecutive key columns of one value
 // row, i.e. 16 contiguous bytes of S, so S_in loads and S_out stores stay
-// row-major.  The path is consumed 32 nodes at a time: its k rows and its
-// weighted u rows (split into bf16 hi + lo, about 16 mantissa bits, so the
-// update keeps fp32-level accuracy) are staged transposed in LDS, each MFMA
-// operand one 16-byte read, the next chunk's loads issued before the current
-// chunk's products.
-constexpr int kMfmaChunk = 32;
+// row-major.  The path is consumed 64 nodes at a time (a chunk's loads are
+// one HBM round trip, so fewer, larger chunks): its k rows and its weighted
+// u rows (split into bf16 hi + lo, about 16 mantissa bits, so the update
+// keeps fp32-level accuracy) are staged transposed in LDS, each MFMA operand
+// one 16-byte read, the next chunk's loads issued before the current chunk's
+// products.
+constexpr int kMfmaChunk = 64;
 constexpr int kMfmaHalves = 2;                       // value-row halves per (b, h)
 constexpr int kHalfRows = kFastD / kMfmaHalves;
 
@@ -294,27 +295,28 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
         const float dec = __expf(ga);
 #pragma unroll
         for (int tc = 0; tc < 8; ++tc) D[tc] *= dec;
-        // staging: path node m of the chunk, key columns kseg .. +15 and value
-        // rows useg .. +7 of this half.  Consecutive lanes take consecutive
-        // nodes, so each transposed 2-byte store of a wave covers one 64-byte
-        // run of a row (and a second row's run) rather than eight rows that
-        // share one LDS bank.
-        const int m = tid & 31, kseg = (tid >> 5) * 16, useg = (tid >> 5) * 8;
-        static_assert(kThreads == 32 * 8 && kMfmaChunk == 32, "32 nodes x 8 column segments");
+        // staging: path node m of the chunk, key columns kseg .. +31 and value
+        // rows useg .. +15 of this half.  The lanes of a wave take the chunk's
+        // 64 nodes in order, so each transposed 2-byte store of a wave fills
+        // one 128-byte row of the staging tile (no two lanes in one bank but
+        // the two halves of a 4-byte word).
+        const int m = tid & 63, kseg = (tid >> 6) * 32, useg = (tid >> 6) * 16;
+        static_assert(kThreads == 64 * 4 && kMfmaChunk == 64 && kHalfRows == 4 * 16,
+                      "64 nodes x 4 column segments");
         // chunk loads, unconditional (rows past the path re-read its last node
         // with weight 0), issued one chunk ahead of their use
-        u32x4 k0, k1;
-        float4 u4[2];
+        u32x4 kv[4];
+        float4 u4[4];
         float lgj;
         auto load_chunk = [&](int p0) {
             const int pn = min(kMfmaChunk, plen - p0);
             const int j = s_idx[p0 + min(m, pn - 1)];
             const uint16_t* kr = K + ((rows.row0 + j) * a.Hk + hk) * kFastD + kseg;
-            k0 = *reinterpret_cast<const u32x4*>(kr);
-            k1 = *reinterpret_cast<const u32x4*>(kr + 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kv[i] = *reinterpret_cast<const u32x4*>(kr + 8 * i);
             const float* ur = U + (size_t)j * kFastD + r0 + useg;
-            u4[0] = *reinterpret_cast<const float4*>(ur);
-            u4[1] = *reinterpret_cast<const float4*>(ur + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u4[i] = *reinterpret_cast<const float4*>(ur + 4 * i);
             lgj = lg[j];
         };
         load_chunk(0);
@@ -322,15 +324,14 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
             lds_barrier();                             // the previous chunk's operands are consumed
             {
                 const float w = m < plen - p0 ? __expf(ga - lgj) : 0.f;
-                const float uv[8] = {u4[0].x, u4[0].y, u4[0].z, u4[0].w, u4[1].x, u4[1].y, u4[1].z, u4[1].w};
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const uint32_t kw = (e < 8 ? k0[e >> 1] : k1[(e - 8) >> 1]) >> (16 * (e & 1));
+                for (int e = 0; e < 32; ++e) {
+                    const uint32_t kw = kv[e >> 3][(e >> 1) & 3] >> (16 * (e & 1));
                     s_kT[(kseg + e) * kMfmaChunk + m] = (uint16_t)(kw & 0xffffu);
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = w * uv[e];
+                for (int e = 0; e < 16; ++e) {
+                    const float x = w * u4[e >> 2][e & 3];
                     const uint16_t hi = __builtin_bit_cast(uint16_t, (__bf16)x);
                     const uint16_t lo = __builtin_bit_cast(uint16_t, (__bf16)(x - __uint_as_float((uint32_t)hi << 16)));
                     s_uhT[(useg + e) * kMfmaChunk + m] = hi;
@@ -340,15 +341,23 @@ __global__ __launch_bounds__(kThreads) void commit_kernel_mfma(CommitArgs a) {
             // (LDS-only barriers: the loads just issued stay in flight over them)
             if (p0 + kMfmaChunk < plen) load_chunk(p0 + kMfmaChunk);
             lds_barrier();
-            const int off = (16 * wave + ln) * kMfmaChunk + 8 * lq;
-            const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_uhT + off));
-            const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_ulT + off));
+            // two K = 32 halves of the chunk per accumulator tile (the second
+            // only when the chunk holds more than 32 nodes: short paths)
+            const int pn = min(kMfmaChunk, plen - p0);
 #pragma unroll
-            for (int tc = 0; tc < 8; ++tc) {
-                const bf16x8 ak = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(s_kT + (16 * tc + ln) * kMfmaChunk + 8 * lq));
-                D[tc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bh, D[tc], 0, 0, 0);
-                D[tc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bl, D[tc], 0, 0, 0);
+            for (int hf = 0; hf < kMfmaChunk / 32; ++hf) {
+                if (32 * hf >= pn) break;                  // uniform
+                const int off = (16 * wave + ln) * kMfmaChunk + 32 * hf + 8 * lq;
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_uhT + off));
+                const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_ulT + off));
+#pragma unroll
+                for (int tc = 0; tc < 8; ++tc) {
+                    const bf16x8 ak = __builtin_bit_cast(
+                        bf16x8,
+                        *reinterpret_cast<const u32x4*>(s_kT + (16 * tc + ln) * kMfmaChunk + 32 * hf + 8 * lq));
+                    D[tc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bh, D[tc], 0, 0, 0);
+                    D[tc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bl, D[tc], 0, 0, 0);
+                }
             }
         }
     }
