@@ -343,10 +343,10 @@ def cpu_baseline(s, budget_s):
 
 # ---------------------------------------------------------------- copy
 
-def copy_calibration(mib):
+def copy_bandwidth(mib):
     """A plain device-to-device copy of a known size (torch's copy kernel): the
     reference for scaling FETCH_SIZE / WRITE_SIZE counters and the achievable
-    streaming bandwidth on this machine."""
+    streaming bandwidth on this machine.  Returns what it measured."""
     import torch
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -363,8 +363,10 @@ def copy_calibration(mib):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
     moved = 2 * n * 4
-    print(json.dumps({"copy_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4,
-                      "us_per_copy": ms * 1e3, "GBs": moved / (ms * 1e-3) / 1e9}), flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4,
+            "us_per_copy": ms * 1e3, "GBs": moved / (ms * 1e-3) / 1e9}
 
 
 # ---------------------------------------------------------------- traffic
@@ -405,7 +407,7 @@ def main():
                     help="verify and commit as two launches per layer")
     args = ap.parse_args()
     if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
+        print(json.dumps(copy_bandwidth(args.copy_calibration)), flush=True)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -429,6 +431,9 @@ def main():
         kernel = "verify"
         vb = r["verify_bytes"]
     achieved = vb / (launch_ms * 1e-3) / 1e9
+    # what plain streaming reaches here: 1 GiB read + 1 GiB written, after the
+    # timed region
+    copy_gbs = copy_bandwidth(1024)["GBs"]
     base = None
     if args.cpu_budget > 0:
         log("timing the oracle on the host")
@@ -461,6 +466,7 @@ def main():
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": profiled_traffic(kernel, s.name), "alg_bytes_per_launch": vb,
             "launch_us": launch_ms * 1e3,
+            "copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
         },
         "verify": {
             "launch_us": r["verify_ms"] * 1e3, "alg_bytes_per_launch": r["verify_bytes"],

@@ -66,7 +66,7 @@ def custom(seed, parents, Hk, Hv, d, io="bf16", beta_mu=0.0):
     return parent, lay
 
 
-RAGGED = [1, 2, 33, 37, 64, 100, 127, 129, 200, 255, 256, 257, 300, 512, 513]
+RAGGED = [1, 2, 33, 37, 64, 100, 127, 129, 200, 255, 256, 257, 300, 512, 513, 1000, 1024]
 
 
 @pytest.mark.parametrize("N", RAGGED)

@@ -210,8 +210,10 @@ size_t verify_generic_lds_bytes(int N) { return (size_t)GenericLds(N).words() * 
 
 hipError_t launch_verify_generic(const VerifyArgs& a, int io, hipStream_t stream) {
     const size_t lds = verify_generic_lds_bytes(a.N);
-    // dynamic LDS plus the kernel's ~1.1 KB of static LDS must fit 160 KiB
-    if (lds + 2048 > (size_t)kMaxLds) return hipErrorInvalidValue;
+    // dynamic LDS plus the kernel's static LDS (two flags, s_part, s_acc:
+    // 2056 bytes) must fit 160 KiB; 1024 nodes take 159748 + 2056
+    constexpr size_t kStaticLds = 2 * sizeof(int) + kThreads * sizeof(int) + kMaxHead * sizeof(float);
+    if (lds + kStaticLds > (size_t)kMaxLds) return hipErrorInvalidValue;
     const void* fn = io == GDN_BF16 ? (const void*)verify_generic_kernel<GDN_BF16>
                                     : (const void*)verify_generic_kernel<GDN_F32>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
