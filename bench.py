@@ -233,7 +233,9 @@ def run_gpu(args, s):
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
-    live_ms = sum(a.elapsed_time(b) for a, b in marks) / (len(marks) * L)
+    per_step = sorted(a.elapsed_time(b) / L for a, b in marks)
+    live_ms = sum(per_step) / len(per_step)
+    live_med_ms = per_step[len(per_step) // 2]
     log(f"timed {args.steps} steps: {total_ms:.3f} ms; dominant launch {live_ms * 1e3:.1f} us in the timed region")
 
     # per-kernel averages, same stream, same launch configuration
@@ -264,7 +266,7 @@ def run_gpu(args, s):
     build = time_tree_build(s, stream, reps)
     return {
         "total_ms": total_ms, "verify_ms": verify_ms, "commit_ms": commit_ms,
-        "fused_ms": fused_ms, "accept_ms": accept_ms, "live_ms": live_ms,
+        "fused_ms": fused_ms, "accept_ms": accept_ms, "live_ms": live_ms, "live_med_ms": live_med_ms,
         "verify_bytes": verify_bytes(s, e, sizes),
         "commit_bytes": commit_bytes(s, e, path_lens, sizes),
         "path_lens": path_lens, "parent": parent, "accepted": accepted, "sizes": sizes,
@@ -466,6 +468,7 @@ def main():
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": profiled_traffic(kernel, s.name), "alg_bytes_per_launch": vb,
             "launch_us": launch_ms * 1e3,
+            "launch_us_median_step": r["live_med_ms"] * 1e3,
             "copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
         },
         "verify": {
