@@ -118,15 +118,6 @@ __device__ __forceinline__ float quad_bcast(float x, int k) {
     }
 }
 
-// A/B fragment of a 16-node block of k or q straight from global memory: lane
-// l gets row 16 blk + l % 16 (clamped to N - 1), columns 32 cs + 8 (l / 16)..+7.
-__device__ __forceinline__ bf16x8 g_frag(const uint16_t* base, size_t row_stride, int blk,
-                                         int cs, int lane, int N) {
-    const int row = min(16 * blk + (lane & 15), N - 1);
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                          base + (size_t)row * row_stride + 32 * cs + 8 * (lane >> 4)));
-}
-
 // Waves 0 .. NS-1 solve: wave w owns value columns 64 slice + 32 w .. +31 as
 // two 16-column groups (two independent MFMA chains per product).  Waves NS ..
 // NS+NG-1 are Gram waves: they compute the next block row's tiles and (the
@@ -160,14 +151,18 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     __shared__ __attribute__((aligned(16))) int32_t s_jump[NP];
     __shared__ unsigned long long s_occ[NB];    // bit s of row t: tile (t, s), s < t, not all zero
     __shared__ uint8_t s_tcol[NB][NB];          // row t's tiles: t, then its occupied blocks s < t, descending
-    __shared__ int s_more[3];                   // per-round "a link is left" flags of the gate doubling
+    __shared__ int s_more[9];                   // per-round flags of the three doubling loops (3 each)
+    // the node order the kernel works in: a preorder (every subtree one run of
+    // positions), position -> node, and each position's last descendant
+    __shared__ uint16_t s_perm[NP];
+    __shared__ __attribute__((aligned(8))) int16_t s_last[NP];
+    __shared__ int s_mlast[NB];                 // largest s_last of each 16-position block
     // k rows of blocks 0 .. KC-1 in MFMA operand order: (block s, chunk cs) is
     // 1 KB, lane l's 16 bytes at l * 16 (row 16 s + l % 16, columns 32 cs +
     // 8 (l / 16) .. +7), so a fragment read is one conflict-free ds_read_b128
     __shared__ __attribute__((aligned(16))) uint16_t s_kc[KC * 4 * 512];
 
     const int N = a.N, Hv = a.Hv, Hk = a.Hk, G = Hv / Hk;
-    const int W = (N + 31) / 32;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool solver = wave < NS;
@@ -202,43 +197,167 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + (rows.row0 * Hk + hk) * kD;
     const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + (rows.row0 * Hk + hk) * kD;
     const size_t kq_row = (size_t)Hk * kD;
-    // ---- path log-gates G (synchronous pointer doubling), beta, occupancy ----
-    const uint32_t* gmask = a.anc_mask + (size_t)b * N * W;
+    // ---- a preorder of the tree, path log-gates G, beta, tile occupancy ----
+    // In a preorder (children in index order) j is a strict ancestor of i
+    // exactly when j < i <= last(j), last(j) the position of j's last
+    // descendant, so a block row's ancestors sit in few column blocks (a
+    // random tree's rows touch most blocks in the caller's order) and the
+    // tile masks need no ancestor rows.  Outputs stay in the caller's order.
+    // Scratch while it is built: the X / Y row buffers.
+    constexpr int WC = NP / 32;                         // words of a children row
+    constexpr int PER = NP / NT > 0 ? NP / NT : 1;
+    uint32_t* s_cm = reinterpret_cast<uint32_t*>(&s_xrow[0][0]);  // [NP + 1][WC]; row NP: the roots
+    int32_t* s_fc = reinterpret_cast<int32_t*>(&s_yrow[0][0]);    // [NP + 1] first child, -1: none
+    int32_t* s_nx = s_fc + (NP + 1);                    // [NP] node after the subtree (n: none; -1 pending)
+    int32_t* s_ptr = s_nx + NP;                         // [NP] doubling link
+    int32_t* s_rk = s_ptr + NP;                         // [NP] list distance to the last node
+    int32_t* s_sc = s_rk + NP;                          // [NP] list link (n: past the last node)
+    static_assert((NP + 1) * WC * 4 <= sizeof(s_xrow) && (5 * NP + 1) * 4 <= sizeof(s_yrow),
+                  "preorder scratch fits the row buffers");
+    bool not_chain = false;                             // a chain is its own preorder
     for (int i = tid; i < NP; i += NT) {
         const bool v = i < n;
-        s_jump[i] = v ? a.parent[rows.row0 + i] : -1;
+        const int p = v ? a.parent[rows.row0 + i] : -1;
+        not_chain |= v && p != i - 1;
+        s_jump[i] = p;
         s_lg[i] = v ? logf(a.g[(rows.row0 + i) * Hv + h]) : 0.f;
         s_beta[i] = v ? a.beta[(rows.row0 + i) * Hv + h] : 0.f;
+        s_perm[i] = (uint16_t)min(i, max(n - 1, 0));
+        s_last[i] = v ? (int16_t)(n - 1) : (int16_t)-1;
     }
-    for (int t = tid; t < NB; t += NT) s_occ[t] = 0ull;
-    if (tid < 3) s_more[tid] = 0;
+    for (int x = tid; x < (NP + 1) * WC; x += NT) s_cm[x] = 0u;
+    if (tid < 9) s_more[tid] = 0;
+    // a chain skips the construction (nt = 0): the identity and last = n - 1
+    const int nt = __syncthreads_or(not_chain) ? n : 0;
+    for (int i = tid; i < nt; i += NT) {                // bit i of its parent's children row
+        const int p = s_jump[i];
+        atomicOr(&s_cm[(p < 0 ? NP : p) * WC + (i >> 5)], 1u << (i & 31));
+    }
     __syncthreads();
-    {
-        // occupancy: OR of the ancestor words of block t's rows, word w covering
-        // column blocks 2w and 2w + 1 (the 16 row loads issued together)
-        for (int x = tid; x < nblk * W; x += NT) {
-            const int t = x / W, w = x % W;
-            uint32_t r[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) r[i] = gmask[(size_t)min(16 * t + i, N - 1) * W + w];
-            uint32_t acc = 0;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc |= r[i];
-            const unsigned long long bits = ((acc & 0xffffu) ? 1ull << (2 * w) : 0ull) |
-                                            ((acc >> 16) ? 1ull << (2 * w + 1) : 0ull);
-            if (bits) atomicOr(&s_occ[t], bits);
+    for (int v = tid; v <= NP; v += NT) {               // first child (row NP: the first root)
+        int f = -1;
+        if (v < nt || v == NP)
+            for (int w = 0; w < WC; ++w) {
+                const uint32_t x = s_cm[v * WC + w];
+                if (x) {
+                    f = 32 * w + __builtin_ctz(x);
+                    break;
+                }
+            }
+        s_fc[v] = f;
+    }
+    for (int i = tid; i < nt; i += NT) {                // next sibling, else pending
+        const int p = s_jump[i];
+        const uint32_t* r = s_cm + (p < 0 ? NP : p) * WC;
+        int nsib = -1;
+        uint32_t x = r[i >> 5] & ~((2u << (i & 31)) - 1u);   // siblings above i in its word
+        for (int w = i >> 5;;) {
+            if (x) {
+                nsib = 32 * w + __builtin_ctz(x);
+                break;
+            }
+            if (++w >= WC) break;
+            x = r[w];
         }
+        s_nx[i] = nsib >= 0 ? nsib : (p < 0 ? n : -1);
+        s_ptr[i] = p;
+    }
+    __syncthreads();
+    // the node after a subtree: the subtree root's next sibling, else its
+    // parent's (pointer doubling up the path; a root-level node always has one)
+    for (int rd = 0;; ++rd) {
+        int res[PER], nq[PER];
+        bool more = false;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + k * NT;
+            res[k] = -2;
+            nq[k] = 0;
+            if (i < nt && s_nx[i] < 0) {
+                const int q = s_ptr[i];
+                const int rq = s_nx[q];
+                if (rq >= 0) res[k] = rq;
+                else {
+                    nq[k] = s_ptr[q];
+                    res[k] = -1;
+                    more = true;
+                }
+            }
+        }
+        if (tid == 0) s_more[(rd + 1) % 3] = 0;
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + k * NT;
+            if (res[k] >= 0) s_nx[i] = res[k];
+            else if (res[k] == -1) s_ptr[i] = nq[k];
+        }
+        if (more) s_more[rd % 3] = 1;
+        lds_barrier();
+        if (!s_more[rd % 3]) break;
+    }
+    for (int i = tid; i < nt; i += NT) {                // preorder successor: first child, else the node after
+        const int f = s_fc[i];
+        const int sc = f >= 0 ? f : s_nx[i];
+        s_sc[i] = sc;
+        s_rk[i] = sc < n ? 1 : 0;
+    }
+    __syncthreads();
+    for (int rd = 0;; ++rd) {                           // list ranking by pointer doubling
+        int nr[PER], ns[PER];
+        bool more = false;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + k * NT;
+            nr[k] = -1;
+            ns[k] = n;
+            if (i < nt) {
+                const int sc = s_sc[i];
+                if (sc < n) {
+                    nr[k] = s_rk[i] + s_rk[sc];
+                    ns[k] = s_sc[sc];
+                    more |= ns[k] < n;
+                }
+            }
+        }
+        if (tid == 0) s_more[3 + (rd + 1) % 3] = 0;
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + k * NT;
+            if (nr[k] >= 0) {
+                s_rk[i] = nr[k];
+                s_sc[i] = ns[k];
+            }
+        }
+        if (more) s_more[3 + rd % 3] = 1;
+        lds_barrier();
+        if (!s_more[3 + rd % 3]) break;
+    }
+    for (int i = tid; i < nt; i += NT) {                // position n - 1 - rank
+        const int pi = min(max(n - 1 - s_rk[i], 0), n - 1);
+        const int nx = s_nx[i];
+        s_perm[pi] = (uint16_t)i;
+        s_last[pi] = (int16_t)((nx < n ? n - 1 - s_rk[nx] : n) - 1);
+    }
+    __syncthreads();
+    auto node_at = [&](int pos) __attribute__((always_inline)) {   // position (clamped) -> node
+        return min((int)s_perm[min(pos, n - 1)], n - 1);
+    };
+    for (int sb = tid; sb < NB; sb += NT) {
+        int m = -1;
+        for (int e = 0; e < 16; ++e) m = max(m, (int)s_last[16 * sb + e]);
+        s_mlast[sb] = m;
     }
     // k rows of the cached blocks into registers (1 KB unit wave + 8 r: block
     // u / 4, chunk u % 4), written to LDS once the tree's gates are summed, so
-    // the loads overlap that work; issued after the loads waited on above
-    // (loads retire in order).  Rows clamped to n - 1.
+    // the loads overlap that work.  Positions clamped to n - 1.
     constexpr int KCR = KC * 4 / (NT / 64);             // units per wave
     u32x4 kcr[KCR];
 #pragma unroll
     for (int r = 0; r < KCR; ++r) {
         const int u = wave + (NT / 64) * r;
-        const int row = min(16 * (u >> 2) + ln, n - 1);
+        const int row = node_at(16 * (u >> 2) + ln);
         kcr[r] = *reinterpret_cast<const u32x4*>(Kb + (size_t)row * kq_row + 32 * (u & 3) + 8 * lq);
     }
 
@@ -247,7 +366,6 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     // while a node still has a link to follow and clears flag (r + 1) % 3
     // before its first barrier: two LDS-only barriers per round
     for (int rd = 0;; ++rd) {
-        constexpr int PER = NP / NT > 0 ? NP / NT : 1;
         int nn[PER];
         float gj[PER];
         bool more = false;
@@ -259,7 +377,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             gj[k] = j >= 0 ? s_lg[j] : 0.f;
             more |= nn[k] >= 0;
         }
-        if (tid == 0) s_more[(rd + 1) % 3] = 0;
+        if (tid == 0) s_more[6 + (rd + 1) % 3] = 0;
         lds_barrier();
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
@@ -269,18 +387,37 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 s_jump[i] = nn[k];
             }
         }
-        if (more) s_more[rd % 3] = 1;
+        if (more) s_more[6 + rd % 3] = 1;
         lds_barrier();
-        if (!s_more[rd % 3]) break;
+        if (!s_more[6 + rd % 3]) break;
     }
     if (slice == 0)
         for (int i = tid; i < n; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
 
-    // tile lists (occupancy complete): the diagonal, then the occupied blocks
-    // in descending order, so the blocks past the LDS k cache come first and
-    // get the prefetched slots
-    for (int t = tid; t < nblk; t += NT) {
-        unsigned long long occ = s_occ[t] & ((1ull << t) - 1ull);
+    // G and beta by position (through the scratch: the row buffers are free)
+    {
+        float* tl = reinterpret_cast<float*>(&s_yrow[0][0]);
+        float* tb = tl + NP;
+        for (int i = tid; i < NP; i += NT) {
+            const int v = node_at(i);
+            tl[i] = i < n ? s_lg[v] : 0.f;
+            tb[i] = i < n ? s_beta[v] : 0.f;
+        }
+        __syncthreads();
+        for (int i = tid; i < NP; i += NT) {
+            s_lg[i] = tl[i];
+            s_beta[i] = tb[i];
+        }
+    }
+    // occupancy: tile (t, s), s < t, holds an ancestor pair exactly when a
+    // position of block s has its subtree reaching row t; tile lists: the
+    // diagonal, then the occupied blocks in descending order, so the blocks
+    // past the LDS k cache come first and get the prefetched slots
+    for (int t = tid; t < NB; t += NT) {
+        unsigned long long occ = 0ull;
+        for (int sb = 0; sb < t && t < nblk; ++sb)
+            if (s_mlast[sb] >= 16 * t) occ |= 1ull << sb;
+        s_occ[t] = occ;
         s_tcol[t][0] = (uint8_t)t;
         for (int m = 1; occ; ++m) {
             const int hb = 63 - __clzll((long long)occ);
@@ -321,7 +458,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         // offset (rows clamped to n - 1)
         const uint32_t lane_col = 16u * lq;                 // bytes: 8 bf16 per lane group
         auto frag = [&](const uint16_t* base, int blk, int cs) __attribute__((always_inline)) {
-            const uint32_t row = (uint32_t)min(16 * blk + ln, n - 1);
+            const uint32_t row = (uint32_t)node_at(16 * blk + ln);
             const uint32_t off = row * (uint32_t)(kq_row * 2) + lane_col + 64u * cs;
             return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                   reinterpret_cast<const char*>(base) + off));
@@ -341,10 +478,15 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         // the products masked and decayed into -X / Y (bf16, tile layout) in the
         // row buffers of parity t & 1; for s == t the diagonal X block in fp32,
         // transposed, for the inversion
-        auto tile_store = [&](int t, int s, f32x4 A, f32x4 C, uint32_t mword) __attribute__((always_inline)) {
+        auto tile_store = [&](int t, int s, f32x4 A, f32x4 C) __attribute__((always_inline)) {
             const int par = t & 1;
             const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
-            const uint32_t bits = i < n ? (mword >> (j0 & 31)) & 15u : 0u;
+            const uint2 lw = *reinterpret_cast<const uint2*>(&s_last[j0]);     // last(j0 .. j0 + 3)
+            const int lst[4] = {(int)(int16_t)(lw.x & 0xffffu), (int)(int16_t)(lw.x >> 16),
+                                (int)(int16_t)(lw.y & 0xffffu), (int)(int16_t)(lw.y >> 16)};
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bits |= (i < n && j0 + e < i && i <= lst[e]) ? 1u << e : 0u;
             const float lgi = s_lg[i], bei = s_beta[i];
             const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[j0]);
             const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
@@ -407,7 +549,6 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             bf16x8 k[4], q[4];
         };
         bf16x8 kp[TPW][4];
-        uint32_t wp[TPW];
         auto load_kq = [&](RowOps& o, int t) __attribute__((always_inline)) {
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) {
@@ -424,8 +565,9 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
 #pragma unroll
                 for (int cs = 0; cs < 4; ++cs)
                     kp[i][cs] = sc >= KC ? frag(Kb, sc, cs) : *reinterpret_cast<const bf16x8*>(Kb);
+            } else {
+                (void)sc;
             }
-            wp[i] = gmask[(size_t)min(16 * t + ln, N - 1) * W + ((16 * sc + 4 * lq) >> 5)];
         };
         auto kc_frag = [&](int sblk, int cs) __attribute__((always_inline)) {
             return *reinterpret_cast<const bf16x8*>(s_kc + (min(sblk, KC - 1) * 4 + cs) * 512 + lane * 8);
@@ -442,7 +584,6 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 const unsigned long long occ = row_occ(tr), occn = row_occ(tn);
                 const int ntile = __popcll(occ) + 1, ntn = __popcll(occn) + 1;
                 f32x4 Ap[TPW], Cp[TPW];
-                uint32_t wc[TPW];
 #pragma unroll
                 for (int i = 0; i < TPW; ++i) {
                     const int m = gw + i * NG;
@@ -454,16 +595,14 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                         else ks[cs] = sc < KC ? kc_frag(sc, cs) : kp[i][cs];
                     }
                     tile_products(cur.k, cur.q, ks, Ap[i], Cp[i]);
-                    wc[i] = wp[i];
                 }
 #pragma unroll
                 for (int i = 0; i < TPW; ++i) load_tile(i, tn, occn, ntn);
 #pragma unroll
                 for (int i = 0; i < TPW; ++i) {
                     const int m = gw + i * NG;
-                    if (m < ntile) tile_store(tr, tile_col(tr, occ, m), Ap[i], Cp[i], wc[i]);
+                    if (m < ntile) tile_store(tr, tile_col(tr, occ, m), Ap[i], Cp[i]);
                 }
-                const int ii = min(16 * tr + ln, n - 1);
                 for (int m = gw + TPW * NG; m < ntile; m += NG) {
                     const int sc = tile_col(tr, occ, m);
                     bf16x8 k0[4];
@@ -471,7 +610,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                     for (int cs = 0; cs < 4; ++cs) k0[cs] = sc < KC ? kc_frag(sc, cs) : frag(Kb, sc, cs);
                     f32x4 A0, C0;
                     tile_products(cur.k, cur.q, k0, A0, C0);
-                    tile_store(tr, sc, A0, C0, gmask[(size_t)ii * W + ((16 * sc + 4 * lq) >> 5)]);
+                    tile_store(tr, sc, A0, C0);
                 }
                 // projections of row t + 1 for column group pg
                 if (pg >= 0) {
@@ -580,7 +719,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                         up[g][p] = stack_pair(ut, zero4);
                 }
             }
-            if (node < n) *reinterpret_cast<f32x4*>(Ug + (size_t)node * kD + c0 + 16 * g + 4 * lq) = UT;
+            if (node < n) *reinterpret_cast<f32x4*>(Ug + (size_t)node_at(node) * kD + c0 + 16 * g + 4 * lq) = UT;
         }
         // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T over occupied tiles
         f32x4 Oc[CG], Oc2[CG];
@@ -614,7 +753,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[g][m] + Oc[g][m];
                 const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
                 const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
-                *reinterpret_cast<uint2*>(O + vo_base + (size_t)node * vo_row + c0 + 16 * g + 4 * lq) =
+                *reinterpret_cast<uint2*>(O + vo_base + (size_t)node_at(node) * vo_row + c0 + 16 * g + 4 * lq) =
                     make_uint2(lo, hi);
             }
         }
@@ -625,7 +764,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     auto load_v = [&](int t, uint2 (&v)[CG]) __attribute__((always_inline)) {
 #pragma unroll
         for (int g = 0; g < CG; ++g)
-            v[g] = *reinterpret_cast<const uint2*>(Vp + (size_t)min(16 * t + ln, n - 1) * vo_row + 16 * g);
+            v[g] = *reinterpret_cast<const uint2*>(Vp + (size_t)node_at(16 * t + ln) * vo_row + 16 * g);
     };
     uint2 va[CG], vb[CG];
     load_v(0, va);
