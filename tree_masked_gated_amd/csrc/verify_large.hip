@@ -8,13 +8,16 @@
 //  - tree_prep_kernel, one workgroup per sequence, validates the parent row
 //    and writes the strict-ancestor bit rows, depth and status to the cache;
 //  - verify_large_kernel, one workgroup per (sequence, value head, column
-//    slice), walks the 16-node block rows t in order.  For each row it computes
-//    only the Gram tiles (t, s) whose nodes have an ancestor pair (a tile
-//    occupancy taken from the ancestor rows), spread over the waves, into an
-//    LDS row buffer (two of them, alternating); every wave runs the row's
-//    blocked substitution and output stage for its 16 value columns, two node
-//    blocks per MFMA.  Row t + 1's tiles are computed while row t is solved, so
-//    one barrier per row separates them.
+//    slice), relabels the tree's nodes in preorder (every subtree one run of
+//    positions, so ancestry is an interval test and a block row's ancestors
+//    sit in few column blocks) and walks the 16-position block rows t in
+//    order.  For each row it computes only the Gram tiles (t, s) that hold an
+//    ancestor pair, spread over the waves, into an LDS row buffer (two of
+//    them, alternating); the solve waves run the row's blocked substitution
+//    and output stage for their value columns, two blocks per MFMA.  Row
+//    t + 1's tiles are computed while row t is solved, so one barrier per row
+//    separates them.  Inputs are gathered and outputs written at the caller's
+//    node indices.
 // k / q rows are read from global memory (L2) straight into MFMA operand
 // registers, a row ahead of their use.
 #include "gdn_common.hpp"
