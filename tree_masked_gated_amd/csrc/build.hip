@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
     for (;;) {
         // 1. the expanded nodes' children, as keys, sorted descending
         const int nc = ne * K, P = pow2_at_least(nc);
-        for (int x = lane; x < P; x += kBuildThreads) {
+        auto child_key = [&](int x) {
             uint64_t key = 0;              // padding: below every candidate
             if (x < nc) {
                 const int t = x / K, c = x - t * K;
@@ -111,24 +111,42 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
                 const float base = p < 0 ? 0.0f : sc[p];
                 key = cand_key(base + lp[(size_t)(p + 1) * K + c], p, c);
             }
-            ck[x] = key;
-        }
-        __syncthreads();
-        for (int k = 2; k <= P; k <<= 1)
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int i = lane; i < P; i += kBuildThreads) {
-                    const int ij = i ^ j;
-                    if (ij > i) {
-                        const uint64_t x = ck[i], y = ck[ij];
-                        const bool desc = (i & k) == 0;
-                        if (desc ? x < y : x > y) {
-                            ck[i] = y;
-                            ck[ij] = x;
+            return key;
+        };
+        if (P <= kBuildThreads) {
+            // one key per lane, the same bitonic network in registers: the
+            // pair (i, i ^ j) keeps its larger key at i when block i & k
+            // runs descending, its smaller key otherwise
+            uint64_t key = child_key(lane);
+            for (int k = 2; k <= P; k <<= 1)
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    const uint32_t lo = __shfl_xor((unsigned int)key, j);
+                    const uint32_t hi = __shfl_xor((unsigned int)(key >> 32), j);
+                    const uint64_t other = ((uint64_t)hi << 32) | lo;
+                    const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+                    key = keep_max ? (key > other ? key : other) : (key < other ? key : other);
+                }
+            if (lane < P) ck[lane] = key;
+            __syncthreads();
+        } else {
+            for (int x = lane; x < P; x += kBuildThreads) ck[x] = child_key(x);
+            __syncthreads();
+            for (int k = 2; k <= P; k <<= 1)
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    for (int i = lane; i < P; i += kBuildThreads) {
+                        const int ij = i ^ j;
+                        if (ij > i) {
+                            const uint64_t x = ck[i], y = ck[ij];
+                            const bool desc = (i & k) == 0;
+                            if (desc ? x < y : x > y) {
+                                ck[i] = y;
+                                ck[ij] = x;
+                            }
                         }
                     }
+                    __syncthreads();
                 }
-                __syncthreads();
-            }
+        }
         // 2. merge into the open list, keeping the best N - n
         const int R = N - n;
         const uint64_t* A = lists[cur] + head;
