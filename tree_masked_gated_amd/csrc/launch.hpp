@@ -18,7 +18,7 @@ hipError_t launch_verify_tiled(const VerifyArgs& a, int io, hipStream_t stream);
 hipError_t launch_commit_verify_tiled(const VerifyArgs& a, const CommitArgs& c, int io, hipStream_t stream);
 
 // MFMA verification of larger trees: d_k = d_v = 128, bf16 io, 129 .. 512 nodes
-// (two launches: the tree's ancestor rows into the cache, then the solve).
+// (one launch: the tree check, its ancestor rows into the cache, the solve).
 bool verify_large_supported(const VerifyArgs& a, int io);
 hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream);
 

@@ -4,20 +4,19 @@
 // Same method as the small-tree kernel (page "Trees from Marginals:
 // Autoregressive drafting with factorized priors", section 3: the Gram matrix,
 // a tiled forward substitution and the output stage, fused), laid out for trees
-// whose k / q rows and interaction tiles no longer fit in LDS together:
-//  - tree_prep_kernel, one workgroup per sequence, validates the parent row
-//    and writes the strict-ancestor bit rows, depth and status to the cache;
-//  - verify_large_kernel, one workgroup per (sequence, value head, column
-//    slice), relabels the tree's nodes in preorder (every subtree one run of
-//    positions, so ancestry is an interval test and a block row's ancestors
-//    sit in few column blocks) and walks the 16-position block rows t in
-//    order.  For each row it computes only the Gram tiles (t, s) that hold an
-//    ancestor pair, spread over the waves, into an LDS row buffer (two of
-//    them, alternating); the solve waves run the row's blocked substitution
-//    and output stage for their value columns, two blocks per MFMA.  Row
-//    t + 1's tiles are computed while row t is solved, so one barrier per row
-//    separates them.  Inputs are gathered and outputs written at the caller's
-//    node indices.
+// whose k / q rows and interaction tiles no longer fit in LDS together, in
+// one launch: verify_large_kernel, one workgroup per (sequence, value head,
+// column slice), checks the parent row and relabels the tree's nodes in
+// preorder (every subtree one run of positions, so ancestry is an interval
+// test and a block row's ancestors sit in few column blocks; one workgroup
+// per tree writes the ancestor rows, depth and status from it).  It walks the
+// 16-position block rows t in order: for each row it computes only the Gram
+// tiles (t, s) that hold an ancestor pair, spread over the waves, into an LDS
+// row buffer (two of them, alternating), and the solve waves run the row's
+// blocked substitution and output stage for their value columns, two blocks
+// per MFMA.  Row t + 1's tiles are computed while row t is solved, so one
+// barrier per row separates them.  Inputs are gathered and outputs written at
+// the caller's node indices.
 // k / q rows are read from global memory (L2) straight into MFMA operand
 // registers, a row ahead of their use.
 #include "gdn_common.hpp"
@@ -28,86 +27,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int kPrepMaxN = 512;       // largest tree of this path
-constexpr int kPrepThreads = 1024;
-
-// Ancestor rows, depth and status of one sequence's tree, into the cache, by
-// synchronous pointer doubling over (node, word) pairs: node i keeps a covered
-// set C_i (itself and its nearest ancestors, a bit row) and nx_i, its nearest
-// ancestor outside C_i; a round adds C_(nx_i) and moves nx_i to nx_(nx_i),
-// every pair reading before any pair writes, so C_i doubles per round until
-// it is i with all its ancestors.  Two threads per node, eight row words
-// each (two 16-byte LDS accesses), so a round is a handful of LDS accesses
-// and two barriers.
-__global__ __launch_bounds__(kPrepThreads) void tree_prep_kernel(VerifyArgs a) {
-    constexpr int WP = kPrepMaxN / 32;                  // row stride in LDS (words)
-    static_assert(kPrepThreads == 2 * kPrepMaxN && WP == 16, "two threads per node, 8 words each");
-    __shared__ __attribute__((aligned(16))) uint32_t s_mask[kPrepMaxN * WP];
-    __shared__ int32_t s_jump[kPrepMaxN];
-    __shared__ int s_flag;
-    __shared__ int s_more[3];                           // per-round "a link is left" flags, round r uses r % 3
-    const int b = blockIdx.x, N = a.N, W = (N + 31) / 32, tid = threadIdx.x;
-    const SeqRows rows = seq_rows(a.offsets, b, N);     // the cache keeps N rows per tree
-    const int n = max(rows.n, 0);
-    const int i = tid >> 1, hh = tid & 1;               // node, half row (words 8 hh .. +7)
-    if (tid == 0) s_flag = 0x7fffffff;
-    if (tid < 3) s_more[tid] = 0;
-    __syncthreads();
-    if (hh == 0 && i < n) {
-        const int p = a.parent[rows.row0 + i];
-        s_jump[i] = p;
-        if (p < -1 || p >= i) atomicMin(&s_flag, i);
-    }
-    uint4* row = reinterpret_cast<uint4*>(s_mask + i * WP + 8 * hh);
-    {
-        uint32_t w8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w8[e] = (i >> 5) == 8 * hh + e ? 1u << (i & 31) : 0u;
-        row[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
-        row[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
-    }
-    __syncthreads();
-    const int status = rows.n < 0 ? -1 : s_flag == 0x7fffffff ? 0 : s_flag + 1;
-    if (status == 0) {
-        // Round r raises flag r % 3 while some node still has a link to follow
-        // and clears flag (r + 1) % 3 before its first barrier (the last
-        // readers of that flag finished two rounds earlier): two LDS-only
-        // barriers per round, no workgroup reduction.
-        for (int rd = 0;; ++rd) {
-            const int j = i < n ? s_jump[i] : -1;
-            uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
-            int nj = -1;
-            if (j >= 0) {
-                const uint4* rj = reinterpret_cast<const uint4*>(s_mask + j * WP + 8 * hh);
-                a0 = rj[0];
-                a1 = rj[1];
-                nj = s_jump[j];
-            }
-            if (tid == 0) s_more[(rd + 1) % 3] = 0;
-            lds_barrier();
-            if (j >= 0) {
-                uint4 r0 = row[0], r1 = row[1];
-                r0.x |= a0.x; r0.y |= a0.y; r0.z |= a0.z; r0.w |= a0.w;
-                r1.x |= a1.x; r1.y |= a1.y; r1.z |= a1.z; r1.w |= a1.w;
-                row[0] = r0;
-                row[1] = r1;
-                if (hh == 0) s_jump[i] = nj;
-            }
-            if (j >= 0 && nj >= 0) s_more[rd % 3] = 1;
-            lds_barrier();
-            if (!s_more[rd % 3]) break;
-        }
-    }
-    // strict rows (bit i cleared), zero for an invalid tree
-    uint32_t* gm = a.anc_mask + (size_t)b * N * W;
-    for (int x = tid; x < N * W; x += kPrepThreads) {
-        const int r = x / W, w = x - r * W;
-        gm[x] = (status || r >= n) ? 0u : s_mask[r * WP + w] & ~((r >> 5) == w ? 1u << (r & 31) : 0u);
-    }
-    for (int r = tid; r < N; r += kPrepThreads)
-        a.depth[(size_t)b * N + r] = (status || r >= n) ? -1 : row_popc(s_mask + r * WP, W) - 1;
-    if (tid == 0) a.status[b] = status;
-}
+constexpr int kLargeMaxN = 512;      // largest tree of this path
 
 // x of lane k of each lane quad, to all four lanes (k a compile-time value
 // once the caller's loop is unrolled).
@@ -160,6 +80,8 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     __shared__ uint16_t s_perm[NP];
     __shared__ __attribute__((aligned(8))) int16_t s_last[NP];
     __shared__ int s_mlast[NB];                 // largest s_last of each 16-position block
+    __shared__ int s_bad;                       // first node with an invalid parent
+    __shared__ int16_t s_hop[NP];               // nodes on the path to the root (depth + 1), by doubling
     // k rows of blocks 0 .. KC-1 in MFMA operand order: (block s, chunk cs) is
     // 1 KB, lane l's 16 bytes at l * 16 (row 16 s + l % 16, columns 32 cs +
     // 8 (l / 16) .. +7), so a fragment read is one conflict-free ds_read_b128
@@ -182,7 +104,27 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     uint16_t* O = static_cast<uint16_t*>(a.o);
     float* Ug = a.u + ((size_t)b * Hv + h) * (size_t)N * kD;
 
-    const int status = a.status[b];
+    // tree check, the same in every workgroup of the tree: 0, or one plus the
+    // first node whose parent is outside [-1, i); -1 for rows past the
+    // batch's offsets.  One workgroup per tree publishes the ancestor rows,
+    // depth and status (zero rows and depth -1 past the tree or for an
+    // invalid one).
+    const int W = (N + 31) / 32;
+    const bool writer = h == 0 && slice == 0;
+    uint32_t* gm = a.anc_mask + (size_t)b * N * W;
+    if (tid == 0) s_bad = 0x7fffffff;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+        const int p = a.parent[rows.row0 + i];
+        if (p < -1 || p >= i) atomicMin(&s_bad, i);
+    }
+    __syncthreads();
+    const int status = rows.n < 0 ? -1 : s_bad == 0x7fffffff ? 0 : s_bad + 1;
+    if (writer && (status || n == 0)) {
+        for (int x = tid; x < N * W; x += NT) gm[x] = 0u;
+        for (int r = tid; r < N; r += NT) a.depth[(size_t)b * N + r] = -1;
+        if (tid == 0) a.status[b] = status;
+    }
     if (status) {                                       // invalid tree: NaN outputs
         const float qnan = __uint_as_float(0x7fc00000u);
         if (solver)
@@ -227,6 +169,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         s_beta[i] = v ? a.beta[(rows.row0 + i) * Hv + h] : 0.f;
         s_perm[i] = (uint16_t)min(i, max(n - 1, 0));
         s_last[i] = v ? (int16_t)(n - 1) : (int16_t)-1;
+        s_hop[i] = v ? (int16_t)1 : (int16_t)0;
     }
     for (int x = tid; x < (NP + 1) * WC; x += NT) s_cm[x] = 0u;
     if (tid < 9) s_more[tid] = 0;
@@ -344,6 +287,41 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         s_last[pi] = (int16_t)((nx < n ? n - 1 - s_rk[nx] : n) - 1);
     }
     __syncthreads();
+    // ancestor rows from the preorder: j is a strict ancestor of r exactly when
+    // pos(j) < pos(r) <= last(pos(j)), and only j < r can be one.  Each node's
+    // (pos, last) is packed once into the free children-row scratch (nodes
+    // past the tree get pos 0xffff, never below a row's position); the tree's
+    // workgroups share the (row, word) pairs, one pair per thread.
+    const int nparts = Hv * csplit, part = h * csplit + slice;
+    {
+        uint32_t* pk = s_cm;
+        for (int j = tid; j < NP; j += NT) {
+            uint32_t v = 0xffffu;
+            if (j < n) {
+                const int pj = nt ? min(max(n - 1 - s_rk[j], 0), n - 1) : j;
+                v = (uint32_t)pj | ((uint32_t)(uint16_t)s_last[pj] << 16);
+            }
+            pk[j] = v;
+        }
+        __syncthreads();
+        for (int x = part + nparts * tid; x < N * W; x += nparts * NT) {
+            const int r = x / W, w = x - r * W;
+            uint32_t bits = 0u;
+            if (r < n && 32 * w <= r) {
+                const uint32_t pr = pk[r] & 0xffffu;
+#pragma unroll
+                for (int e = 0; e < 32; e += 4) {
+                    const uint4 q4 = *reinterpret_cast<const uint4*>(pk + 32 * w + e);
+                    const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        bits |= ((q[k] & 0xffffu) < pr && pr <= (q[k] >> 16)) ? 1u << (e + k) : 0u;
+                }
+            }
+            gm[x] = bits;
+        }
+        if (writer && tid == 0) a.status[b] = 0;
+    }
     auto node_at = [&](int pos) __attribute__((always_inline)) {   // position (clamped) -> node
         return min((int)s_perm[min(pos, n - 1)], n - 1);
     };
@@ -369,7 +347,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     // while a node still has a link to follow and clears flag (r + 1) % 3
     // before its first barrier: two LDS-only barriers per round
     for (int rd = 0;; ++rd) {
-        int nn[PER];
+        int nn[PER], hj[PER];
         float gj[PER];
         bool more = false;
 #pragma unroll
@@ -378,6 +356,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             const int j = i < NP ? s_jump[i] : -1;
             nn[k] = j >= 0 ? s_jump[j] : -1;
             gj[k] = j >= 0 ? s_lg[j] : 0.f;
+            hj[k] = j >= 0 ? s_hop[j] : 0;
             more |= nn[k] >= 0;
         }
         if (tid == 0) s_more[6 + (rd + 1) % 3] = 0;
@@ -387,6 +366,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             const int i = tid + k * NT;
             if (i < NP && s_jump[i] >= 0) {
                 s_lg[i] += gj[k];
+                s_hop[i] = (int16_t)(s_hop[i] + hj[k]);
                 s_jump[i] = nn[k];
             }
         }
@@ -396,6 +376,8 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     }
     if (slice == 0)
         for (int i = tid; i < n; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
+    for (int r = part + nparts * tid; r < N; r += nparts * NT)   // depth: the rows' shares again
+        a.depth[(size_t)b * N + r] = r < n ? s_hop[r] - 1 : -1;
 
     // G and beta by position (through the scratch: the row buffers are free)
     {
@@ -787,19 +769,15 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
 }  // namespace
 
 bool verify_large_supported(const VerifyArgs& a, int io) {
-    return io == GDN_BF16 && a.dk == kD && a.dv == kD && a.N > 128 && a.N <= kPrepMaxN;
+    return io == GDN_BF16 && a.dk == kD && a.dv == kD && a.N > 128 && a.N <= kLargeMaxN;
 }
 
 hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream) {
     (void)io;
     VerifyArgs copy = a;
-    void* pargs[] = {&copy};
-    hipError_t e = hipLaunchKernel((const void*)tree_prep_kernel, dim3((unsigned)a.B), dim3(kPrepThreads),
-                                   pargs, 0, stream);
-    if (e != hipSuccess) return e;
-    // two column slices of 64 value columns per (sequence, value head), four
-    // waves each: a wave holds up to 32 stacked U pairs and may use the whole
-    // register file of its SIMD
+    // two column slices of 64 value columns per (sequence, value head), eight
+    // waves each: a solve wave holds up to 32 stacked U pairs and may use the
+    // whole register file of its SIMD
     int csplit = 2;
     const void* fn = a.N <= 256 ? (const void*)verify_large_kernel<16> : (const void*)verify_large_kernel<32>;
     void* args[] = {&copy, &csplit};
