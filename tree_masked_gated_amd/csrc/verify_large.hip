@@ -106,9 +106,9 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
 
     // tree check, the same in every workgroup of the tree: 0, or one plus the
     // first node whose parent is outside [-1, i); -1 for rows past the
-    // batch's offsets.  One workgroup per tree publishes the ancestor rows,
-    // depth and status (zero rows and depth -1 past the tree or for an
-    // invalid one).
+    // batch's offsets.  For an invalid or empty tree one workgroup publishes
+    // zero ancestor rows, depth -1 and the status; a valid tree's rows and
+    // depths are shared out once its preorder is known.
     const int W = (N + 31) / 32;
     const bool writer = h == 0 && slice == 0;
     uint32_t* gm = a.anc_mask + (size_t)b * N * W;
@@ -528,8 +528,8 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             return __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]);
         };
         // k / q fragments of a row (two sets, alternating by row) and, refilled
-        // once their products are issued, the k rows and ancestor words of this
-        // wave's first TPW tiles of the next row
+        // once their products are issued, the k rows of this wave's first TPW
+        // tiles of the next row
         struct RowOps {
             bf16x8 k[4], q[4];
         };
