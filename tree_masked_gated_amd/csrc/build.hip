@@ -147,33 +147,29 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
                     __syncthreads();
                 }
         }
-        // 2. merge into the open list, keeping the best N - n
+        // 2. merge into the open list, keeping the best N - n; 3. the step:
+        // the best m open candidates become nodes n .. n + m - 1, recorded by
+        // whichever thread places them
         const int R = N - n;
         const uint64_t* A = lists[cur] + head;
         const int na = len - head;
         uint64_t* out = lists[cur ^ 1];
-        for (int x = lane; x < na; x += kBuildThreads) {
-            const int pos = x + count_larger(ck, nc, A[x]);
-            if (pos < R) out[pos] = A[x];
-        }
-        for (int x = lane; x < nc; x += kBuildThreads) {
-            const int pos = x + count_larger(A, na, ck[x]);
-            if (pos < R) out[pos] = ck[x];
-        }
+        len = min(na + nc, R);
+        const int m = min(min(w, R), len);
+        auto place = [&](int pos, uint64_t key) {
+            if (pos < R) out[pos] = key;
+            if (pos < m) {
+                sc[n + pos] = bits_score((uint32_t)(key >> 32));
+                par[n + pos] = key_parent(key);
+                rk[n + pos] = key_rank(key);
+            }
+        };
+        for (int x = lane; x < na; x += kBuildThreads) place(x + count_larger(ck, nc, A[x]), A[x]);
+        for (int x = lane; x < nc; x += kBuildThreads) place(x + count_larger(A, na, ck[x]), ck[x]);
         cur ^= 1;
         head = 0;
-        len = min(na + nc, R);
         __syncthreads();
-        // 3. the step: the best m open candidates become nodes n .. n + m - 1
-        const int m = min(min(w, R), len);
         if (m == 0) break;                 // (never: every step adds K >= 1 candidates)
-        for (int t = lane; t < m; t += kBuildThreads) {
-            const uint64_t key = lists[cur][t];
-            sc[n + t] = bits_score((uint32_t)(key >> 32));
-            par[n + t] = key_parent(key);
-            rk[n + t] = key_rank(key);
-        }
-        __syncthreads();
         e0 = n;
         ne = m;
         head = m;
