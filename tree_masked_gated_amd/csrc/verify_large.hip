@@ -41,9 +41,9 @@ __device__ __forceinline__ float quad_bcast(float x, int k) {
     }
 }
 
-// Waves 0 .. NS-1 solve: wave w owns value columns 64 slice + 32 w .. +31 as
-// two 16-column groups (two independent MFMA chains per product).  Waves NS ..
-// NS+NG-1 are Gram waves: they compute the next block row's tiles and (the
+// Waves 0 .. NS-1 solve: wave w owns value columns 64 slice + 16 CG w .. as CG
+// 16-column groups (with two, two independent MFMA chains per product).  Waves
+// NS .. NS+NG-1 are Gram waves: they compute the next block row's tiles and (the
 // last NCG of them, one 16-column group each) its projections K_t S0^T and
 // S0 Q_t^T into LDS, while the solve waves run the current row; one barrier
 // per row.  The two roles run separate loops with the same barrier count, so
@@ -52,10 +52,15 @@ template <int NB>
 __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int csplit) {
     constexpr int NP = 16 * NB;                 // padded node count
     constexpr int NT = 512;
-    constexpr int NS = 2;                       // solve waves, 32 value columns each
-    constexpr int NG = 6;                       // Gram waves
+    // solve waves hold their U blocks in registers (CG * NB / 2 stacked
+    // pairs): 512-node trees split the columns over four solve waves so each
+    // keeps room for loads in flight, leaving four Gram waves (a preorder row
+    // has few tiles)
+    constexpr int NS = NB > 16 ? 4 : 2;         // solve waves, 16 CG value columns each
+    constexpr int NG = 8 - NS;                  // Gram waves
     constexpr int NCG = 4;                      // 16-column groups per workgroup
-    constexpr int CG = 2;                       // groups per solve wave
+    constexpr int CG = NCG / NS;                // groups per solve wave
+    static_assert(NS * CG == NCG && NG >= NCG, "column groups cover the slice; every group has a projection wave");
     constexpr int NPR = NB / 2;                 // U pairs
     constexpr int TPW = 3;                      // tiles per Gram wave requested a row ahead
     constexpr int KC = 16;                      // node blocks whose k rows are cached in LDS
@@ -128,8 +133,8 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     if (status) {                                       // invalid tree: NaN outputs
         const float qnan = __uint_as_float(0x7fc00000u);
         if (solver)
-            for (int x = lane; x < N * 32; x += 64) {
-                const int i = x / 32, c = cbase + 32 * wave + x % 32;
+            for (int x = lane; x < N * 16 * CG; x += 64) {
+                const int i = x / (16 * CG), c = cbase + 16 * CG * wave + x % (16 * CG);
                 if (i < n) O[vo_base + (size_t)i * vo_row + c] = 0x7fc0;
                 Ug[(size_t)i * kD + c] = qnan;
             }
@@ -628,7 +633,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     }
 
     // ================= solve waves =================
-    const int c0 = cbase + 32 * wave;                   // this wave's first value column
+    const int c0 = cbase + 16 * CG * wave;              // this wave's first value column
     const s16x4 zero4 = {0, 0, 0, 0};
     const bool hi_half = lq >= 2;
     s16x4 ident;
@@ -651,8 +656,8 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         f32x4 R[CG], pqT[CG];
 #pragma unroll
         for (int g = 0; g < CG; ++g) {
-            const f32x4 pk = s_pk[par][2 * wave + g][lane];
-            pqT[g] = s_pq[par][2 * wave + g][lane];
+            const f32x4 pk = s_pk[par][CG * wave + g][lane];
+            pqT[g] = s_pq[par][CG * wave + g][lane];
             const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vt[g]), ident, z);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
