@@ -546,15 +546,16 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
                 o.q[cs] = frag(Qb, t, cs);
             }
         };
-        // (blocks past the LDS cache only: a cached block's slot reads one
-        // line, the same for every lane)
+        // (blocks past the LDS cache only: a cached block's slot issues no
+        // load, and its products read the LDS copy)
         auto load_tile = [&](int i, int t, unsigned long long occ, int ntile) __attribute__((always_inline)) {
             const int m = gw + i * NG;
             const int sc = m < ntile ? tile_col(t, occ, m) : t;
             if constexpr (!KALL) {
+                if (sc >= KC) {                             // (uniform) cached blocks read LDS instead
 #pragma unroll
-                for (int cs = 0; cs < 4; ++cs)
-                    kp[i][cs] = sc >= KC ? frag(Kb, sc, cs) : *reinterpret_cast<const bf16x8*>(Kb);
+                    for (int cs = 0; cs < 4; ++cs) kp[i][cs] = frag(Kb, sc, cs);
+                }
             } else {
                 (void)sc;
             }
