@@ -6,6 +6,18 @@ import numpy as np
 
 import workloads as W
 
+# Worst errors per case, written to the file named by GDN_PARITY_JSON (if set)
+# when the session ends (tests/conftest.py), so that every run leaves a record
+# of the measured errors next to its log.
+ERRORS = {}
+
+
+def record(name, err):
+    """Keep the worst value of each error figure seen for case `name`."""
+    cur = ERRORS.setdefault(name, {})
+    for key, val in err.items():
+        cur[key] = max(cur.get(key, 0.0), float(val))
+
 
 def rel_l2(x, ref):
     x = np.asarray(x, np.float64).ravel()
@@ -86,3 +98,79 @@ def check_exact(gpu, ref):
     assert np.array_equal(gpu["path_len"], ref["path_len"]), "path_len"
     assert np.array_equal(gpu["path"], ref["path"]), "path"
     assert gpu["s0_unchanged"], "verify wrote S0"
+
+
+def gpu_fused_layer(parent, accepted, lay, io, Hk, Hv, device="cuda"):
+    """The benchmark's decode step on one layer: the tree is verified on S0
+    (cache A), then one gdn_tree_commit_verify launch commits its accepted
+    node (S1) and verifies the same tree again on S1 (cache B), exactly the
+    launch sequence of every timed step."""
+    import torch
+    import tree_masked_gated_amd as T
+    B, N = parent.shape
+    d = lay["S0"].shape[-1]
+    dims = T.dims(B, N, Hk, Hv, d, d, io)
+    S0 = W.to_device(lay["S0"], device=device)
+    x = {key: W.to_device(lay[key], io, device) for key in ("q", "k", "v")}
+    x.update({key: W.to_device(lay[key], device=device) for key in ("beta", "g")})
+    par = W.to_device(parent.astype(np.int32), device=device)
+    acc = W.to_device(np.asarray(accepted, np.int32), device=device)
+    o1 = torch.empty((B, N, Hv, d), dtype=x["q"].dtype, device=device)
+    o2 = torch.empty_like(o1)
+    ca, cb = T.TreeCache(dims, device), T.TreeCache(dims, device)
+    S1 = torch.empty_like(S0)
+    path = torch.full((B, N), -7, dtype=torch.int32, device=device)
+    plen = torch.full((B,), -7, dtype=torch.int32, device=device)
+    T.gdn_tree_verify(dims, S0, x["q"], x["k"], x["v"], x["beta"], x["g"], par, o1, ca)
+    T.gdn_tree_commit_verify(dims, S0, S1, x["k"], ca, acc, path, plen, x["q"], x["k"],
+                             x["v"], x["beta"], x["g"], par, o2, cb)
+    torch.cuda.synchronize()
+    cache = lambda c: {"u": c.u.cpu().numpy(), "log_gamma": c.log_gamma.cpu().numpy(),
+                       "anc_mask": c.anc_mask.cpu().numpy().view(np.uint32),
+                       "depth": c.depth.cpu().numpy(), "status": c.tree_status.cpu().numpy()}
+    return {"o1": W.from_device_f64(o1), "o2": W.from_device_f64(o2), "A": cache(ca),
+            "B": cache(cb), "S1": S1.cpu().numpy().astype(np.float64),
+            "path": path.cpu().numpy(), "path_len": plen.cpu().numpy()}
+
+
+def oracle_paths(parent, accepted):
+    """The oracle's committed path and its length for every sequence.  The
+    path depends on the tree alone, so the oracle runs on a one-dimensional
+    head with zero values."""
+    import oracle
+    B, N = parent.shape
+    z = np.zeros((B, N, 1, 1))
+    r = oracle.verify(np.zeros((B, 1, 1, 1)), z, z, z, np.zeros((B, N, 1)), np.ones((B, N, 1)),
+                      parent, np.asarray(accepted, np.int32))
+    return r["path"], r["path_len"]
+
+
+def oracle_commit(parent, accepted, lay, io, S0):
+    """The oracle's committed state of every sequence's accepted node, from
+    the nodes of its root-to-node path alone: the state of a node is the
+    sequential rule applied along that path, so the path, relabelled as a
+    chain, reaches the same state.  Sequences with shorter paths fill the
+    remaining chain slots with independent roots that nothing reads."""
+    import oracle
+    paths, plen = oracle_paths(parent, accepted)
+    B = parent.shape[0]
+    P = max(1, int(plen.max()))
+    f = lambda a: W.io_to_f64(a, io)
+    q, k, v = f(lay["q"]), f(lay["k"]), f(lay["v"])
+    Hk, Hv = q.shape[2], v.shape[2]
+    cq = np.zeros((B, P) + q.shape[2:]); ck = np.zeros_like(cq)
+    cv = np.zeros((B, P) + v.shape[2:])
+    cb = np.zeros((B, P, Hv)); cg = np.ones((B, P, Hv))
+    cpar = np.full((B, P), -1, np.int32)
+    cacc = np.full(B, -1, np.int32)
+    for b in range(B):
+        n = int(plen[b])
+        if n <= 0:
+            continue
+        nodes = paths[b, :n]
+        cq[b, :n], ck[b, :n], cv[b, :n] = q[b, nodes], k[b, nodes], v[b, nodes]
+        cb[b, :n], cg[b, :n] = lay["beta"][b, nodes], lay["g"][b, nodes]
+        cpar[b, :n] = np.arange(-1, n - 1)
+        cacc[b] = n - 1
+    r = oracle.verify(np.asarray(S0, np.float64), cq, ck, cv, cb, cg, cpar, cacc, memo=True)
+    return r["S_commit"], paths, plen

@@ -186,6 +186,32 @@ def pin_chain_is_linear_scan(lib):
     assert np.allclose(r["S_commit"][0, 0], S, rtol=1e-11, atol=1e-13)
 
 
+def pin_chain256_is_linear_scan(lib):
+    """The 256-node chain workload at its full size (8 sequences x 16 heads,
+    d = 128, bf16 q/k/v widened exactly, beta pushed toward 1): every node's
+    output and the committed state of the last node equal a plain sequential
+    scan over the chain, all 128 (sequence, value head) units stepped together
+    with numpy matrix products."""
+    s = W.spec("chain256_b8")
+    parent, accepted = W.make_trees(s)
+    lay = W.make_layer(s, 0)
+    f = lambda a: W.io_to_f64(a, s.io)
+    q, k, v = f(lay["q"]), f(lay["k"]), f(lay["v"])
+    beta, g = lay["beta"].astype(np.float64), lay["g"].astype(np.float64)
+    S0 = lay["S0"].astype(np.float64)
+    assert (accepted == s.n_nodes - 1).all()
+    r = oracle.verify(S0, q, k, v, beta, g, parent, accepted, memo=True, lib=lib)
+    hk = np.arange(s.h_v) // s.group                  # value head -> key head
+    S = S0.copy()                                     # [B][Hv][dv][dk]
+    for t in range(s.n_nodes):
+        kt, qt = k[:, t][:, hk, :, None], q[:, t][:, hk, :, None]
+        gt, bt = g[:, t, :, None, None], beta[:, t, :, None, None]
+        S = gt * S + bt * (v[:, t, :, :, None] - gt * (S @ kt)) @ kt.transpose(0, 1, 3, 2)
+        o = (S @ qt)[..., 0]
+        assert np.allclose(r["o"][:, t], o, rtol=1e-10, atol=1e-12), t
+    assert np.allclose(r["S_commit"], S, rtol=1e-10, atol=1e-12)
+
+
 def pin_masks_paths(lib):
     rng = np.random.default_rng(16)
     trees = some_trees(rng)
@@ -504,4 +530,5 @@ ALL_PINS = [
     pin_non_ancestors_do_not_matter, pin_topological_relabel, pin_memo_equals_walk,
     pin_conventions, pin_accept_brute_force, pin_accept_conventions,
     pin_build_hand_example, pin_build_best_first_top_scores, pin_build_steps_valid,
+    pin_chain256_is_linear_scan,
 ]

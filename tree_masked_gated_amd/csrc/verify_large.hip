@@ -782,8 +782,8 @@ hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream) 
     (void)io;
     VerifyArgs copy = a;
     // two column slices of 64 value columns per (sequence, value head), eight
-    // waves each: a solve wave holds up to 32 stacked U pairs and may use the
-    // whole register file of its SIMD
+    // waves each: two solve waves of 32 columns (trees up to 256 nodes) or four
+    // of 16 (up to 512), each holding 16 stacked U pairs, one wave per SIMD
     int csplit = 2;
     const void* fn = a.N <= 256 ? (const void*)verify_large_kernel<16> : (const void*)verify_large_kernel<32>;
     void* args[] = {&copy, &csplit};
