@@ -3,22 +3,35 @@
 //
 // Same method as the small-tree kernel (page "Trees from Marginals:
 // Autoregressive drafting with factorized priors", section 3: the Gram matrix,
-// a tiled forward substitution and the output stage, fused), laid out for trees
-// whose k / q rows and interaction tiles no longer fit in LDS together, in
-// one launch: verify_large_kernel, one workgroup per (sequence, value head,
-// column slice), checks the parent row and relabels the tree's nodes in
-// preorder (every subtree one run of positions, so ancestry is an interval
-// test and a block row's ancestors sit in few column blocks; one workgroup
-// per tree writes the ancestor rows, depth and status from it).  It walks the
-// 16-position block rows t in order: for each row it computes only the Gram
-// tiles (t, s) that hold an ancestor pair, spread over the waves, into an LDS
-// row buffer (two of them, alternating), and the solve waves run the row's
-// blocked substitution and output stage for their value columns, two blocks
-// per MFMA.  Row t + 1's tiles are computed while row t is solved, so one
-// barrier per row separates them.  Inputs are gathered and outputs written at
-// the caller's node indices.
-// k / q rows are read from global memory (L2) straight into MFMA operand
-// registers, a row ahead of their use.
+// a tiled forward substitution and the output stage, fused), laid out for
+// trees whose interaction tiles do not fit in LDS.  One workgroup per
+// (sequence, value head, 64-column slice), twelve waves in two roles that
+// meet through LDS flags, with no barrier after the setup:
+//
+//  * setup (all waves): the parent row is checked, the tree's nodes are
+//    relabelled in preorder (every subtree one run of positions, so ancestry
+//    is an interval test and a block row's ancestors sit in few column
+//    blocks), the path log-gates are summed by pointer doubling, and the
+//    tree's workgroups share writing its ancestor rows, depths and status.
+//    The workgroup's global inputs are requested first (for trees of up to
+//    256 nodes the k rows, stored into LDS at its end), so their latency
+//    overlaps it; its barriers order LDS only.
+//  * row owners (waves 4 .. 11, 16-position block rows round robin): for a
+//    row t, the diagonal block's inverse D_t = (I + X_tt)^-1 (fp32, kept bf16),
+//    every occupied tile of the row already multiplied by it,
+//    X~_ts = D_t X_ts, and the right-hand side D_t R_t with
+//    R_t = diag(beta)(V_t - diag(e^G) K_t S0^T) (bf16 hi + lo parts of R),
+//    into a ring of LDS slots.  With those the substitution of a row is
+//    U_t = D_t R_t - sum_s X~_ts U_s: one chain of 16x16x16 products, the last
+//    of which waits for the previous row.  Then the row's outputs
+//    O_t = e^G Q_t S0^T + sum_{s <= t} Y_ts U_s, with the Y tiles formed from
+//    the same k operands and U read from LDS as the solve publishes it.
+//  * solve (waves 0 .. 3, 16 value columns each): row by row, the chain of
+//    the row's X~ products on D_t R_t; U_t goes to LDS (bf16, for later rows
+//    and the outputs) and to the cache (fp32).  The solve waves read no
+//    global memory.
+//
+// Inputs are gathered and outputs written at the caller's node indices.
 #include "gdn_common.hpp"
 #include "launch.hpp"
 #include "mfma_tiles.hpp"
@@ -28,6 +41,17 @@ namespace gdn {
 namespace {
 
 constexpr int kLargeMaxN = 512;      // largest tree of this path
+constexpr int kLargeWaves = 12;
+constexpr int kLargeThreads = 64 * kLargeWaves;
+constexpr int kSolveWaves = 4;       // one 16-column group each: 64 columns per workgroup
+constexpr int kOwners = kLargeWaves - kSolveWaves;
+constexpr int kChunkG = 3;           // k operands of a row's tiles requested together (global memory)
+constexpr int kChunkL = 2;           // ... read together (LDS)
+
+// buffer resources for stores that must not branch on a lane's validity: a
+// lane's store past the buffer is dropped
+constexpr int kBufferFlags = 0x00020000;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // x of lane k of each lane quad, to all four lanes (k a compile-time value
 // once the caller's loop is unrolled).
@@ -41,65 +65,90 @@ __device__ __forceinline__ float quad_bcast(float x, int k) {
     }
 }
 
-// Waves 0 .. NS-1 solve: wave w owns value columns 64 slice + 16 CG w .. as CG
-// 16-column groups (with two, two independent MFMA chains per product).  Waves
-// NS .. NS+NG-1 are Gram waves: they compute the next block row's tiles and (the
-// last NCG of them, one 16-column group each) its projections K_t S0^T and
-// S0 Q_t^T into LDS, while the solve waves run the current row; one barrier
-// per row.  The two roles run separate loops with the same barrier count, so
-// neither keeps the other's registers.
+// Spin until *f >= v.  The flags live in LDS and only grow; a flag's writer
+// never waits for its readers' later work, so every wait ends.
+__device__ __forceinline__ void wait_flag_ge(int* f, int v) {
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < v)
+        __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+}
+// This wave's LDS reads and writes are complete, then lane 0 stores v.
+__device__ __forceinline__ void publish_set(int* f, int v, int lane) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// (Masked entries are computed for every lane and then selected, so no lane
+// takes a branch: e^(G_i - G_j) is taken of min(G_i - G_j, 0), which leaves
+// every ancestor pair's value unchanged -- the path of i contains j's, and
+// every gate is at most 1 -- and keeps the discarded ones finite.)
+
+// A 16x16 bf16 tile as a 16x16x16 A operand: lane l holds row l % 16,
+// columns 4 (l / 16) .. +3, one 8-byte word per lane.  Element (r, c) in
+// halfwords:
+__device__ __forceinline__ int a16_pos(int r, int c) { return (r + 16 * (c >> 2)) * 4 + (c & 3); }
+
+// 16-byte chunk c of 128-element bf16 row r in LDS, XOR-swizzled by the row's
+// low bits so the 16 rows of a fragment read fall in distinct banks.
+__device__ __forceinline__ int row_chunk(int r, int c) { return r * kD + ((c ^ (r & 15)) << 3); }
+
 template <int NB>
-__global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int csplit) {
-    constexpr int NP = 16 * NB;                 // padded node count
-    constexpr int NT = 512;
-    // solve waves hold their U blocks in registers (CG * NB / 2 stacked
-    // pairs): 512-node trees split the columns over four solve waves so each
-    // keeps room for loads in flight, leaving four Gram waves (a preorder row
-    // has few tiles)
-    constexpr int NS = NB > 16 ? 4 : 2;         // solve waves, 16 CG value columns each
-    constexpr int NG = 8 - NS;                  // Gram waves
-    constexpr int NCG = 4;                      // 16-column groups per workgroup
-    constexpr int CG = NCG / NS;                // groups per solve wave
-    static_assert(NS * CG == NCG && NG >= NCG, "column groups cover the slice; every group has a projection wave");
-    constexpr int NPR = NB / 2;                 // U pairs
-    constexpr int TPW = 3;                      // tiles per Gram wave requested a row ahead
-    constexpr int KC = 16;                      // node blocks whose k rows are cached in LDS
-    constexpr bool KALL = NB <= KC;             // every block cached: no k rows from L2 in the Gram
-    // -X and Y tiles of one block row, by column block s, for rows of either
-    // parity; a spare tile at the end (a pair read may run 512 bytes past the
-    // last tile; those lanes are zeroed before use)
-    __shared__ __attribute__((aligned(16))) uint16_t s_xrow[2][NB * 256 + 256];
-    __shared__ __attribute__((aligned(16))) uint16_t s_yrow[2][NB * 256 + 256];
-    __shared__ __attribute__((aligned(16))) uint16_t s_dinv[2][256];
-    __shared__ __attribute__((aligned(16))) float s_xd[2][256];
-    __shared__ __attribute__((aligned(16))) f32x4 s_pk[2][NCG][64];   // K_t S0^T, accumulator layout
-    __shared__ __attribute__((aligned(16))) f32x4 s_pq[2][NCG][64];   // S0 Q_t^T
+struct LargeShape {
+    static constexpr int NP = 16 * NB;
+    static constexpr bool KLDS = NB <= 16;              // the k rows sit in LDS
+    static constexpr int WC = NP / 32;                  // words of a children row
+    static constexpr int SCRATCH = ((NP + 1) * WC + 5 * NP + 1) * 4;   // the preorder's
+    static constexpr int RING0 = NB <= 16 ? 84 * 512 : 136 * 512;
+    static constexpr int BIG = RING0 > SCRATCH ? RING0 : SCRATCH;
+    static constexpr int RING = BIG / 1024 * 2;         // 512-byte slots in flight (even)
+};
+
+template <int NB>
+__global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyArgs a, int units) {
+    using L = LargeShape<NB>;
+    constexpr int kChunk = L::KLDS ? kChunkL : kChunkG;
+    constexpr int NP = L::NP;
+    constexpr int NT = kLargeThreads;
+    constexpr bool KLDS = L::KLDS;
+    constexpr int WC = L::WC;
+    constexpr int SCRATCH = L::SCRATCH;
+    constexpr int BIG = L::BIG;
+    constexpr int RING = L::RING;
+    constexpr int PL = (NP + NT - 1) / NT;              // tree entries per thread
+    // the ring: per row, D_t R_t of the four column groups (two slots each,
+    // 16 bytes per lane) and the row's -X~ tiles (8 bytes per lane each);
+    // during the setup the preorder's scratch
+    __shared__ __attribute__((aligned(16))) uint2 s_big[BIG / 8];
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[KLDS ? NP * kD : 8];   // k rows, node order
+    __shared__ __attribute__((aligned(16))) uint16_t s_s0[64 * kD];            // the slice's S0 rows, bf16
+    __shared__ __attribute__((aligned(16))) uint2 s_u[NB][kSolveWaves][64];   // U_t, bf16 B operands
     __shared__ __attribute__((aligned(16))) float s_lg[NP];
     __shared__ __attribute__((aligned(16))) float s_beta[NP];
     __shared__ __attribute__((aligned(16))) int32_t s_jump[NP];
-    __shared__ unsigned long long s_occ[NB];    // bit s of row t: tile (t, s), s < t, not all zero
-    __shared__ uint8_t s_tcol[NB][NB];          // row t's tiles: t, then its occupied blocks s < t, descending
-    __shared__ int s_more[9];                   // per-round flags of the three doubling loops (3 each)
-    // the node order the kernel works in: a preorder (every subtree one run of
-    // positions), position -> node, and each position's last descendant
-    __shared__ uint16_t s_perm[NP];
-    __shared__ __attribute__((aligned(8))) int16_t s_last[NP];
-    __shared__ int s_mlast[NB];                 // largest s_last of each 16-position block
-    __shared__ int s_bad;                       // first node with an invalid parent
-    __shared__ int16_t s_hop[NP];               // nodes on the path to the root (depth + 1), by doubling
-    // k rows of blocks 0 .. KC-1 in MFMA operand order: (block s, chunk cs) is
-    // 1 KB, lane l's 16 bytes at l * 16 (row 16 s + l % 16, columns 32 cs +
-    // 8 (l / 16) .. +7), so a fragment read is one conflict-free ds_read_b128
-    __shared__ __attribute__((aligned(16))) uint16_t s_kc[KC * 4 * 512];
+    __shared__ uint16_t s_perm[NP];                     // position -> node
+    __shared__ __attribute__((aligned(8))) int16_t s_last[NP];   // position of the last descendant
+    __shared__ int16_t s_hop[NP];                       // nodes on the path to the root (depth + 1)
+    __shared__ int s_mlast[NB];                         // largest s_last of each block
+    __shared__ uint8_t s_tcol[NB][NB];                  // row t's occupied blocks s < t, ascending
+    __shared__ int s_tn[NB];                            // their number
+    __shared__ int s_gslot[NB + 1];                     // first tile of row t, counted over all rows
+    __shared__ int s_rstar[NB];                         // rows consumed before row t's ring slots are free
+    __shared__ int s_xready[NB];                        // row t's ring slots published
+    __shared__ int s_uready[kSolveWaves];               // rows finished by each solve wave
+    __shared__ int s_more[9];                           // per-round flags of the three doubling loops
+    __shared__ int s_bad;                               // first node with an invalid parent
+    __shared__ int s_notchain;                          // some node's parent is not the node before it
 
     const int N = a.N, Hv = a.Hv, Hk = a.Hk, G = Hv / Hk;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool solver = wave < NS;
-    const int item = blockIdx.x;
-    const int slice = item % csplit, bh = item / csplit;
-    const int h = bh % Hv, b = bh / Hv, hk = h / G;
-    const int cbase = slice * (16 * NCG);               // the workgroup's first value column
+    // workgroups are dealt to the 8 XCDs round robin: the two slices of a
+    // (sequence, head) are 8 workgroups apart, on one XCD, sharing its L2
+    const int bid = blockIdx.x;
+    const int unit = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1;
+    if (unit >= units) return;
+    const int h = unit % Hv, b = unit / Hv, hk = h / G;
+    const int cbase = 64 * slice;                       // the workgroup's first value column
     // this tree's rows in the node arrays (n nodes); the cache keeps N rows per tree
     const SeqRows rows = seq_rows(a.offsets, b, N);
     const int n = max(rows.n, 0);
@@ -108,7 +157,54 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     const size_t vo_base = (rows.row0 * Hv + h) * kD;
     uint16_t* O = static_cast<uint16_t*>(a.o);
     float* Ug = a.u + ((size_t)b * Hv + h) * (size_t)N * kD;
+    const bool solver = wave < kSolveWaves;
+    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + (rows.row0 * Hk + hk) * kD;
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + (rows.row0 * Hk + hk) * kD;
+    const size_t kq_row = (size_t)Hk * kD;
 
+    // ---- the workgroup's inputs, requested before anything waits ----
+    // parent, g, beta of the tree's nodes
+    int par_r[PL];
+    float g_r[PL], beta_r[PL];
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+        const int i = tid + k * NT;
+        const bool v = i < n;
+        par_r[k] = v ? a.parent[rows.row0 + i] : -1;
+        g_r[k] = v ? a.g[(rows.row0 + i) * Hv + h] : 1.f;
+        beta_r[k] = v ? a.beta[(rows.row0 + i) * Hv + h] : 0.f;
+    }
+    // the slice's 64 S0 rows (fp32; converted into LDS after the setup)
+    constexpr int S0L = 64 * kD / 4 / NT + 1;           // float4 loads per thread
+    float4 s0_r[S0L];
+    const float* S0p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)cbase * kD;
+#pragma unroll
+    for (int k = 0; k < S0L; ++k) {                     // (float4 index in the 64 x 128 slice, clamped)
+        const int x = min(tid + k * NT, 64 * kD / 4 - 1);
+        s0_r[k] = *reinterpret_cast<const float4*>(S0p + 4 * x);
+    }
+    // k rows of the tree (node order, rows past the tree copy row n - 1) into
+    // registers, written to LDS at the end of the setup: one 1 KB unit is
+    // four rows, lane l taking row 4u + l / 16 and its logical chunk
+    // (l % 16) ^ (row & 15), so the store is one contiguous 16-byte write per lane
+    constexpr int KI = KLDS ? (NP / 4 + kLargeWaves - 1) / kLargeWaves : 1;
+    u32x4 k_r[KI];
+    if constexpr (KLDS) {
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk) {
+            const int u = min(wave + kk * kLargeWaves, NP / 4 - 1);
+            const int row = 4 * u + (lane >> 4), pc = lane & 15;
+            const int srow = min(row, max(n - 1, 0));
+            k_r[kk] = *reinterpret_cast<const u32x4*>(Kb + (size_t)srow * kq_row + ((pc ^ (row & 15)) << 3));
+        }
+    }
+    // (the tree's values are used only below: their arithmetic may not be
+    // moved up to the loads, where it would wait for them before the other
+    // requests are out)
+#pragma unroll
+    for (int k = 0; k < PL; ++k) asm volatile("" : "+v"(par_r[k]), "+v"(g_r[k]), "+v"(beta_r[k]));
+    // (Every barrier of the setup orders LDS only: the global loads above and
+    // the cache rows stored below stay in flight across it.)
     // tree check, the same in every workgroup of the tree: 0, or one plus the
     // first node whose parent is outside [-1, i); -1 for rows past the
     // batch's offsets.  For an invalid or empty tree one workgroup publishes
@@ -117,13 +213,17 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     const int W = (N + 31) / 32;
     const bool writer = h == 0 && slice == 0;
     uint32_t* gm = a.anc_mask + (size_t)b * N * W;
-    if (tid == 0) s_bad = 0x7fffffff;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-        const int p = a.parent[rows.row0 + i];
-        if (p < -1 || p >= i) atomicMin(&s_bad, i);
+    if (tid == 0) {
+        s_bad = 0x7fffffff;
+        s_notchain = 0;
     }
-    __syncthreads();
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+        const int i = tid + k * NT;
+        if (i < n && (par_r[k] < -1 || par_r[k] >= i)) atomicMin(&s_bad, i);
+    }
+    lds_barrier();
     const int status = rows.n < 0 ? -1 : s_bad == 0x7fffffff ? 0 : s_bad + 1;
     if (writer && (status || n == 0)) {
         for (int x = tid; x < N * W; x += NT) gm[x] = 0u;
@@ -133,8 +233,8 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     if (status) {                                       // invalid tree: NaN outputs
         const float qnan = __uint_as_float(0x7fc00000u);
         if (solver)
-            for (int x = lane; x < N * 16 * CG; x += 64) {
-                const int i = x / (16 * CG), c = cbase + 16 * CG * wave + x % (16 * CG);
+            for (int x = lane; x < N * 16; x += 64) {
+                const int i = x >> 4, c = cbase + 16 * wave + (x & 15);
                 if (i < n) O[vo_base + (size_t)i * vo_row + c] = 0x7fc0;
                 Ug[(size_t)i * kD + c] = qnan;
             }
@@ -144,47 +244,67 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     }
     if (n == 0) return;                                 // an empty tree: nothing to verify
 
-    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + (rows.row0 * Hk + hk) * kD;
-    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + (rows.row0 * Hk + hk) * kD;
-    const size_t kq_row = (size_t)Hk * kD;
     // ---- a preorder of the tree, path log-gates G, beta, tile occupancy ----
     // In a preorder (children in index order) j is a strict ancestor of i
     // exactly when j < i <= last(j), last(j) the position of j's last
     // descendant, so a block row's ancestors sit in few column blocks (a
     // random tree's rows touch most blocks in the caller's order) and the
     // tile masks need no ancestor rows.  Outputs stay in the caller's order.
-    // Scratch while it is built: the X / Y row buffers.
-    constexpr int WC = NP / 32;                         // words of a children row
-    constexpr int PER = NP / NT > 0 ? NP / NT : 1;
-    uint32_t* s_cm = reinterpret_cast<uint32_t*>(&s_xrow[0][0]);  // [NP + 1][WC]; row NP: the roots
-    int32_t* s_fc = reinterpret_cast<int32_t*>(&s_yrow[0][0]);    // [NP + 1] first child, -1: none
+    // Scratch while it is built: the ring area.
+    uint32_t* s_cm = reinterpret_cast<uint32_t*>(s_big);          // [NP + 1][WC]; row NP: the roots
+    int32_t* s_fc = reinterpret_cast<int32_t*>(s_cm + (NP + 1) * WC);   // [NP + 1] first child, -1: none
     int32_t* s_nx = s_fc + (NP + 1);                    // [NP] node after the subtree (n: none; -1 pending)
     int32_t* s_ptr = s_nx + NP;                         // [NP] doubling link
     int32_t* s_rk = s_ptr + NP;                         // [NP] list distance to the last node
     int32_t* s_sc = s_rk + NP;                          // [NP] list link (n: past the last node)
-    static_assert((NP + 1) * WC * 4 <= sizeof(s_xrow) && (5 * NP + 1) * 4 <= sizeof(s_yrow),
-                  "preorder scratch fits the row buffers");
+    static_assert(SCRATCH <= BIG, "preorder scratch fits the ring area");
     bool not_chain = false;                             // a chain is its own preorder
-    for (int i = tid; i < NP; i += NT) {
-        const bool v = i < n;
-        const int p = v ? a.parent[rows.row0 + i] : -1;
-        not_chain |= v && p != i - 1;
-        s_jump[i] = p;
-        s_lg[i] = v ? logf(a.g[(rows.row0 + i) * Hv + h]) : 0.f;
-        s_beta[i] = v ? a.beta[(rows.row0 + i) * Hv + h] : 0.f;
-        s_perm[i] = (uint16_t)min(i, max(n - 1, 0));
-        s_last[i] = v ? (int16_t)(n - 1) : (int16_t)-1;
-        s_hop[i] = v ? (int16_t)1 : (int16_t)0;
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+        const int i = tid + k * NT;
+        if (i < NP) {
+            const bool v = i < n;
+            not_chain |= v && par_r[k] != i - 1;
+            s_jump[i] = v ? par_r[k] : -1;
+            s_lg[i] = v ? logf(g_r[k]) : 0.f;
+            s_beta[i] = v ? beta_r[k] : 0.f;
+            s_perm[i] = (uint16_t)min(i, max(n - 1, 0));
+            s_last[i] = v ? (int16_t)(n - 1) : (int16_t)-1;
+            s_hop[i] = v ? (int16_t)1 : (int16_t)0;
+        }
     }
     for (int x = tid; x < (NP + 1) * WC; x += NT) s_cm[x] = 0u;
+    if constexpr (KLDS) {
+#pragma unroll
+        for (int kk = 0; kk < KI; ++kk) {
+            const int u = wave + kk * kLargeWaves;
+            if (u < NP / 4) *reinterpret_cast<u32x4*>(s_k + 4 * u * kD + 8 * lane) = k_r[kk];
+        }
+    }
+    // the slice's S0 rows as bf16 (row c at LDS row c, chunks swizzled)
+#pragma unroll
+    for (int k = 0; k < S0L; ++k) {
+        const int x = tid + k * NT;
+        if (x < 64 * kD / 4) {
+            const int r = x >> 5, c4 = x & 31;          // row, float4 within the row
+            uint2 w;
+            w.x = (uint32_t)bf16_rne(s0_r[k].x) | ((uint32_t)bf16_rne(s0_r[k].y) << 16);
+            w.y = (uint32_t)bf16_rne(s0_r[k].z) | ((uint32_t)bf16_rne(s0_r[k].w) << 16);
+            *reinterpret_cast<uint2*>(s_s0 + row_chunk(r, c4 >> 1) + 4 * (c4 & 1)) = w;
+        }
+    }
     if (tid < 9) s_more[tid] = 0;
+    if (tid < NB) s_xready[tid] = 0;
+    if (tid < kSolveWaves) s_uready[tid] = 0;
     // a chain skips the construction (nt = 0): the identity and last = n - 1
-    const int nt = __syncthreads_or(not_chain) ? n : 0;
+    if (not_chain) s_notchain = 1;
+    lds_barrier();
+    const int nt = s_notchain ? n : 0;
     for (int i = tid; i < nt; i += NT) {                // bit i of its parent's children row
         const int p = s_jump[i];
         atomicOr(&s_cm[(p < 0 ? NP : p) * WC + (i >> 5)], 1u << (i & 31));
     }
-    __syncthreads();
+    lds_barrier();
     for (int v = tid; v <= NP; v += NT) {               // first child (row NP: the first root)
         int f = -1;
         if (v < nt || v == NP)
@@ -213,14 +333,14 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         s_nx[i] = nsib >= 0 ? nsib : (p < 0 ? n : -1);
         s_ptr[i] = p;
     }
-    __syncthreads();
+    lds_barrier();
     // the node after a subtree: the subtree root's next sibling, else its
     // parent's (pointer doubling up the path; a root-level node always has one)
     for (int rd = 0;; ++rd) {
-        int res[PER], nq[PER];
+        int res[PL], nq[PL];
         bool more = false;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
+        for (int k = 0; k < PL; ++k) {
             const int i = tid + k * NT;
             res[k] = -2;
             nq[k] = 0;
@@ -238,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         if (tid == 0) s_more[(rd + 1) % 3] = 0;
         lds_barrier();
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
+        for (int k = 0; k < PL; ++k) {
             const int i = tid + k * NT;
             if (res[k] >= 0) s_nx[i] = res[k];
             else if (res[k] == -1) s_ptr[i] = nq[k];
@@ -253,12 +373,12 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         s_sc[i] = sc;
         s_rk[i] = sc < n ? 1 : 0;
     }
-    __syncthreads();
+    lds_barrier();
     for (int rd = 0;; ++rd) {                           // list ranking by pointer doubling
-        int nr[PER], ns[PER];
+        int nr[PL], ns[PL];
         bool more = false;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
+        for (int k = 0; k < PL; ++k) {
             const int i = tid + k * NT;
             nr[k] = -1;
             ns[k] = n;
@@ -274,7 +394,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         if (tid == 0) s_more[3 + (rd + 1) % 3] = 0;
         lds_barrier();
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
+        for (int k = 0; k < PL; ++k) {
             const int i = tid + k * NT;
             if (nr[k] >= 0) {
                 s_rk[i] = nr[k];
@@ -291,13 +411,13 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         s_perm[pi] = (uint16_t)i;
         s_last[pi] = (int16_t)((nx < n ? n - 1 - s_rk[nx] : n) - 1);
     }
-    __syncthreads();
+    lds_barrier();
     // ancestor rows from the preorder: j is a strict ancestor of r exactly when
     // pos(j) < pos(r) <= last(pos(j)), and only j < r can be one.  Each node's
     // (pos, last) is packed once into the free children-row scratch (nodes
     // past the tree get pos 0xffff, never below a row's position); the tree's
     // workgroups share the (row, word) pairs, one pair per thread.
-    const int nparts = Hv * csplit, part = h * csplit + slice;
+    const int nparts = Hv * 2, part = h * 2 + slice;
     {
         uint32_t* pk = s_cm;
         for (int j = tid; j < NP; j += NT) {
@@ -308,7 +428,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
             }
             pk[j] = v;
         }
-        __syncthreads();
+        lds_barrier();
         for (int x = part + nparts * tid; x < N * W; x += nparts * NT) {
             const int r = x / W, w = x - r * W;
             uint32_t bits = 0u;
@@ -335,28 +455,39 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         for (int e = 0; e < 16; ++e) m = max(m, (int)s_last[16 * sb + e]);
         s_mlast[sb] = m;
     }
-    // k rows of the cached blocks into registers (1 KB unit wave + 8 r: block
-    // u / 4, chunk u % 4), written to LDS once the tree's gates are summed, so
-    // the loads overlap that work.  Positions clamped to n - 1.
-    constexpr int KCR = KC * 4 / (NT / 64);             // units per wave
-    u32x4 kcr[KCR];
-#pragma unroll
-    for (int r = 0; r < KCR; ++r) {
-        const int u = wave + (NT / 64) * r;
-        const int row = node_at(16 * (u >> 2) + ln);
-        kcr[r] = *reinterpret_cast<const u32x4*>(Kb + (size_t)row * kq_row + 32 * (u & 3) + 8 * lq);
-    }
 
-    // path log-gates by synchronous pointer doubling (each node adds its
-    // link's sum and jumps to the link's link); round r raises flag r % 3
-    // while a node still has a link to follow and clears flag (r + 1) % 3
-    // before its first barrier: two LDS-only barriers per round
-    for (int rd = 0;; ++rd) {
-        int nn[PER], hj[PER];
-        float gj[PER];
+    // path log-gates.  A chain's are prefix sums: a scan within each wave
+    // (lane shifts) and the preceding waves' totals.  Any other tree's by
+    // synchronous pointer doubling (each node adds its link's sum and jumps
+    // to the link's link); round r raises flag r % 3 while a node still has a
+    // link to follow and clears flag (r + 1) % 3 before its first barrier: two
+    // LDS-only barriers per round
+    if (nt == 0) {
+        static_assert(NP <= NT, "one chain node per thread");
+        float x = tid < NP ? s_lg[tid] : 0.f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        // (past the preorder's scratch, whose packed rows may still be read)
+        float* wsum = reinterpret_cast<float*>(reinterpret_cast<char*>(s_big) + SCRATCH);
+        static_assert(SCRATCH + 4 * kLargeWaves <= BIG, "wave sums fit the ring area");
+        if (lane == 63) wsum[wave] = x;
+        lds_barrier();
+        for (int w = 0; w < wave; ++w) x += wsum[w];
+        if (tid < NP) {
+            s_lg[tid] = x;
+            s_hop[tid] = (int16_t)(tid < n ? tid + 1 : 0);
+        }
+        lds_barrier();
+    }
+    for (int rd = 0; nt; ++rd) {
+        int nn[PL], hj[PL];
+        float gj[PL];
         bool more = false;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
+        for (int k = 0; k < PL; ++k) {
             const int i = tid + k * NT;
             const int j = i < NP ? s_jump[i] : -1;
             nn[k] = j >= 0 ? s_jump[j] : -1;
@@ -367,7 +498,7 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
         if (tid == 0) s_more[6 + (rd + 1) % 3] = 0;
         lds_barrier();
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
+        for (int k = 0; k < PL; ++k) {
             const int i = tid + k * NT;
             if (i < NP && s_jump[i] >= 0) {
                 s_lg[i] += gj[k];
@@ -384,390 +515,379 @@ __global__ __launch_bounds__(512, 1) void verify_large_kernel(VerifyArgs a, int 
     for (int r = part + nparts * tid; r < N; r += nparts * NT)   // depth: the rows' shares again
         a.depth[(size_t)b * N + r] = r < n ? s_hop[r] - 1 : -1;
 
-    // G and beta by position (through the scratch: the row buffers are free)
-    {
-        float* tl = reinterpret_cast<float*>(&s_yrow[0][0]);
+    // G and beta by position (through the scratch: the ring area is free; a
+    // chain is in position order already)
+    if (nt) {
+        float* tl = reinterpret_cast<float*>(s_big);
         float* tb = tl + NP;
         for (int i = tid; i < NP; i += NT) {
             const int v = node_at(i);
             tl[i] = i < n ? s_lg[v] : 0.f;
             tb[i] = i < n ? s_beta[v] : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
         for (int i = tid; i < NP; i += NT) {
             s_lg[i] = tl[i];
             s_beta[i] = tb[i];
         }
     }
     // occupancy: tile (t, s), s < t, holds an ancestor pair exactly when a
-    // position of block s has its subtree reaching row t; tile lists: the
-    // diagonal, then the occupied blocks in descending order, so the blocks
-    // past the LDS k cache come first and get the prefetched slots
+    // position of block s has its subtree reaching row t.  Row t's tiles in
+    // ascending s, so the tile of the block just before it (the one that
+    // waits for the previous row's U) comes last.
     for (int t = tid; t < NB; t += NT) {
-        unsigned long long occ = 0ull;
+        int m = 0;
         for (int sb = 0; sb < t && t < nblk; ++sb)
-            if (s_mlast[sb] >= 16 * t) occ |= 1ull << sb;
-        s_occ[t] = occ;
-        s_tcol[t][0] = (uint8_t)t;
-        for (int m = 1; occ; ++m) {
-            const int hb = 63 - __clzll((long long)occ);
-            s_tcol[t][m] = (uint8_t)hb;
-            occ &= ~(1ull << hb);
-        }
+            if (s_mlast[sb] >= 16 * t) s_tcol[t][m++] = (uint8_t)sb;
+        s_tn[t] = m;
     }
+    lds_barrier();
+    // the ring: row t takes the next 8 + s_tn[t] slots, rounded up to an even
+    // count so that 2-slot objects never wrap (counted over all rows, modulo
+    // RING); they may be written once every row whose slots they reuse has
+    // been consumed by all solve waves.  One wave, row r in lane r.
+    lds_barrier();
+    if (wave == 0) {
+        const int tn = lane < nblk ? s_tn[lane] : 0;
+        const int sl = lane < nblk ? 8 + tn + (tn & 1) : 0;
+        int inc = sl;
 #pragma unroll
-    for (int r = 0; r < KCR; ++r)
-        *reinterpret_cast<u32x4*>(s_kc + (wave + (NT / 64) * r) * 512 + lane * 8) = kcr[r];
-    __syncthreads();
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(inc, d);
+            if (lane >= d) inc += y;
+        }
+        const int gsl = inc - sl;                       // first slot of row lane; lane nblk: the total
+        const int target = inc - RING;                  // rows starting below it must be consumed
+        int cnt = 0;
+        for (int r = 0; r < nblk; ++r) {
+            const int gr = __builtin_amdgcn_readlane(gsl, r);
+            cnt += (r < lane && gr < target) ? 1 : 0;
+        }
+        if (lane <= NB) s_gslot[lane] = gsl;
+        if (lane < NB) s_rstar[lane] = cnt;
+    }
+    lds_barrier();
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    auto row_occ = [&](int t) __attribute__((always_inline)) {
-        // (readfirstlane returns a signed int: widen through uint32_t, and keep
-        // only column blocks 0 .. t - 1)
-        return (((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(s_occ[t] >> 32)) << 32) |
-                (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)s_occ[t])) &
-               ((1ull << t) - 1ull);
-    };
 
-    if (!solver) {
-        // ================= Gram waves =================
-        const int gw = wave - NS;
-        const int pg = gw - (NG - NCG);                 // projection column group (>= 0: this wave's)
-        // the projection group's S0 rows as bf16 B / A operands
-        bf16x8 sb[4];
-        {
-            const int col0 = cbase + 16 * max(pg, 0);
-            const float* p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(col0 + ln) * kD + 8 * lq;
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs)
-                sb[cs] = to_bf16x8(*reinterpret_cast<const float4*>(p + 32 * cs),
-                                   *reinterpret_cast<const float4*>(p + 32 * cs + 4));
+    // k / q fragment of node block blk, column chunk cs: lane (r, q) holds
+    // row 16 blk + r (clamped), columns 32 cs + 8 q .. +7.  From global
+    // memory (a uniform base and a 32-bit lane offset) or, for k, from LDS.
+    const uint32_t lane_col = 16u * lq;
+    auto gfrag = [&](const uint16_t* base, int blk, int cs) __attribute__((always_inline)) {
+        const uint32_t row = (uint32_t)node_at(16 * blk + ln);
+        const uint32_t off = row * (uint32_t)(kq_row * 2) + lane_col + 64u * cs;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                              reinterpret_cast<const char*>(base) + off));
+    };
+    auto kfrag = [&](int blk, int cs) __attribute__((always_inline)) {
+        if constexpr (KLDS) {
+            const int row = node_at(16 * blk + ln);
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(row, 4 * cs + lq)));
+        } else {
+            return gfrag(Kb, blk, cs);
         }
-        // k / q fragment of node block blk, column chunk cs, from global memory
-        // (L2): the block's base is uniform, the lane's row / column a 32-bit
-        // offset (rows clamped to n - 1)
-        const uint32_t lane_col = 16u * lq;                 // bytes: 8 bf16 per lane group
-        auto frag = [&](const uint16_t* base, int blk, int cs) __attribute__((always_inline)) {
-            const uint32_t row = (uint32_t)node_at(16 * blk + ln);
-            const uint32_t off = row * (uint32_t)(kq_row * 2) + lane_col + 64u * cs;
-            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                  reinterpret_cast<const char*>(base) + off));
-        };
-        // Gram products of tile (t, s): A = K_s K_t^T, C = K_s Q_t^T (node j of
-        // block s in rows, node i of block t in columns)
-        auto tile_products = [&](const bf16x8 (&kt)[4], const bf16x8 (&qt)[4], const bf16x8 (&ks)[4],
-                                 f32x4& A, f32x4& C) __attribute__((always_inline)) {
-            A = z;
-            C = z;
+    };
+    // S0 rows col0 + r of the slice: lane (r, q) holds columns 32 cs + 8 q ..
+    // +7; the same registers are the B operand S0^T (for K S0^T) and the A
+    // operand S0 (for S0 Q^T)
+    auto s0frag = [&](int col0, int cs) __attribute__((always_inline)) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_s0 + row_chunk(col0 + ln, 4 * cs + lq)));
+    };
+    // ring slot x, as 8-byte (tiles) or 16-byte (right-hand sides) lane words
+    uint2* ring8 = s_big;
+    u32x4* ring16 = reinterpret_cast<u32x4*>(s_big);
+    auto slot_at = [&](int x) __attribute__((always_inline)) { return x < RING ? x : x - RING; };
+
+    // Nothing of the setup is in flight past this point (its loads are
+    // consumed; its cache stores have long completed), so the loops below
+    // start from an empty count and the compiler's waits in them count only
+    // their own requests.
+    wait_vmem_all();
+    if (solver) {
+        // ================= solve waves =================
+        const int g = wave;
+        const int c0 = cbase + 16 * g;                  // this wave's first value column
+        const __amdgpu_buffer_rsrc_t u_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(Ug, (short)0, N * kD * 4, kBufferFlags);
+        s16x4 uprev = {0, 0, 0, 0};
+        for (int t = 0; t < nblk; ++t) {
+            const int nts = s_tn[t];
+            const int base = s_gslot[t] % RING;
+            wait_flag_ge(&s_xready[t], 1);
+            // D_t R_t of this group: 16 bytes per lane in slot base + 2g
+            f32x4 acc = __builtin_bit_cast(f32x4, ring16[slot_at(base + 2 * g) * 32 + lane]);
+            // U_t = D_t R_t - sum_s X~_ts U_s (the tiles hold -X~); four tiles'
+            // operands are read before their products
+            int sl = slot_at(base + 8);
+            f32x4 acc2 = z;
+            int m = 0;
+            for (; m + 4 <= nts; m += 4) {
+                s16x4 xa[4], ub[4];
 #pragma unroll
-            for (int cs = 0; cs < 4; ++cs) {
-                A = mfma32(ks[cs], kt[cs], A);
-                C = mfma32(ks[cs], qt[cs], C);
-            }
-        };
-        // the products masked and decayed into -X / Y (bf16, tile layout) in the
-        // row buffers of parity t & 1; for s == t the diagonal X block in fp32,
-        // transposed, for the inversion
-        auto tile_store = [&](int t, int s, f32x4 A, f32x4 C) __attribute__((always_inline)) {
-            const int par = t & 1;
-            const int i = 16 * t + ln, j0 = 16 * s + 4 * lq;
-            const uint2 lw = *reinterpret_cast<const uint2*>(&s_last[j0]);     // last(j0 .. j0 + 3)
-            const int lst[4] = {(int)(int16_t)(lw.x & 0xffffu), (int)(int16_t)(lw.x >> 16),
-                                (int)(int16_t)(lw.y & 0xffffu), (int)(int16_t)(lw.y >> 16)};
-            uint32_t bits = 0u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bits |= (i < n && j0 + e < i && i <= lst[e]) ? 1u << e : 0u;
-            const float lgi = s_lg[i], bei = s_beta[i];
-            const float4 lgj = *reinterpret_cast<const float4*>(&s_lg[j0]);
-            const float lj[4] = {lgj.x, lgj.y, lgj.z, lgj.w};
-            float xv[4];
-            uint16_t yv[4], nxv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool anc = (bits >> e) & 1u;
-                const bool self = (j0 + e == i) && i < n;
-                const float d = (anc || self) ? __expf(lgi - lj[e]) : 0.f;
-                xv[e] = anc ? bei * d * A[e] : 0.f;
-                yv[e] = bf16_rne(d * C[e]);
-                nxv[e] = bf16_rne(-xv[e]);
-            }
-            const int tp = a32_pos(ln, 4 * lq);
-            *reinterpret_cast<uint2*>(&s_yrow[par][s * 256 + tp]) =
-                make_uint2(yv[0] | ((uint32_t)yv[1] << 16), yv[2] | ((uint32_t)yv[3] << 16));
-            if (s < t) {
-                *reinterpret_cast<uint2*>(&s_xrow[par][s * 256 + tp]) =
-                    make_uint2(nxv[0] | ((uint32_t)nxv[1] << 16), nxv[2] | ((uint32_t)nxv[3] << 16));
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s_xd[par][(4 * lq + e) * 16 + ln] = xv[e];   // [col][row]
-            }
-        };
-        // D = (I + X_tt)^-1 in fp32 by right-looking substitution, four lanes
-        // per column: lane 4c + q holds rows 4q .. 4q+3 of column c; step m
-        // broadcasts y_m from its owner within the lane quad and updates the
-        // rows below it
-        auto diag_inverse = [&](int t) __attribute__((always_inline)) {
-            const int par = t & 1;
-            const int c = lane >> 2, qd = lane & 3;
-            float acc[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = (4 * qd + e == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < 15; ++m) {
-                const float4 xc = *reinterpret_cast<const float4*>(&s_xd[par][m * 16 + 4 * qd]);
-                const float ym = quad_bcast(acc[m & 3], m >> 2);
-                const float xr[4] = {xc.x, xc.y, xc.z, xc.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {                     // rows below m only
-                    const float upd = fmaf(-xr[e], ym, acc[e]);
-                    acc[e] = 4 * qd + e > m ? upd : acc[e];
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s_dinv[par][a32_pos(4 * qd + e, c)] = bf16_rne(acc[e]);
-        };
-        // Row t's tiles: the diagonal tile first, then the occupied column
-        // blocks s < t, descending; Gram wave gw computes tiles gw, gw + NG, ...
-        auto tile_col = [&](int t, unsigned long long occ, int m) __attribute__((always_inline)) {
-            (void)occ;
-            return __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]);
-        };
-        // k / q fragments of a row (two sets, alternating by row) and, refilled
-        // once their products are issued, the k rows of this wave's first TPW
-        // tiles of the next row
-        struct RowOps {
-            bf16x8 k[4], q[4];
-        };
-        bf16x8 kp[TPW][4];
-        auto load_kq = [&](RowOps& o, int t) __attribute__((always_inline)) {
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs) {
-                o.k[cs] = frag(Kb, t, cs);
-                o.q[cs] = frag(Qb, t, cs);
-            }
-        };
-        // (blocks past the LDS cache only: a cached block's slot issues no
-        // load, and its products read the LDS copy)
-        auto load_tile = [&](int i, int t, unsigned long long occ, int ntile) __attribute__((always_inline)) {
-            const int m = gw + i * NG;
-            const int sc = m < ntile ? tile_col(t, occ, m) : t;
-            if constexpr (!KALL) {
-                if (sc >= KC) {                             // (uniform) cached blocks read LDS instead
-#pragma unroll
-                    for (int cs = 0; cs < 4; ++cs) kp[i][cs] = frag(Kb, sc, cs);
-                }
-            } else {
-                (void)sc;
-            }
-        };
-        auto kc_frag = [&](int sblk, int cs) __attribute__((always_inline)) {
-            return *reinterpret_cast<const bf16x8*>(s_kc + (min(sblk, KC - 1) * 4 + cs) * 512 + lane * 8);
-        };
-        // step t: row t + 1's tiles and projections (operands in cur, its first
-        // tiles' k rows in kp), requesting row t + 2's operands into nxt and kp;
-        // the last rows re-read the last row (harmless).  The first TPW tiles'
-        // products are issued together (independent chains), then their k
-        // registers are refilled, then they are masked and stored.
-        auto gstep = [&](int t, const RowOps& cur, RowOps& nxt) __attribute__((always_inline)) {
-            if (t + 1 < nblk) {
-                const int tr = t + 1, tn = min(t + 2, nblk - 1);
-                load_kq(nxt, tn);
-                const unsigned long long occ = row_occ(tr), occn = row_occ(tn);
-                const int ntile = __popcll(occ) + 1, ntn = __popcll(occn) + 1;
-                f32x4 Ap[TPW], Cp[TPW];
-#pragma unroll
-                for (int i = 0; i < TPW; ++i) {
-                    const int m = gw + i * NG;
-                    const int sc = m < ntile ? tile_col(tr, occ, m) : tr;    // (unused slot: a valid tile)
-                    bf16x8 ks[4];
-#pragma unroll
-                    for (int cs = 0; cs < 4; ++cs) {
-                        if constexpr (KALL) ks[cs] = kc_frag(sc, cs);
-                        else ks[cs] = sc < KC ? kc_frag(sc, cs) : kp[i][cs];
-                    }
-                    tile_products(cur.k, cur.q, ks, Ap[i], Cp[i]);
+                for (int e = 0; e < 4; ++e) {
+                    const int s = __builtin_amdgcn_readfirstlane((int)s_tcol[t][m + e]);
+                    xa[e] = __builtin_bit_cast(s16x4, ring8[slot_at(sl + e) * 64 + lane]);
+                    ub[e] = s == t - 1 ? uprev : __builtin_bit_cast(s16x4, s_u[s][g][lane]);
                 }
 #pragma unroll
-                for (int i = 0; i < TPW; ++i) load_tile(i, tn, occn, ntn);
-#pragma unroll
-                for (int i = 0; i < TPW; ++i) {
-                    const int m = gw + i * NG;
-                    if (m < ntile) tile_store(tr, tile_col(tr, occ, m), Ap[i], Cp[i]);
+                for (int e = 0; e < 4; ++e) {
+                    if (e & 1) acc2 = mfma16(xa[e], ub[e], acc2);
+                    else acc = mfma16(xa[e], ub[e], acc);
                 }
-                for (int m = gw + TPW * NG; m < ntile; m += NG) {
-                    const int sc = tile_col(tr, occ, m);
-                    bf16x8 k0[4];
-#pragma unroll
-                    for (int cs = 0; cs < 4; ++cs) k0[cs] = sc < KC ? kc_frag(sc, cs) : frag(Kb, sc, cs);
-                    f32x4 A0, C0;
-                    tile_products(cur.k, cur.q, k0, A0, C0);
-                    tile_store(tr, sc, A0, C0);
-                }
-                // projections of row t + 1 for column group pg
-                if (pg >= 0) {
-                    f32x4 pk = z, pq = z;
-#pragma unroll
-                    for (int cs = 0; cs < 4; ++cs) {
-                        pk = mfma32(cur.k[cs], sb[cs], pk);     // [node][r]
-                        pq = mfma32(sb[cs], cur.q[cs], pq);     // [r][node]
-                    }
-                    s_pk[tr & 1][pg][lane] = pk;
-                    s_pq[tr & 1][pg][lane] = pq;
-                }
-                if (gw == 0) diag_inverse(tr);                  // the diagonal tile is this wave's first
+                sl = slot_at(sl + 4);
             }
-            lds_barrier();
-        };
-        RowOps A, B;
-        load_kq(A, 0);
-        {
-            const unsigned long long occ0 = row_occ(0);
+            for (; m < nts; ++m) {
+                const int s = __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]);
+                const s16x4 xa = __builtin_bit_cast(s16x4, ring8[sl * 64 + lane]);
+                const s16x4 ub = s == t - 1 ? uprev : __builtin_bit_cast(s16x4, s_u[s][g][lane]);
+                acc = mfma16(xa, ub, acc);
+                sl = slot_at(sl + 1);
+            }
+            acc += acc2;
+            uprev = to_bf16x4(acc);
+            s_u[t][g][lane] = __builtin_bit_cast(uint2, uprev);
+            publish_set(&s_uready[g], t + 1, lane);    // also frees row t's ring slots
+            // the cache row: lane (n, q) holds rows 4q .. 4q+3 of column n;
+            // positions past the tree store outside the buffer and are dropped
 #pragma unroll
-            for (int i = 0; i < TPW; ++i) load_tile(i, 0, occ0, __popcll(occ0) + 1);
-        }
-        gstep(-1, A, B);                                // row 0; requests row 1
-        for (int t = 0; t < nblk; t += 2) {
-            gstep(t, B, A);
-            if (t + 1 < nblk) gstep(t + 1, A, B);
+            for (int mm = 0; mm < 4; ++mm) {
+                const int i = 16 * t + 4 * lq + mm;
+                const int off = i < n ? (node_at(i) * kD + c0 + ln) * 4 : 0x7fffffff;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mm]), u_rsrc, off, 0, 0);
+            }
         }
         return;
     }
 
-    // ================= solve waves =================
-    const int c0 = cbase + 16 * CG * wave;              // this wave's first value column
-    const s16x4 zero4 = {0, 0, 0, 0};
-    const bool hi_half = lq >= 2;
+    // ================= row owners =================
+    const int p = wave - kSolveWaves;                   // 0 .. kOwners - 1
+    // o rows of this tree and head: node v's row at v Hv kD elements
+    const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        O + vo_base, (short)0, ((n - 1) * Hv + 1) * kD * 2, kBufferFlags);
+    const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + vo_base + cbase;   // (+ 4 lq per lane below)
     s16x4 ident;
 #pragma unroll
     for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
-    bf16x8 up[CG][NPR];                                 // [U_2p; U_2p+1] as 16x16x32 B operands
+    for (int t = p; t < nblk; t += kOwners) {
+        const int nts = s_tn[t];
+        // operands, requested before the wait for ring space: k of the row,
+        // its v rows for the four groups (lane (r, q): columns 16 gg + 4q ..
+        // +3 of row r) and, when k comes from global memory, k of its first
+        // kChunk occupied blocks (from LDS they are read tile by tile)
+        bf16x8 kt[4], kx[kChunk][4];
+        uint2 vt[4];
 #pragma unroll
-    for (int g = 0; g < CG; ++g)
+        for (int cs = 0; cs < 4; ++cs) kt[cs] = kfrag(t, cs);
+        {
+            const uint32_t vr = (uint32_t)node_at(16 * t + ln) * (uint32_t)(vo_row * 2);   // (bytes, a uniform base)
 #pragma unroll
-        for (int p = 0; p < NPR; ++p) up[g][p] = zero8;
-
-    // row t of the blocked substitution and the output stage for this wave's
-    // two column groups, from the published tiles and projections of row t
-    // (parity t & 1); every tile read feeds both groups
-    auto solve_row = [&](int t, const uint2 (&vt)[CG]) __attribute__((always_inline)) {
-        const int par = t & 1;
-        const unsigned long long occ = row_occ(t);
-        const uint16_t* xr = s_xrow[par];
-        const uint16_t* yr = s_yrow[par];
-        f32x4 R[CG], pqT[CG];
+            for (int gg = 0; gg < 4; ++gg)
+                vt[gg] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(Vb) + vr + 8u * lq + 32u * gg);
+        }
+        // k of the occupied blocks m0 .. m0 + kChunk - 1 (past the row's: its own)
+        auto load_chunk = [&](int m0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int g = 0; g < CG; ++g) {
-            const f32x4 pk = s_pk[par][CG * wave + g][lane];
-            pqT[g] = s_pq[par][CG * wave + g][lane];
-            const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vt[g]), ident, z);
+            for (int e = 0; e < kChunk; ++e) {
+                const int s = m0 + e < nts ? (int)s_tcol[t][m0 + e] : t;
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) kx[e][cs] = kfrag(s, cs);
+            }
+        };
+        if constexpr (!KLDS) load_chunk(0);             // (from LDS: after the inverse, fewer live registers)
+        // this row's nodes (rows 4q .. 4q+3 of the accumulator layout)
+        float bei[4], lgi4[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            bei[m] = s_beta[16 * t + 4 * lq + m];
+            lgi4[m] = s_lg[16 * t + 4 * lq + m];
+        }
+#pragma unroll
+        for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_uready[gg], s_rstar[t]);
+        const int base = s_gslot[t] % RING;
+        // ---- D_t = (I + X_tt)^-1, with the row's right-hand-side slots as
+        // scratch (X_tt in fp32 at slot base, D as an A operand at base + 2) ----
+        float* xd = reinterpret_cast<float*>(&ring8[base * 64]);
+        uint16_t* dd = reinterpret_cast<uint16_t*>(&ring8[slot_at(base + 2) * 64]);
+        {
+            f32x4 gr = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) gr = mfma32(kt[cs], kt[cs], gr);   // lane (j, q): [i = 4q + m][j]
+            const int pj = 16 * t + ln;
+            const int lj = s_last[pj];
+            const float lgj = s_lg[pj];
+            float4 xv;
+            float* xp = reinterpret_cast<float*>(&xv);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int i = 16 * t + 4 * lq + m;
-                R[g][m] = s_beta[i] * (vd[m] - __expf(s_lg[i]) * pk[m]);
+                const int pi = 16 * t + 4 * lq + m;
+                const bool anc = (pj < pi) & (pi <= lj);
+                const float x = bei[m] * __expf(fminf(lgi4[m] - lgj, 0.f)) * gr[m];
+                xp[m] = anc ? x : 0.f;
             }
-        }
-        // R_t += sum_{s<t} (-X_ts) U_s over occupied tiles, two blocks per MFMA;
-        // even and odd pairs accumulate apart (four independent chains)
-        f32x4 R2[CG];
+            *reinterpret_cast<float4*>(&xd[ln * 16 + 4 * lq]) = xv;      // [col j][row i]
+            // fp32 forward substitution, four lanes per column: lane 4c + qd
+            // holds rows 4qd .. 4qd+3 of column c; step m broadcasts y_m from
+            // its owner within the lane quad and updates the rows below it
+            const int c = lane >> 2, qd = lane & 3;
+            float accd[4];
 #pragma unroll
-        for (int g = 0; g < CG; ++g) R2[g] = z;
+            for (int e = 0; e < 4; ++e) accd[e] = (4 * qd + e == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int p = 0; p < NPR; ++p) {
-            const int s = 2 * p;
-            if (s < t) {
-                const bool o0 = (occ >> s) & 1ull;
-                const bool o1 = s + 1 < t && ((occ >> (s + 1)) & 1ull);
-                if (o0 || o1) {
-                    bf16x8 nx = *reinterpret_cast<const bf16x8*>(xr + s * 256 + lane * 8);
-                    if (!(hi_half ? o1 : o0)) nx = zero8;
+            for (int m = 0; m < 15; ++m) {
+                const float4 xc = *reinterpret_cast<const float4*>(&xd[m * 16 + 4 * qd]);
+                const float ym = quad_bcast(accd[m & 3], m >> 2);
+                const float xr[4] = {xc.x, xc.y, xc.z, xc.w};
 #pragma unroll
-                    for (int g = 0; g < CG; ++g) {
-                        if (p & 1) R2[g] = mfma32(nx, up[g][p], R2[g]);
-                        else R[g] = mfma32(nx, up[g][p], R[g]);
-                    }
+                for (int e = 0; e < 4; ++e) {                 // rows below m only
+                    const float upd = fmaf(-xr[e], ym, accd[e]);
+                    accd[e] = 4 * qd + e > m ? upd : accd[e];
                 }
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
         }
+        const s16x4 dt = __builtin_bit_cast(s16x4, reinterpret_cast<const uint2*>(dd)[lane]);   // A: D; B: D^T
+        // ---- the row's -X~ tiles, kChunk at a time (their reads and products
+        // independent of each other) ----
+        for (int m0 = 0; m0 < nts; m0 += kChunk) {
+            if (m0 > 0 || KLDS) load_chunk(m0);
+            int sc[kChunk];
+            f32x4 gr[kChunk];
+            int lj[kChunk];
+            float lgj[kChunk];
 #pragma unroll
-        for (int g = 0; g < CG; ++g) R[g] += R2[g];
-        const bf16x8 di = *reinterpret_cast<const bf16x8*>(s_dinv[par] + (ln + 16 * (lq & 1)) * 8);
-        const int node = 16 * t + ln;
+            for (int e = 0; e < kChunk; ++e) {
+                sc[e] = m0 + e < nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m0 + e]) : t;
+                lj[e] = s_last[16 * sc[e] + ln];
+                lgj[e] = s_lg[16 * sc[e] + ln];
+                gr[e] = z;
+            }
 #pragma unroll
-        for (int g = 0; g < CG; ++g) {
+            for (int cs = 0; cs < 4; ++cs)
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) gr[e] = mfma32(kt[cs], kx[e][cs], gr[e]);   // lane (j, q): [i = 4q + m][j]
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) {
+                s16x4 xa;                               // X^T as an A operand
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const int pi = 16 * t + 4 * lq + mm;
+                    const bool anc = (sc[e] < t) & (pi <= lj[e]);   // (pj < pi: s < t)
+                    const float x = bei[mm] * __expf(fminf(lgi4[mm] - lgj[e], 0.f)) * gr[e][mm];
+                    xa[mm] = (short)bf16_rne(anc ? x : 0.f);
+                }
+                const f32x4 xt = mfma16(xa, dt, z);     // X^T D^T: lane (i, q) holds X~[i][4q + m]
+                s16x4 nx;
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) nx[mm] = (short)bf16_rne(-xt[mm]);
+                if (m0 + e < nts) ring8[slot_at(base + 8 + m0 + e) * 64 + lane] = __builtin_bit_cast(uint2, nx);
+            }
+        }
+        bf16x8 qt[4];                                   // q of the row, for the outputs
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) qt[cs] = gfrag(Qb, t, cs);
+        // ---- D_t R_t of the four groups, R_t = diag(beta)(V_t - diag(e^G) K_t S0^T);
+        // V moves into the accumulator layout by an exact product with I ----
+        f32x4 rt[4];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            f32x4 ks = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) ks = mfma32(kt[cs], s0frag(16 * gg, cs), ks);   // [node][col]
+            const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vt[gg]), ident, z);
+            f32x4 R;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) R[m] = bei[m] * (vd[m] - __expf(lgi4[m]) * ks[m]);
             s16x4 rh, rl;
-            split4(R[g], rh, rl);
-            const bf16x8 rr = stack_pair(rh, rl);
-            const f32x4 U = mfma32(di, rr, z);
-            const f32x4 UT = mfma32(rr, di, z);
-            const s16x4 ut = to_bf16x4(U);
+            split4(R, rh, rl);
+            rt[gg] = mfma16(dt, rl, mfma16(dt, rh, z));
+        }
+        // (the scratch in slots base .. base + 2 is read: D is in registers)
 #pragma unroll
-            for (int p = 0; p < NPR; ++p) {
-                if (p == (t >> 1)) {
-                    if (t & 1)
-                        up[g][p] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, up[g][p]) |
-                                                                  __builtin_bit_cast(u32x4, stack_pair(zero4, ut)));
-                    else
-                        up[g][p] = stack_pair(ut, zero4);
+        for (int gg = 0; gg < 4; ++gg) ring16[slot_at(base + 2 * gg) * 32 + lane] = __builtin_bit_cast(u32x4, rt[gg]);
+        publish_set(&s_xready[t], 1, lane);
+        // (q is used only below this point: its products may not be moved
+        // ahead of the publication, which would then wait for its loads)
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) asm volatile("" : "+v"(qt[cs]));
+        // ---- outputs O_t = e^G Q_t S0^T + sum_{s <= t} Y_ts U_s ----
+        f32x4 oc[4];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            oc[gg] = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) oc[gg] = mfma32(s0frag(16 * gg, cs), qt[cs], oc[gg]);   // [col][node]
+        }
+        const int pi = 16 * t + ln;                     // this lane's node (column of the products)
+        const float lgi = s_lg[pi];
+        const float egi = __expf(lgi);
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) oc[gg] *= egi;
+        // Y tiles four at a time: their Gram products first, then the wait for
+        // the last of their rows of U (rows are published in order), then the
+        // products with U of every column group
+        auto y_group = [&](const int (&sc)[kChunk], int cnt, const bf16x8 (&ks)[kChunk][4]) __attribute__((always_inline)) {
+            f32x4 gr[kChunk];
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) gr[e] = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs)
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e) gr[e] = mfma32(ks[e][cs], qt[cs], gr[e]);   // lane (i, q): [j = 4q + m][i]
+            s16x4 yb[kChunk];                           // Y^T as B operands
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e)
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const int pj = 16 * sc[e] + 4 * lq + mm;
+                    const int lpj = s_last[pj];
+                    const bool anc = (e < cnt) & (pj <= pi) & (pi <= lpj);
+                    const float y = __expf(fminf(lgi - s_lg[pj], 0.f)) * gr[e][mm];
+                    yb[e][mm] = (short)bf16_rne(anc ? y : 0.f);
                 }
+            int smax = sc[0];
+#pragma unroll
+            for (int e = 1; e < kChunk; ++e) smax = e < cnt ? max(smax, sc[e]) : smax;
+#pragma unroll
+            for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_uready[gg], smax + 1);
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e)
+                if (e < cnt)
+#pragma unroll
+                    for (int gg = 0; gg < 4; ++gg)
+                        oc[gg] = mfma16(__builtin_bit_cast(s16x4, s_u[sc[e]][gg][lane]), yb[e], oc[gg]);
+        };
+        // the occupied blocks s < t, then the diagonal block (its wait is for
+        // the solve's row t)
+        const int nall = nts + 1;
+        for (int m0 = 0; m0 < nall; m0 += kChunk) {
+            // (a single chunk of tiles is still in registers, and past the row's
+            // blocks it holds the row's own; a diagonal block left alone in a
+            // chunk of its own takes the row's k)
+            if (nts > kChunk || (KLDS && nts == 0)) {
+                load_chunk(m0);
+            } else if (m0 > 0) {
+#pragma unroll
+                for (int e = 0; e < kChunk; ++e)
+#pragma unroll
+                    for (int cs = 0; cs < 4; ++cs) kx[e][cs] = kt[cs];
             }
-            if (node < n) *reinterpret_cast<f32x4*>(Ug + (size_t)node_at(node) * kD + c0 + 16 * g + 4 * lq) = UT;
-        }
-        // O_t^T = e^G P_Q^T + sum_{s<=t} U_s^T Y_ts^T over occupied tiles
-        f32x4 Oc[CG], Oc2[CG];
+            int sc[kChunk];
 #pragma unroll
-        for (int g = 0; g < CG; ++g) Oc[g] = Oc2[g] = z;
-#pragma unroll
-        for (int p = 0; p < NPR; ++p) {
-            const int s = 2 * p;
-            if (s <= t) {
-                const bool o0 = s == t || ((occ >> s) & 1ull);
-                const bool o1 = s + 1 == t || (s + 1 < t && ((occ >> (s + 1)) & 1ull));
-                if (o0 || o1) {
-                    bf16x8 yt = *reinterpret_cast<const bf16x8*>(yr + s * 256 + lane * 8);
-                    if (!(hi_half ? o1 : o0)) yt = zero8;
-#pragma unroll
-                    for (int g = 0; g < CG; ++g) {
-                        if (p & 1) Oc2[g] = mfma32(up[g][p], yt, Oc2[g]);
-                        else Oc[g] = mfma32(up[g][p], yt, Oc[g]);
-                    }
-                }
+            for (int e = 0; e < kChunk; ++e) {
+                const int m = m0 + e;
+                sc[e] = m < nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]) : t;
             }
+            y_group(sc, min(kChunk, nall - m0), kx);
         }
+        // (positions past the tree store outside the buffer and are dropped)
+        const int orow = pi < n ? (node_at(pi) * Hv * kD + cbase + 4 * lq) * 2 : 0x7fffffff;
 #pragma unroll
-        for (int g = 0; g < CG; ++g) Oc[g] += Oc2[g];
-        if (node < n) {
-            const float egn = __expf(s_lg[node]);
-#pragma unroll
-            for (int g = 0; g < CG; ++g) {
-                f32x4 OT;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) OT[m] = egn * pqT[g][m] + Oc[g][m];
-                const uint32_t lo = (uint32_t)bf16_rne(OT[0]) | ((uint32_t)bf16_rne(OT[1]) << 16);
-                const uint32_t hi = (uint32_t)bf16_rne(OT[2]) | ((uint32_t)bf16_rne(OT[3]) << 16);
-                *reinterpret_cast<uint2*>(O + vo_base + (size_t)node_at(node) * vo_row + c0 + 16 * g + 4 * lq) =
-                    make_uint2(lo, hi);
-            }
-        }
-    };
-    // v of row t + 1 is requested before row t's stores (loads and stores
-    // retire in order, so waiting for it never waits for those stores)
-    const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + vo_base + c0 + 4 * lq;
-    auto load_v = [&](int t, uint2 (&v)[CG]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int g = 0; g < CG; ++g)
-            v[g] = *reinterpret_cast<const uint2*>(Vp + (size_t)node_at(16 * t + ln) * vo_row + 16 * g);
-    };
-    uint2 va[CG], vb[CG];
-    load_v(0, va);
-    lds_barrier();
-    for (int t = 0; t < nblk; t += 2) {
-        load_v(min(t + 1, nblk - 1), vb);
-        solve_row(t, va);
-        lds_barrier();
-        if (t + 1 < nblk) {
-            load_v(min(t + 2, nblk - 1), va);
-            solve_row(t + 1, vb);
-            lds_barrier();
+        for (int gg = 0; gg < 4; ++gg) {
+            u32x2 w;
+            w[0] = (uint32_t)bf16_rne(oc[gg][0]) | ((uint32_t)bf16_rne(oc[gg][1]) << 16);
+            w[1] = (uint32_t)bf16_rne(oc[gg][2]) | ((uint32_t)bf16_rne(oc[gg][3]) << 16);
+            __builtin_amdgcn_raw_buffer_store_b64(w, o_rsrc, orow + 32 * gg, 0, 0);
         }
     }
 }
@@ -781,13 +901,13 @@ bool verify_large_supported(const VerifyArgs& a, int io) {
 hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream) {
     (void)io;
     VerifyArgs copy = a;
-    // two column slices of 64 value columns per (sequence, value head), eight
-    // waves each: two solve waves of 32 columns (trees up to 256 nodes) or four
-    // of 16 (up to 512), each holding 16 stacked U pairs, one wave per SIMD
-    int csplit = 2;
+    // two 64-column slices per (sequence, value head); a unit's slices are
+    // 8 workgroups apart, so both run on one XCD
+    int units = a.B * a.Hv;
+    const unsigned grid = 16u * (unsigned)((units + 7) / 8);
     const void* fn = a.N <= 256 ? (const void*)verify_large_kernel<16> : (const void*)verify_large_kernel<32>;
-    void* args[] = {&copy, &csplit};
-    return hipLaunchKernel(fn, dim3((unsigned)(a.B * a.Hv * csplit)), dim3(512), args, 0, stream);
+    void* args[] = {&copy, &units};
+    return hipLaunchKernel(fn, dim3(grid), dim3(kLargeThreads), args, 0, stream);
 }
 
 }  // namespace gdn
