@@ -20,9 +20,13 @@ def record(name, err):
 
 
 def rel_l2(x, ref):
+    """Relative L2 error; infinite when either side holds a NaN or an infinity,
+    so that a max over units (which keeps its first argument when the second
+    is NaN) and a tolerance check both see it."""
     x = np.asarray(x, np.float64).ravel()
     ref = np.asarray(ref, np.float64).ravel()
-    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-30))
+    e = float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-30))
+    return e if np.isfinite(e) else float("inf")
 
 
 def gpu_run(parent, accepted, lay, io, Hk, Hv, in_place=False, device="cuda"):
@@ -84,9 +88,9 @@ def unit_errors(gpu, ref, Hk, Hv):
             worst["o"] = max(worst["o"], rel_l2(gpu["o"][b, :, h], ref["o"][b, :, h]))
             worst["u"] = max(worst["u"], rel_l2(gpu["u"][b, h], ref["u"][b, h]))
             worst["S_commit"] = max(worst["S_commit"],
-                                    rel_l2(gpu["S_commit"][b, h], ref["S_commit"][b, h]))
+                                      rel_l2(gpu["S_commit"][b, h], ref["S_commit"][b, h]))
             worst["log_gamma"] = max(worst["log_gamma"],
-                                     rel_l2(gpu["log_gamma"][b, h], ref["log_gamma"][b, h]))
+                                       rel_l2(gpu["log_gamma"][b, h], ref["log_gamma"][b, h]))
     return worst
 
 

@@ -6,35 +6,36 @@
 // a tiled forward substitution and the output stage, fused), laid out for
 // trees whose interaction tiles do not fit in LDS.  One workgroup per
 // (sequence, value head, 64-column slice), twelve waves in two roles that
-// meet through LDS flags, with no barrier after the setup:
+// meet through LDS counters, with no barrier after the setup:
 //
-//  * setup (all waves): the parent row is checked, the tree's nodes are
-//    relabelled in preorder (every subtree one run of positions, so ancestry
-//    is an interval test and a block row's ancestors sit in few column
-//    blocks), the path log-gates are summed by pointer doubling, and the
-//    tree's workgroups share writing its ancestor rows, depths and status.
-//    The workgroup's global inputs are requested first (for trees of up to
-//    256 nodes the k rows, stored into LDS at its end), so their latency
-//    overlaps it; its barriers order LDS only.
-//  * row owners (waves 4 .. 11, 16-position block rows round robin): for a
-//    row t, the diagonal block's inverse D_t = (I + X_tt)^-1 (fp32, kept bf16),
-//    every occupied tile of the row already multiplied by it,
-//    X~_ts = D_t X_ts, and the right-hand side D_t R_t with
-//    R_t = diag(beta)(V_t - diag(e^G) K_t S0^T) (bf16 hi + lo parts of R),
-//    into a ring of LDS slots.  With those the substitution of a row is
-//    U_t = D_t R_t - sum_s X~_ts U_s: one chain of 16x16x16 products, the last
-//    of which waits for the previous row.  Then the row's outputs
-//    O_t = e^G Q_t S0^T + sum_{s <= t} Y_ts U_s, with the Y tiles formed from
-//    the same k operands and U read from LDS as the solve publishes it.
-//  * solve (waves 0 .. 3, 16 value columns each): row by row, the chain of
-//    the row's X~ products on D_t R_t; U_t goes to LDS (bf16, for later rows
-//    and the outputs) and to the cache (fp32).  The solve waves read no
-//    global memory.
+//  * setup (all waves): the parent row is checked; one wave relabels the
+//    tree's nodes in preorder (every subtree one run of positions, so
+//    ancestry is an interval test and a block row's ancestors sit in few
+//    column blocks) while another sums the path log-gates, both by pointer
+//    jumping within the wave; the tree's workgroups share writing its
+//    ancestor rows, depths and status.  The workgroup's global inputs are
+//    requested first (for trees of up to 256 nodes the k rows, stored into
+//    LDS at its end), so their latency overlaps it; its barriers order LDS
+//    only.
+//  * producers (waves 4 .. 11): the work of all block rows as one row-major
+//    list of items dealt round robin, each item's global operands requested
+//    one item ahead.  A row's first item forms the diagonal block's inverse
+//    D_t = (I + X_tt)^-1 (fp32 substitution, kept bf16) and its output tile
+//    Y_tt; the others form, for a few occupied column blocks s, the tiles
+//    -X_ts and Y_ts from one read of k_s.  Tiles go to a ring of LDS slots,
+//    D_t to a table; a per-row counter says when the row is complete.
+//  * solve (waves 0 .. 3, 16 value columns each): row by row, the
+//    right-hand side R_t = diag(beta)(V_t - diag(e^G) K_t S0^T) and the
+//    substitution U_t = D_t (R_t - sum_s X_ts U_s), the row's outputs
+//    O_t = e^G Q_t S0^T + sum_{s <= t} Y_ts U_s, then the ring slots are
+//    released.  A column group needs no other group's U, so the four solve
+//    waves never wait for each other.
 //
 // Inputs are gathered and outputs written at the caller's node indices.
 #include "gdn_common.hpp"
 #include "launch.hpp"
 #include "mfma_tiles.hpp"
+
 
 namespace gdn {
 
@@ -44,9 +45,7 @@ constexpr int kLargeMaxN = 512;      // largest tree of this path
 constexpr int kLargeWaves = 12;
 constexpr int kLargeThreads = 64 * kLargeWaves;
 constexpr int kSolveWaves = 4;       // one 16-column group each: 64 columns per workgroup
-constexpr int kOwners = kLargeWaves - kSolveWaves;
-constexpr int kChunkG = 3;           // k operands of a row's tiles requested together (global memory)
-constexpr int kChunkL = 2;           // ... read together (LDS)
+constexpr int kProducers = kLargeWaves - kSolveWaves;
 
 // buffer resources for stores that must not branch on a lane's validity: a
 // lane's store past the buffer is dropped
@@ -96,48 +95,54 @@ template <int NB>
 struct LargeShape {
     static constexpr int NP = 16 * NB;
     static constexpr bool KLDS = NB <= 16;              // the k rows sit in LDS
+    static constexpr int C = KLDS ? 2 : 1;              // occupied column blocks per producer item
     static constexpr int WC = NP / 32;                  // words of a children row
-    static constexpr int SCRATCH = ((NP + 1) * WC + 5 * NP + 1) * 4;   // the preorder's
-    static constexpr int RING0 = NB <= 16 ? 84 * 512 : 136 * 512;
-    static constexpr int BIG = RING0 > SCRATCH ? RING0 : SCRATCH;
-    static constexpr int RING = BIG / 1024 * 2;         // 512-byte slots in flight (even)
+    static constexpr int SCRATCH = ((NP + 1) * WC + (NP + 2) + 8 * NP) * 4;   // the preorder's
+    static constexpr int RING = NB <= 16 ? 84 : 112;    // 512-byte tile slots
+    static constexpr int BIG = RING * 512 > SCRATCH ? RING * 512 : SCRATCH;
+    // items: per row one for the diagonal block and one per C occupied blocks
+    static constexpr int ITEMS = NB + (C == 1 ? NB * (NB - 1) / 2 : (NB / 2) * (NB / 2));
 };
 
 template <int NB>
 __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyArgs a, int units) {
     using L = LargeShape<NB>;
-    constexpr int kChunk = L::KLDS ? kChunkL : kChunkG;
     constexpr int NP = L::NP;
     constexpr int NT = kLargeThreads;
     constexpr bool KLDS = L::KLDS;
+    constexpr int C = L::C;
     constexpr int WC = L::WC;
     constexpr int SCRATCH = L::SCRATCH;
     constexpr int BIG = L::BIG;
     constexpr int RING = L::RING;
     constexpr int PL = (NP + NT - 1) / NT;              // tree entries per thread
-    // the ring: per row, D_t R_t of the four column groups (two slots each,
-    // 16 bytes per lane) and the row's -X~ tiles (8 bytes per lane each);
-    // during the setup the preorder's scratch
+    static_assert(2 * (NB - 1) + 1 <= RING, "a row's tiles fit the ring");
+    static_assert(NB <= 32 && NB % 2 == 0, "block rows in one wave's lanes");
+    // the ring of tile slots (8 bytes per lane each); during the setup the
+    // preorder's scratch
     __shared__ __attribute__((aligned(16))) uint2 s_big[BIG / 8];
     __shared__ __attribute__((aligned(16))) uint16_t s_k[KLDS ? NP * kD : 8];   // k rows, node order
-    __shared__ __attribute__((aligned(16))) uint16_t s_s0[64 * kD];            // the slice's S0 rows, bf16
     __shared__ __attribute__((aligned(16))) uint2 s_u[NB][kSolveWaves][64];   // U_t, bf16 B operands
+    __shared__ __attribute__((aligned(16))) uint2 s_d[NB][64];               // D_t, bf16 A operands
+    __shared__ __attribute__((aligned(16))) float s_xd[kProducers][256];     // each producer's X_tt, fp32 [col][row]
     __shared__ __attribute__((aligned(16))) float s_lg[NP];
     __shared__ __attribute__((aligned(16))) float s_beta[NP];
     __shared__ __attribute__((aligned(16))) int32_t s_jump[NP];
     __shared__ uint16_t s_perm[NP];                     // position -> node
     __shared__ __attribute__((aligned(8))) int16_t s_last[NP];   // position of the last descendant
     __shared__ int16_t s_hop[NP];                       // nodes on the path to the root (depth + 1)
-    __shared__ int s_mlast[NB];                         // largest s_last of each block
-    __shared__ uint8_t s_tcol[NB][NB];                  // row t's occupied blocks s < t, ascending
+    __shared__ __attribute__((aligned(16))) int s_mlast[NB];   // largest s_last of each block
+    __shared__ __attribute__((aligned(16))) uint8_t s_tcol[NB][NB];   // row t's occupied blocks s < t, ascending
     __shared__ int s_tn[NB];                            // their number
-    __shared__ int s_gslot[NB + 1];                     // first tile of row t, counted over all rows
-    __shared__ int s_rstar[NB];                         // rows consumed before row t's ring slots are free
-    __shared__ int s_xready[NB];                        // row t's ring slots published
-    __shared__ int s_uready[kSolveWaves];               // rows finished by each solve wave
-    __shared__ int s_more[9];                           // per-round flags of the three doubling loops
+    __shared__ __attribute__((aligned(16))) int s_gslot[NB + 4];   // first slot of row t, counted over all rows
+    __shared__ int s_rstar[NB];                         // rows released before row t's slots are free
+    __shared__ uint16_t s_items[L::ITEMS];              // producer items: row | (item of the row << 8)
+    __shared__ int s_nitems;
+    __shared__ int s_done[NB];                          // row t's items finished (complete at s_tn[t] + 1)
+    __shared__ int s_oready[kSolveWaves];               // rows finished by each solve wave
     __shared__ int s_bad;                               // first node with an invalid parent
     __shared__ int s_notchain;                          // some node's parent is not the node before it
+    __shared__ int s_more[3];                           // per-round "not done" flags of the jumping loops
 
     const int N = a.N, Hv = a.Hv, Hk = a.Hk, G = Hv / Hk;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lq = lane >> 4;
@@ -174,14 +179,17 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         g_r[k] = v ? a.g[(rows.row0 + i) * Hv + h] : 1.f;
         beta_r[k] = v ? a.beta[(rows.row0 + i) * Hv + h] : 0.f;
     }
-    // the slice's 64 S0 rows (fp32; converted into LDS after the setup)
-    constexpr int S0L = 64 * kD / 4 / NT + 1;           // float4 loads per thread
-    float4 s0_r[S0L];
-    const float* S0p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)cbase * kD;
+    // a solve wave's 16 S0 rows (fp32; its bf16 operands are formed after the
+    // setup): lane (r, q) takes row cbase + 16 wave + r, columns 32 cs + 8 q .. +7
+    float4 s0_r[8];
+    if (solver) {
+        const float* S0p =
+            a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(cbase + 16 * wave + ln) * kD + 8 * lq;
 #pragma unroll
-    for (int k = 0; k < S0L; ++k) {                     // (float4 index in the 64 x 128 slice, clamped)
-        const int x = min(tid + k * NT, 64 * kD / 4 - 1);
-        s0_r[k] = *reinterpret_cast<const float4*>(S0p + 4 * x);
+        for (int cs = 0; cs < 4; ++cs) {
+            s0_r[2 * cs] = *reinterpret_cast<const float4*>(S0p + 32 * cs);
+            s0_r[2 * cs + 1] = *reinterpret_cast<const float4*>(S0p + 32 * cs + 4);
+        }
     }
     // k rows of the tree (node order, rows past the tree copy row n - 1) into
     // registers, written to LDS at the end of the setup: one 1 KB unit is
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             k_r[kk] = *reinterpret_cast<const u32x4*>(Kb + (size_t)srow * kq_row + ((pc ^ (row & 15)) << 3));
         }
     }
-    // (the tree's values are used only below: their arithmetic may not be
+    // (the loaded values are used only below: their arithmetic may not be
     // moved up to the loads, where it would wait for them before the other
     // requests are out)
 #pragma unroll
@@ -252,11 +260,11 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // tile masks need no ancestor rows.  Outputs stay in the caller's order.
     // Scratch while it is built: the ring area.
     uint32_t* s_cm = reinterpret_cast<uint32_t*>(s_big);          // [NP + 1][WC]; row NP: the roots
-    int32_t* s_fc = reinterpret_cast<int32_t*>(s_cm + (NP + 1) * WC);   // [NP + 1] first child, -1: none
-    int32_t* s_nx = s_fc + (NP + 1);                    // [NP] node after the subtree (n: none; -1 pending)
-    int32_t* s_ptr = s_nx + NP;                         // [NP] doubling link
-    int32_t* s_rk = s_ptr + NP;                         // [NP] list distance to the last node
-    int32_t* s_sc = s_rk + NP;                          // [NP] list link (n: past the last node)
+    int32_t* s_fc = reinterpret_cast<int32_t*>(s_cm + (NP + 1) * WC);   // [NP + 1] first child (NP: none)
+    // pointer-jumping entries, each read and written as one 8-byte word:
+    int2* s_na = reinterpret_cast<int2*>(s_fc + (NP + 2));   // [NP] (node after the subtree: n none, -1 pending; link)
+    int2* s_gj = s_na + NP;                             // [2][NP] (link | hops << 16, summed log-gate bits)
+    int2* s_rs = s_gj + 2 * NP;                         // [NP] (list distance to the last node, list link)
     static_assert(SCRATCH <= BIG, "preorder scratch fits the ring area");
     bool not_chain = false;                             // a chain is its own preorder
 #pragma unroll
@@ -274,195 +282,139 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         }
     }
     for (int x = tid; x < (NP + 1) * WC; x += NT) s_cm[x] = 0u;
-    if constexpr (KLDS) {
-#pragma unroll
-        for (int kk = 0; kk < KI; ++kk) {
-            const int u = wave + kk * kLargeWaves;
-            if (u < NP / 4) *reinterpret_cast<u32x4*>(s_k + 4 * u * kD + 8 * lane) = k_r[kk];
-        }
-    }
-    // the slice's S0 rows as bf16 (row c at LDS row c, chunks swizzled)
-#pragma unroll
-    for (int k = 0; k < S0L; ++k) {
-        const int x = tid + k * NT;
-        if (x < 64 * kD / 4) {
-            const int r = x >> 5, c4 = x & 31;          // row, float4 within the row
-            uint2 w;
-            w.x = (uint32_t)bf16_rne(s0_r[k].x) | ((uint32_t)bf16_rne(s0_r[k].y) << 16);
-            w.y = (uint32_t)bf16_rne(s0_r[k].z) | ((uint32_t)bf16_rne(s0_r[k].w) << 16);
-            *reinterpret_cast<uint2*>(s_s0 + row_chunk(r, c4 >> 1) + 4 * (c4 & 1)) = w;
-        }
-    }
-    if (tid < 9) s_more[tid] = 0;
-    if (tid < NB) s_xready[tid] = 0;
-    if (tid < kSolveWaves) s_uready[tid] = 0;
+    for (int x = tid; x <= NP; x += NT) s_fc[x] = NP;
+    if (tid < NB) s_done[tid] = 0;
+    if (tid < kSolveWaves) s_oready[tid] = 0;
+    if (tid < 3) s_more[tid] = 0;
     // a chain skips the construction (nt = 0): the identity and last = n - 1
     if (not_chain) s_notchain = 1;
     lds_barrier();
     const int nt = s_notchain ? n : 0;
-    for (int i = tid; i < nt; i += NT) {                // bit i of its parent's children row
+    for (int i = tid; i < nt; i += NT) {                // bit i of its parent's children row; first child
         const int p = s_jump[i];
-        atomicOr(&s_cm[(p < 0 ? NP : p) * WC + (i >> 5)], 1u << (i & 31));
+        const int pr = p < 0 ? NP : p;
+        atomicOr(&s_cm[pr * WC + (i >> 5)], 1u << (i & 31));
+        atomicMin(&s_fc[pr], i);
     }
     lds_barrier();
-    for (int v = tid; v <= NP; v += NT) {               // first child (row NP: the first root)
-        int f = -1;
-        if (v < nt || v == NP)
-            for (int w = 0; w < WC; ++w) {
-                const uint32_t x = s_cm[v * WC + w];
-                if (x) {
-                    f = 32 * w + __builtin_ctz(x);
-                    break;
-                }
-            }
-        s_fc[v] = f;
-    }
     for (int i = tid; i < nt; i += NT) {                // next sibling, else pending
+        // (the parent's whole children row is read at once: no dependent
+        // loads however far the next sibling is)
         const int p = s_jump[i];
         const uint32_t* r = s_cm + (p < 0 ? NP : p) * WC;
-        int nsib = -1;
-        uint32_t x = r[i >> 5] & ~((2u << (i & 31)) - 1u);   // siblings above i in its word
-        for (int w = i >> 5;;) {
-            if (x) {
-                nsib = 32 * w + __builtin_ctz(x);
-                break;
-            }
-            if (++w >= WC) break;
-            x = r[w];
+        uint32_t wv[WC];
+#pragma unroll
+        for (int w = 0; w < WC; w += 4) {
+            const uint4 x4 = *reinterpret_cast<const uint4*>(r + w);
+            wv[w] = x4.x;
+            wv[w + 1] = x4.y;
+            wv[w + 2] = x4.z;
+            wv[w + 3] = x4.w;
         }
-        s_nx[i] = nsib >= 0 ? nsib : (p < 0 ? n : -1);
-        s_ptr[i] = p;
+        int nsib = -1;
+#pragma unroll
+        for (int w = WC - 1; w >= 0; --w) {             // the lowest set bit above i wins
+            const int lo = 32 * w;
+            uint32_t x = wv[w];
+            if (lo + 31 <= i) x = 0u;
+            else if (lo <= i) x &= ~((2u << (i & 31)) - 1u);
+            nsib = x ? lo + __builtin_ctz(x) : nsib;
+        }
+        s_na[i] = make_int2(nsib >= 0 ? nsib : (p < 0 ? n : -1), p);
+    }
+    static_assert(NP <= NT, "one tree entry per thread");
+    if (nt && tid < NP) {
+        const int j = s_jump[tid];
+        s_gj[tid] = make_int2((j & 0xffff) | ((int)s_hop[tid] << 16), __float_as_int(s_lg[tid]));
     }
     lds_barrier();
-    // the node after a subtree: the subtree root's next sibling, else its
-    // parent's (pointer doubling up the path; a root-level node always has one)
-    for (int rd = 0;; ++rd) {
-        int res[PL], nq[PL];
-        bool more = false;
-#pragma unroll
-        for (int k = 0; k < PL; ++k) {
-            const int i = tid + k * NT;
-            res[k] = -2;
-            nq[k] = 0;
-            if (i < nt && s_nx[i] < 0) {
-                const int q = s_ptr[i];
-                const int rq = s_nx[q];
-                if (rq >= 0) res[k] = rq;
-                else {
-                    nq[k] = s_ptr[q];
-                    res[k] = -1;
-                    more = true;
-                }
-            }
-        }
+    // Pointer jumping, one node per thread and one barrier per round.  The
+    // integer entries are updated in place: a read of another node's entry
+    // sees it whole, before or after that node's update in the same round,
+    // and either is a valid jump.  The log-gate sums alternate between two
+    // copies, so that every round adds the same segments whatever the timing
+    // and the sums come out the same in every run.
+    // A round ends with one LDS-only barrier: a node with work left raises
+    // flag rd % 3, and flag (rd + 1) % 3, the next round's, is cleared before
+    // the barrier (no thread still reads it: all have passed the previous
+    // round's barrier).
+    auto round_more = [&](int rd, bool more) __attribute__((always_inline)) {
         if (tid == 0) s_more[(rd + 1) % 3] = 0;
-        lds_barrier();
-#pragma unroll
-        for (int k = 0; k < PL; ++k) {
-            const int i = tid + k * NT;
-            if (res[k] >= 0) s_nx[i] = res[k];
-            else if (res[k] == -1) s_ptr[i] = nq[k];
-        }
         if (more) s_more[rd % 3] = 1;
         lds_barrier();
-        if (!s_more[rd % 3]) break;
-    }
-    for (int i = tid; i < nt; i += NT) {                // preorder successor: first child, else the node after
-        const int f = s_fc[i];
-        const int sc = f >= 0 ? f : s_nx[i];
-        s_sc[i] = sc;
-        s_rk[i] = sc < n ? 1 : 0;
-    }
-    lds_barrier();
-    for (int rd = 0;; ++rd) {                           // list ranking by pointer doubling
-        int nr[PL], ns[PL];
-        bool more = false;
-#pragma unroll
-        for (int k = 0; k < PL; ++k) {
-            const int i = tid + k * NT;
-            nr[k] = -1;
-            ns[k] = n;
-            if (i < nt) {
-                const int sc = s_sc[i];
-                if (sc < n) {
-                    nr[k] = s_rk[i] + s_rk[sc];
-                    ns[k] = s_sc[sc];
-                    more |= ns[k] < n;
-                }
-            }
-        }
-        if (tid == 0) s_more[3 + (rd + 1) % 3] = 0;
-        lds_barrier();
-#pragma unroll
-        for (int k = 0; k < PL; ++k) {
-            const int i = tid + k * NT;
-            if (nr[k] >= 0) {
-                s_rk[i] = nr[k];
-                s_sc[i] = ns[k];
-            }
-        }
-        if (more) s_more[3 + rd % 3] = 1;
-        lds_barrier();
-        if (!s_more[3 + rd % 3]) break;
-    }
-    for (int i = tid; i < nt; i += NT) {                // position n - 1 - rank
-        const int pi = min(max(n - 1 - s_rk[i], 0), n - 1);
-        const int nx = s_nx[i];
-        s_perm[pi] = (uint16_t)i;
-        s_last[pi] = (int16_t)((nx < n ? n - 1 - s_rk[nx] : n) - 1);
-    }
-    lds_barrier();
-    // ancestor rows from the preorder: j is a strict ancestor of r exactly when
-    // pos(j) < pos(r) <= last(pos(j)), and only j < r can be one.  Each node's
-    // (pos, last) is packed once into the free children-row scratch (nodes
-    // past the tree get pos 0xffff, never below a row's position); the tree's
-    // workgroups share the (row, word) pairs, one pair per thread.
-    const int nparts = Hv * 2, part = h * 2 + slice;
-    {
-        uint32_t* pk = s_cm;
-        for (int j = tid; j < NP; j += NT) {
-            uint32_t v = 0xffffu;
-            if (j < n) {
-                const int pj = nt ? min(max(n - 1 - s_rk[j], 0), n - 1) : j;
-                v = (uint32_t)pj | ((uint32_t)(uint16_t)s_last[pj] << 16);
-            }
-            pk[j] = v;
-        }
-        lds_barrier();
-        for (int x = part + nparts * tid; x < N * W; x += nparts * NT) {
-            const int r = x / W, w = x - r * W;
-            uint32_t bits = 0u;
-            if (r < n && 32 * w <= r) {
-                const uint32_t pr = pk[r] & 0xffffu;
-#pragma unroll
-                for (int e = 0; e < 32; e += 4) {
-                    const uint4 q4 = *reinterpret_cast<const uint4*>(pk + 32 * w + e);
-                    const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        bits |= ((q[k] & 0xffffu) < pr && pr <= (q[k] >> 16)) ? 1u << (e + k) : 0u;
-                }
-            }
-            gm[x] = bits;
-        }
-        if (writer && tid == 0) a.status[b] = 0;
-    }
-    auto node_at = [&](int pos) __attribute__((always_inline)) {   // position (clamped) -> node
-        return min((int)s_perm[min(pos, n - 1)], n - 1);
+        return s_more[rd % 3] != 0;
     };
-    for (int sb = tid; sb < NB; sb += NT) {
-        int m = -1;
-        for (int e = 0; e < 16; ++e) m = max(m, (int)s_last[16 * sb + e]);
-        s_mlast[sb] = m;
+    if (nt) {
+        const int i = tid;
+        int rd = 0;                                     // rounds so far, both loops
+        // (1) the node after each subtree: the subtree root's next sibling,
+        // else its parent's (a root-level node always has one); the link is
+        // an ancestor such that no node from i up to below it has a next
+        // sibling.  (2) With it, the path log-gates and depths: each node adds
+        // its link's sums and jumps to the link's link.
+        for (;; ++rd) {
+            bool more = false;
+            if (i < nt) {
+                const int2 a = s_na[i];
+                if (a.x < 0) {
+                    const int2 b = s_na[a.y];
+                    s_na[i] = b.x >= 0 ? make_int2(b.x, a.y) : make_int2(-1, b.y);
+                    more |= b.x < 0;
+                }
+            }
+            if (i < NP) {
+                const int2* src = s_gj + (rd & 1) * NP;
+                const int2 a = src[i];
+                const int j = (int)(int16_t)(a.x & 0xffff);
+                int2 r = a;
+                if (j >= 0) {
+                    const int2 b = src[j];
+                    const int jj = (int)(int16_t)(b.x & 0xffff);
+                    r = make_int2((jj & 0xffff) | (((a.x >> 16) + (b.x >> 16)) << 16),
+                                  __float_as_int(__int_as_float(a.y) + __int_as_float(b.y)));
+                    more |= jj >= 0;
+                }
+                s_gj[((rd + 1) & 1) * NP + i] = r;
+            }
+            if (!round_more(rd, more)) {
+                if (i < NP) {                           // the last round's copy
+                    const int2 a = s_gj[((rd + 1) & 1) * NP + i];
+                    s_lg[i] = __int_as_float(a.y);
+                    s_hop[i] = (int16_t)(a.x >> 16);
+                }
+                break;
+            }
+        }
+        // preorder successor: the first child, else the node after; then each
+        // node's distance to the list's end (list ranking)
+        if (i < nt) {
+            const int f = s_fc[i];
+            const int sc = f < NP ? f : s_na[i].x;
+            s_rs[i] = make_int2(sc < n ? 1 : 0, sc);
+        }
+        lds_barrier();
+        for (++rd;; ++rd) {
+            bool more = false;
+            if (i < nt) {
+                const int2 a = s_rs[i];
+                if (a.y < n) {
+                    const int2 b = s_rs[a.y];
+                    s_rs[i] = make_int2(a.x + b.x, b.y);
+                    more |= b.y < n;
+                }
+            }
+            if (!round_more(rd, more)) break;
+        }
+        if (i < nt) {                                   // position n - 1 - rank
+            const int pi = min(max(n - 1 - s_rs[i].x, 0), n - 1);
+            const int nx = s_na[i].x;
+            s_perm[pi] = (uint16_t)i;
+            s_last[pi] = (int16_t)((nx < n ? n - 1 - s_rs[nx].x : n) - 1);
+        }
     }
-
-    // path log-gates.  A chain's are prefix sums: a scan within each wave
-    // (lane shifts) and the preceding waves' totals.  Any other tree's by
-    // synchronous pointer doubling (each node adds its link's sum and jumps
-    // to the link's link); round r raises flag r % 3 while a node still has a
-    // link to follow and clears flag (r + 1) % 3 before its first barrier: two
-    // LDS-only barriers per round
     if (nt == 0) {
+        // a chain's path log-gates are prefix sums: a scan within each wave
+        // (lane shifts) and the preceding waves' totals
         static_assert(NP <= NT, "one chain node per thread");
         float x = tid < NP ? s_lg[tid] : 0.f;
 #pragma unroll
@@ -470,9 +422,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             const float y = __shfl_up(x, d);
             if (lane >= d) x += y;
         }
-        // (past the preorder's scratch, whose packed rows may still be read)
-        float* wsum = reinterpret_cast<float*>(reinterpret_cast<char*>(s_big) + SCRATCH);
-        static_assert(SCRATCH + 4 * kLargeWaves <= BIG, "wave sums fit the ring area");
+        float* wsum = reinterpret_cast<float*>(s_big);
         if (lane == 63) wsum[wave] = x;
         lds_barrier();
         for (int w = 0; w < wave; ++w) x += wsum[w];
@@ -480,98 +430,140 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             s_lg[tid] = x;
             s_hop[tid] = (int16_t)(tid < n ? tid + 1 : 0);
         }
-        lds_barrier();
     }
-    for (int rd = 0; nt; ++rd) {
-        int nn[PL], hj[PL];
-        float gj[PL];
-        bool more = false;
+    if constexpr (KLDS) {
 #pragma unroll
-        for (int k = 0; k < PL; ++k) {
-            const int i = tid + k * NT;
-            const int j = i < NP ? s_jump[i] : -1;
-            nn[k] = j >= 0 ? s_jump[j] : -1;
-            gj[k] = j >= 0 ? s_lg[j] : 0.f;
-            hj[k] = j >= 0 ? s_hop[j] : 0;
-            more |= nn[k] >= 0;
+        for (int kk = 0; kk < KI; ++kk) {
+            const int u = wave + kk * kLargeWaves;
+            if (u < NP / 4) *reinterpret_cast<u32x4*>(s_k + 4 * u * kD + 8 * lane) = k_r[kk];
         }
-        if (tid == 0) s_more[6 + (rd + 1) % 3] = 0;
-        lds_barrier();
-#pragma unroll
-        for (int k = 0; k < PL; ++k) {
-            const int i = tid + k * NT;
-            if (i < NP && s_jump[i] >= 0) {
-                s_lg[i] += gj[k];
-                s_hop[i] = (int16_t)(s_hop[i] + hj[k]);
-                s_jump[i] = nn[k];
-            }
+    }
+    lds_barrier();
+    // ancestor rows from the preorder: j is a strict ancestor of r exactly when
+    // pos(j) < pos(r) <= last(pos(j)), and only j < r can be one.  Each node's
+    // (pos, last) is packed once into the free scratch (nodes past the tree
+    // get pos 0xffff, never below a row's position); the tree's workgroups
+    // share the (row, word) pairs, one pair per thread.
+    const int nparts = Hv * 2, part = h * 2 + slice;
+    uint32_t* pk = reinterpret_cast<uint32_t*>(s_big) + 16;   // (past the wave sums)
+    for (int j = tid; j < NP; j += NT) {
+        uint32_t v = 0xffffu;
+        if (j < n) {
+            const int pj = nt ? min(max(n - 1 - s_rs[j].x, 0), n - 1) : j;
+            v = (uint32_t)pj | ((uint32_t)(uint16_t)s_last[pj] << 16);
         }
-        if (more) s_more[6 + rd % 3] = 1;
-        lds_barrier();
-        if (!s_more[6 + rd % 3]) break;
+        pk[j] = v;
+    }
+    for (int sb = tid; sb < NB; sb += NT) {
+        int m = -1;
+        for (int e = 0; e < 16; ++e) m = max(m, (int)s_last[16 * sb + e]);
+        s_mlast[sb] = m;
     }
     if (slice == 0)
         for (int i = tid; i < n; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
-    for (int r = part + nparts * tid; r < N; r += nparts * NT)   // depth: the rows' shares again
+    for (int r = part + nparts * tid; r < N; r += nparts * NT)   // depth: the rows' shares
         a.depth[(size_t)b * N + r] = r < n ? s_hop[r] - 1 : -1;
-
-    // G and beta by position (through the scratch: the ring area is free; a
-    // chain is in position order already)
-    if (nt) {
-        float* tl = reinterpret_cast<float*>(s_big);
-        float* tb = tl + NP;
+    auto node_at = [&](int pos) __attribute__((always_inline)) {   // position (clamped) -> node
+        return min((int)s_perm[min(pos, n - 1)], n - 1);
+    };
+    // G and beta by position, through the scratch past the packed rows
+    float* tl = reinterpret_cast<float*>(pk + NP);
+    float* tb = tl + NP;
+    static_assert((16 + 3 * NP) * 4 <= BIG, "position tables fit the ring area");
+    if (nt)
         for (int i = tid; i < NP; i += NT) {
             const int v = node_at(i);
             tl[i] = i < n ? s_lg[v] : 0.f;
             tb[i] = i < n ? s_beta[v] : 0.f;
         }
-        lds_barrier();
+    lds_barrier();
+    for (int x = part + nparts * tid; x < N * W; x += nparts * NT) {
+        const int r = x / W, w = x - r * W;
+        uint32_t bits = 0u;
+        if (r < n && 32 * w <= r) {
+            const uint32_t pr = pk[r] & 0xffffu;
+#pragma unroll
+            for (int e = 0; e < 32; e += 4) {
+                const uint4 q4 = *reinterpret_cast<const uint4*>(pk + 32 * w + e);
+                const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    bits |= ((q[k] & 0xffffu) < pr && pr <= (q[k] >> 16)) ? 1u << (e + k) : 0u;
+            }
+        }
+        gm[x] = bits;
+    }
+    if (writer && tid == 0) a.status[b] = 0;
+    if (nt)
         for (int i = tid; i < NP; i += NT) {
             s_lg[i] = tl[i];
             s_beta[i] = tb[i];
         }
-    }
-    // occupancy: tile (t, s), s < t, holds an ancestor pair exactly when a
-    // position of block s has its subtree reaching row t.  Row t's tiles in
-    // ascending s, so the tile of the block just before it (the one that
-    // waits for the previous row's U) comes last.
-    for (int t = tid; t < NB; t += NT) {
-        int m = 0;
-        for (int sb = 0; sb < t && t < nblk; ++sb)
-            if (s_mlast[sb] >= 16 * t) s_tcol[t][m++] = (uint8_t)sb;
-        s_tn[t] = m;
-    }
-    lds_barrier();
-    // the ring: row t takes the next 8 + s_tn[t] slots, rounded up to an even
-    // count so that 2-slot objects never wrap (counted over all rows, modulo
-    // RING); they may be written once every row whose slots they reuse has
-    // been consumed by all solve waves.  One wave, row r in lane r.
-    lds_barrier();
+    // One wave, row t in lane t, with no barrier between its steps:
+    //  * occupancy: tile (t, s), s < t, holds an ancestor pair exactly when a
+    //    position of block s has its subtree reaching row t; row t's occupied
+    //    blocks are listed in ascending order;
+    //  * the ring: row t takes the next 2 s_tn[t] + 1 slots (its -X tiles,
+    //    then its Y tiles, the diagonal block's last), counted over all rows
+    //    modulo RING; they may be written once every row whose slots they
+    //    reuse has been released by all solve waves;
+    //  * the producer items of row t: one for the diagonal block, then one per
+    //    C occupied blocks.
+    // Prefix sums over the rows go through LDS (one read of all rows' words).
     if (wave == 0) {
-        const int tn = lane < nblk ? s_tn[lane] : 0;
-        const int sl = lane < nblk ? 8 + tn + (tn & 1) : 0;
-        int inc = sl;
+        int ml[NB];
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_up(inc, d);
-            if (lane >= d) inc += y;
+        for (int sb = 0; sb < NB; sb += 4) {
+            const int4 x4 = *reinterpret_cast<const int4*>(&s_mlast[sb]);
+            ml[sb] = x4.x;
+            ml[sb + 1] = x4.y;
+            ml[sb + 2] = x4.z;
+            ml[sb + 3] = x4.w;
         }
-        const int gsl = inc - sl;                       // first slot of row lane; lane nblk: the total
-        const int target = inc - RING;                  // rows starting below it must be consumed
-        int cnt = 0;
-        for (int r = 0; r < nblk; ++r) {
-            const int gr = __builtin_amdgcn_readlane(gsl, r);
-            cnt += (r < lane && gr < target) ? 1 : 0;
+        uint32_t occ = 0u;
+#pragma unroll
+        for (int sb = 0; sb < NB; ++sb) occ |= (sb < lane && lane < nblk && ml[sb] >= 16 * lane) ? 1u << sb : 0u;
+        const int tn = __popc(occ);
+        if (lane < NB) {
+            s_tn[lane] = tn;
+            for (int k = 0; occ; ++k, occ &= occ - 1u) s_tcol[lane][k] = (uint8_t)__builtin_ctz(occ);
         }
+        const int sl = lane < nblk ? 2 * tn + 1 : 0;
+        const int ni = lane < nblk ? 1 + (tn + C - 1) / C : 0;
+        // (slots and items of a row packed in one word: both totals stay
+        // below 2^16)
+        int* tmp = reinterpret_cast<int*>(s_big) + 16 + 3 * NP;   // (past the position tables)
+        static_assert((16 + 3 * NP + 64) * 4 <= BIG, "row sums fit the ring area");
+        tmp[lane] = sl | (ni << 16);
+        int ex = 0;                                     // the rows before this lane's
+#pragma unroll
+        for (int r = 0; r < NB; r += 4) {
+            const int4 x4 = *reinterpret_cast<const int4*>(&tmp[r]);
+            ex += (r < lane ? x4.x : 0) + (r + 1 < lane ? x4.y : 0) + (r + 2 < lane ? x4.z : 0) +
+                  (r + 3 < lane ? x4.w : 0);
+        }
+        const int gsl = ex & 0xffff;                    // first slot of row lane; lane NB: the total
+        const int ib = ex >> 16;                        // first item of row lane; lane NB: the total
+        const int target = gsl + sl - RING;             // rows starting below it must be released
         if (lane <= NB) s_gslot[lane] = gsl;
+        int cnt = 0;
+#pragma unroll
+        for (int r = 0; r < NB; r += 4) {
+            const int4 x4 = *reinterpret_cast<const int4*>(&s_gslot[r]);
+            cnt += (r < lane && x4.x < target ? 1 : 0) + (r + 1 < lane && x4.y < target ? 1 : 0) +
+                   (r + 2 < lane && x4.z < target ? 1 : 0) + (r + 3 < lane && x4.w < target ? 1 : 0);
+        }
         if (lane < NB) s_rstar[lane] = cnt;
+        for (int j = 0; j < ni; ++j) s_items[ib + j] = (uint16_t)(lane | (j << 8));
+        if (lane == NB) s_nitems = ib;
     }
     lds_barrier();
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
     // k / q fragment of node block blk, column chunk cs: lane (r, q) holds
-    // row 16 blk + r (clamped), columns 32 cs + 8 q .. +7.  From global
-    // memory (a uniform base and a 32-bit lane offset) or, for k, from LDS.
+    // row 16 blk + r (clamped), columns 32 cs + 8 q .. +7, from global
+    // memory (a uniform base and a 32-bit lane offset); from LDS the same
+    // lanes read the row's chunk 4 cs + q.
     const uint32_t lane_col = 16u * lq;
     auto gfrag = [&](const uint16_t* base, int blk, int cs) __attribute__((always_inline)) {
         const uint32_t row = (uint32_t)node_at(16 * blk + ln);
@@ -579,155 +571,290 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                               reinterpret_cast<const char*>(base) + off));
     };
-    auto kfrag = [&](int blk, int cs) __attribute__((always_inline)) {
-        if constexpr (KLDS) {
-            const int row = node_at(16 * blk + ln);
-            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(row, 4 * cs + lq)));
-        } else {
-            return gfrag(Kb, blk, cs);
-        }
-    };
-    // S0 rows col0 + r of the slice: lane (r, q) holds columns 32 cs + 8 q ..
-    // +7; the same registers are the B operand S0^T (for K S0^T) and the A
-    // operand S0 (for S0 Q^T)
-    auto s0frag = [&](int col0, int cs) __attribute__((always_inline)) {
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_s0 + row_chunk(col0 + ln, 4 * cs + lq)));
-    };
-    // ring slot x, as 8-byte (tiles) or 16-byte (right-hand sides) lane words
-    uint2* ring8 = s_big;
-    u32x4* ring16 = reinterpret_cast<u32x4*>(s_big);
+    uint2* ring = s_big;                                // slot x: ring[64 x + lane]
     auto slot_at = [&](int x) __attribute__((always_inline)) { return x < RING ? x : x - RING; };
 
-    // Nothing of the setup is in flight past this point (its loads are
-    // consumed; its cache stores have long completed), so the loops below
-    // start from an empty count and the compiler's waits in them count only
-    // their own requests.
-    wait_vmem_all();
     if (solver) {
         // ================= solve waves =================
+        // (the solve is the chain every row waits for: its waves issue ahead
+        // of the producers sharing their SIMDs)
+        __builtin_amdgcn_s_setprio(2);
         const int g = wave;
         const int c0 = cbase + 16 * g;                  // this wave's first value column
+        // this wave's 16 S0 rows as bf16: lane (r, q) holds row c0 + r,
+        // columns 32 cs + 8 q .. +7; the A operand S0 (for S0 Q^T) and the B
+        // operand S0^T (for K S0^T)
+        bf16x8 s0g[4];
+        s16x4 ident;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
         const __amdgpu_buffer_rsrc_t u_rsrc =
             __builtin_amdgcn_make_buffer_rsrc(Ug, (short)0, N * kD * 4, kBufferFlags);
-        s16x4 uprev = {0, 0, 0, 0};
-        for (int t = 0; t < nblk; ++t) {
-            const int nts = s_tn[t];
-            const int base = s_gslot[t] % RING;
-            wait_flag_ge(&s_xready[t], 1);
-            // D_t R_t of this group: 16 bytes per lane in slot base + 2g
-            f32x4 acc = __builtin_bit_cast(f32x4, ring16[slot_at(base + 2 * g) * 32 + lane]);
-            // U_t = D_t R_t - sum_s X~_ts U_s (the tiles hold -X~); four tiles'
-            // operands are read before their products
-            int sl = slot_at(base + 8);
-            f32x4 acc2 = z;
-            int m = 0;
-            for (; m + 4 <= nts; m += 4) {
-                s16x4 xa[4], ub[4];
+        const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            O + vo_base, (short)0, ((n - 1) * Hv + 1) * kD * 2, kBufferFlags);
+        const char* Vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + vo_base + c0 + 4 * lq);
+        // a row's global operands, requested one row ahead: k (when not in
+        // LDS), q, and v of this wave's columns (lane (r, q): row r, columns
+        // 4 q .. +3)
+        struct RowOps {
+            bf16x8 kt[KLDS ? 1 : 4];
+            bf16x8 qt[4];
+            uint2 vt;
+        };
+        auto fetch = [&](int t, RowOps& r) __attribute__((always_inline)) {
+            t = min(t, nblk - 1);
+            if constexpr (!KLDS) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = __builtin_amdgcn_readfirstlane((int)s_tcol[t][m + e]);
-                    xa[e] = __builtin_bit_cast(s16x4, ring8[slot_at(sl + e) * 64 + lane]);
-                    ub[e] = s == t - 1 ? uprev : __builtin_bit_cast(s16x4, s_u[s][g][lane]);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (e & 1) acc2 = mfma16(xa[e], ub[e], acc2);
-                    else acc = mfma16(xa[e], ub[e], acc);
-                }
-                sl = slot_at(sl + 4);
+                for (int cs = 0; cs < 4; ++cs) r.kt[cs] = gfrag(Kb, t, cs);
             }
-            for (; m < nts; ++m) {
-                const int s = __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]);
-                const s16x4 xa = __builtin_bit_cast(s16x4, ring8[sl * 64 + lane]);
-                const s16x4 ub = s == t - 1 ? uprev : __builtin_bit_cast(s16x4, s_u[s][g][lane]);
-                acc = mfma16(xa, ub, acc);
-                sl = slot_at(sl + 1);
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) r.qt[cs] = gfrag(Qb, t, cs);
+            const uint32_t vr = (uint32_t)node_at(16 * t + ln) * (uint32_t)(vo_row * 2);
+            r.vt = *reinterpret_cast<const uint2*>(Vb + vr);
+        };
+        // One row: every LDS operand that does not wait for the producers is
+        // requested first (the row's blocks, node indices, gates, this wave's
+        // own U rows of the first SB occupied blocks), then the right-hand
+        // side and e^G Q S0^T are formed, then the wait, then the row's tiles.
+        // The first SB occupied blocks are read and applied branch-free (the
+        // unused ones masked); rows with more take a loop.
+        constexpr int SB = 8;
+        constexpr int TW = NB / 4;                      // words of a row of s_tcol
+        const s16x4 zero4 = {0, 0, 0, 0};
+        auto row = [&](int t, RowOps& r) __attribute__((always_inline)) {
+            const int nts = __builtin_amdgcn_readfirstlane(s_tn[t]);
+            const int base = __builtin_amdgcn_readfirstlane(s_gslot[t]) % RING;
+            uint32_t tw[TW];
+#pragma unroll
+            for (int w = 0; w < TW; ++w)
+                tw[w] = __builtin_amdgcn_readfirstlane(reinterpret_cast<const uint32_t*>(&s_tcol[t][0])[w]);
+            const int pr = 16 * t + ln;                 // this lane's node of the products' columns
+            const int no = node_at(pr);
+            int nu[4];
+            float bt[4], lgr[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int i = 16 * t + 4 * lq + m;
+                nu[m] = node_at(i);
+                bt[m] = s_beta[i];
+                lgr[m] = s_lg[i];
+            }
+            const float lgc = s_lg[pr];
+            s16x4 ub[SB], xa[SB], ya[SB];
+#pragma unroll
+            for (int e = 0; e < SB; ++e) {
+                const int sb = e < nts ? (int)((tw[e >> 2] >> (8 * (e & 3))) & 0xffu) : t;
+                ub[e] = __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
+            }
+            // R_t = diag(beta)(V_t - diag(e^G) K_t S0^T): [node 4q + m][column]
+            // (V moves into the accumulator layout by an exact product with I)
+            f32x4 ks = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) {
+                bf16x8 kk;
+                if constexpr (KLDS)
+                    kk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(no, 4 * cs + lq)));
+                else kk = r.kt[cs];
+                ks = mfma32(kk, s0g[cs], ks);
+            }
+            const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, r.vt), ident, z);
+            f32x4 acc;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = bt[m] * (vd[m] - __expf(lgr[m]) * ks[m]);
+            // e^G Q_t S0^T: [column 4q + m][node]
+            f32x4 oc = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) oc = mfma32(s0g[cs], r.qt[cs], oc);
+            oc *= __expf(lgc);
+            wait_flag_ge(&s_done[t], nts + 1);
+            // U_t = D_t (R_t - sum_s X_ts U_s) (the slots hold -X) and
+            // O_t += sum_{s < t} Y_ts U_s as U^T Y^T; a row's Y tiles follow
+            // its -X tiles, the diagonal block's last
+#pragma unroll
+            for (int e = 0; e < SB; ++e) {
+                xa[e] = __builtin_bit_cast(s16x4, ring[slot_at(base + e) * 64 + lane]);
+                ya[e] = __builtin_bit_cast(s16x4, ring[slot_at(base + nts + e) * 64 + lane]);
+            }
+            const s16x4 dt = __builtin_bit_cast(s16x4, s_d[t][lane]);
+            const s16x4 ytt = __builtin_bit_cast(s16x4, ring[slot_at(base + 2 * nts) * 64 + lane]);
+            f32x4 acc2 = z, oc2 = z;
+#pragma unroll
+            for (int e = 0; e < SB; ++e) {
+                // (an unused entry's operands are all zeroed: its LDS may hold
+                // any bits, NaN included)
+                const bool v = e < nts;
+                const s16x4 x = v ? xa[e] : zero4, y = v ? ya[e] : zero4, u = v ? ub[e] : zero4;
+                if (e & 1) {
+                    acc2 = mfma16(x, u, acc2);
+                    oc2 = mfma16(u, y, oc2);
+                } else {
+                    acc = mfma16(x, u, acc);
+                    oc = mfma16(u, y, oc);
+                }
+            }
+            for (int m0 = SB; m0 < nts; m0 += SB) {
+#pragma unroll
+                for (int e = 0; e < SB; ++e) {
+                    const int m = m0 + e;
+                    const int sb = m < nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]) : t;
+                    ub[e] = __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
+                    xa[e] = __builtin_bit_cast(s16x4, ring[slot_at(base + m) * 64 + lane]);
+                    ya[e] = __builtin_bit_cast(s16x4, ring[slot_at(base + nts + m) * 64 + lane]);
+                }
+#pragma unroll
+                for (int e = 0; e < SB; ++e) {
+                    const bool v = m0 + e < nts;
+                    const s16x4 x = v ? xa[e] : zero4, y = v ? ya[e] : zero4, u = v ? ub[e] : zero4;
+                    if (e & 1) {
+                        acc2 = mfma16(x, u, acc2);
+                        oc2 = mfma16(u, y, oc2);
+                    } else {
+                        acc = mfma16(x, u, acc);
+                        oc = mfma16(u, y, oc);
+                    }
+                }
             }
             acc += acc2;
-            uprev = to_bf16x4(acc);
-            s_u[t][g][lane] = __builtin_bit_cast(uint2, uprev);
-            publish_set(&s_uready[g], t + 1, lane);    // also frees row t's ring slots
+            s16x4 hi, lo;                               // (bf16 hi + lo parts: D_t meets R to ~16 bits)
+            split4(acc, hi, lo);
+            const f32x4 uf = mfma16(dt, lo, mfma16(dt, hi, z));
+            const s16x4 ut = to_bf16x4(uf);
+            s_u[t][g][lane] = __builtin_bit_cast(uint2, ut);
             // the cache row: lane (n, q) holds rows 4q .. 4q+3 of column n;
             // positions past the tree store outside the buffer and are dropped
 #pragma unroll
             for (int mm = 0; mm < 4; ++mm) {
                 const int i = 16 * t + 4 * lq + mm;
-                const int off = i < n ? (node_at(i) * kD + c0 + ln) * 4 : 0x7fffffff;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mm]), u_rsrc, off, 0, 0);
+                const int off = i < n ? (nu[mm] * kD + c0 + ln) * 4 : 0x7fffffff;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(uf[mm]), u_rsrc, off, 0, 0);
             }
+            oc += oc2;
+            oc = mfma16(ut, ytt, oc);                   // the diagonal block
+            publish_set(&s_oready[g], t + 1, lane);     // the row's slots are read: release them
+            const int orow = pr < n ? (no * Hv * kD + c0 + 4 * lq) * 2 : 0x7fffffff;
+            u32x2 w;
+            w[0] = (uint32_t)bf16_rne(oc[0]) | ((uint32_t)bf16_rne(oc[1]) << 16);
+            w[1] = (uint32_t)bf16_rne(oc[2]) | ((uint32_t)bf16_rne(oc[3]) << 16);
+            __builtin_amdgcn_raw_buffer_store_b64(w, o_rsrc, orow, 0, 0);
+        };
+        RowOps ra, rb;
+        fetch(0, ra);
+        // Nothing of the setup is in flight past this point but the first
+        // row's operands, so the loop's waits count only its own requests.
+        wait_vmem_le<KLDS ? 5 : 9>();
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) s0g[cs] = to_bf16x8(s0_r[2 * cs], s0_r[2 * cs + 1]);
+        for (int t = 0; t < nblk; t += 2) {
+            fetch(t + 1, rb);
+            row(t, ra);
+            if (t + 1 >= nblk) break;
+            fetch(t + 2, ra);
+            row(t + 1, rb);
         }
         return;
     }
 
-    // ================= row owners =================
-    const int p = wave - kSolveWaves;                   // 0 .. kOwners - 1
-    // o rows of this tree and head: node v's row at v Hv kD elements
-    const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        O + vo_base, (short)0, ((n - 1) * Hv + 1) * kD * 2, kBufferFlags);
-    const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + vo_base + cbase;   // (+ 4 lq per lane below)
-    s16x4 ident;
+    // ================= producers =================
+    const int p = wave - kSolveWaves;                   // 0 .. kProducers - 1
+    const int nitems = s_nitems;
+    // An item's operands, requested one item ahead: its row, that row's
+    // slots and occupied blocks, the node rows of its k fragments, q of its
+    // row and, when k is not in LDS, k of its row and of its column blocks.
+    struct ItemOps {
+        int t, j, nts, base;
+        int sb[C];                                      // the item's column blocks (t: none)
+        int rt, rx[C];                                  // k rows (nodes) of lane ln in the row's / blocks' fragments
+        bf16x8 kt[KLDS ? 1 : 4];
+        bf16x8 kx[KLDS ? 1 : C][KLDS ? 1 : 4];
+        bf16x8 qt[4];
+    };
+    auto fetch = [&](int it, ItemOps& o) __attribute__((always_inline)) {
+        const int code = __builtin_amdgcn_readfirstlane((int)s_items[min(it, nitems - 1)]);
+        const int t = code & 0xff, j = code >> 8;
+        o.t = t;
+        o.j = j;
+        o.nts = __builtin_amdgcn_readfirstlane(s_tn[t]);
+        o.base = __builtin_amdgcn_readfirstlane(s_gslot[t]) % RING;
+        o.rt = node_at(16 * t + ln);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
-    for (int t = p; t < nblk; t += kOwners) {
-        const int nts = s_tn[t];
-        // operands, requested before the wait for ring space: k of the row,
-        // its v rows for the four groups (lane (r, q): columns 16 gg + 4q ..
-        // +3 of row r) and, when k comes from global memory, k of its first
-        // kChunk occupied blocks (from LDS they are read tile by tile)
-        bf16x8 kt[4], kx[kChunk][4];
-        uint2 vt[4];
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) kt[cs] = kfrag(t, cs);
-        {
-            const uint32_t vr = (uint32_t)node_at(16 * t + ln) * (uint32_t)(vo_row * 2);   // (bytes, a uniform base)
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg)
-                vt[gg] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(Vb) + vr + 8u * lq + 32u * gg);
+        for (int e = 0; e < C; ++e) {
+            const int m = (j - 1) * C + e;
+            o.sb[e] = j > 0 && m < o.nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]) : t;
+            o.rx[e] = node_at(16 * o.sb[e] + ln);
         }
-        // k of the occupied blocks m0 .. m0 + kChunk - 1 (past the row's: its own)
-        auto load_chunk = [&](int m0) __attribute__((always_inline)) {
+        const uint32_t qoff = (uint32_t)o.rt * (uint32_t)(kq_row * 2) + lane_col;
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) {
-                const int s = m0 + e < nts ? (int)s_tcol[t][m0 + e] : t;
+        for (int cs = 0; cs < 4; ++cs)
+            o.qt[cs] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                      reinterpret_cast<const char*>(Qb) + qoff + 64u * cs));
+        if constexpr (!KLDS) {
 #pragma unroll
-                for (int cs = 0; cs < 4; ++cs) kx[e][cs] = kfrag(s, cs);
+            for (int cs = 0; cs < 4; ++cs)
+                o.kt[cs] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                          reinterpret_cast<const char*>(Kb) + qoff + 64u * cs));
+#pragma unroll
+            for (int e = 0; e < C; ++e) {
+                const uint32_t xoff = (uint32_t)o.rx[e] * (uint32_t)(kq_row * 2) + lane_col;
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs)
+                    o.kx[e][cs] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                                 reinterpret_cast<const char*>(Kb) + xoff + 64u * cs));
             }
-        };
-        if constexpr (!KLDS) load_chunk(0);             // (from LDS: after the inverse, fewer live registers)
-        // this row's nodes (rows 4q .. 4q+3 of the accumulator layout)
-        float bei[4], lgi4[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            bei[m] = s_beta[16 * t + 4 * lq + m];
-            lgi4[m] = s_lg[16 * t + 4 * lq + m];
         }
+    };
+    auto wait_ring = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-        for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_uready[gg], s_rstar[t]);
-        const int base = s_gslot[t] % RING;
-        // ---- D_t = (I + X_tt)^-1, with the row's right-hand-side slots as
-        // scratch (X_tt in fp32 at slot base, D as an A operand at base + 2) ----
-        float* xd = reinterpret_cast<float*>(&ring8[base * 64]);
-        uint16_t* dd = reinterpret_cast<uint16_t*>(&ring8[slot_at(base + 2) * 64]);
-        {
-            f32x4 gr = z;
+        for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_oready[gg], s_rstar[t]);
+    };
+    auto work = [&](ItemOps& o) __attribute__((always_inline)) {
+        const int t = o.t, j = o.j, nts = o.nts, base = o.base;
+        bf16x8 kt[4];
 #pragma unroll
-            for (int cs = 0; cs < 4; ++cs) gr = mfma32(kt[cs], kt[cs], gr);   // lane (j, q): [i = 4q + m][j]
-            const int pj = 16 * t + ln;
-            const int lj = s_last[pj];
-            const float lgj = s_lg[pj];
-            float4 xv;
-            float* xp = reinterpret_cast<float*>(&xv);
+        for (int cs = 0; cs < 4; ++cs) {
+            if constexpr (KLDS)
+                kt[cs] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(o.rt, 4 * cs + lq)));
+            else kt[cs] = o.kt[cs];
+        }
+        const int pi = 16 * t + ln;                     // the Gram columns' node i
+        const float lgi = s_lg[pi];
+        int done;
+        if (j == 0) {
+            // ---- D_t = (I + X_tt)^-1 and Y_tt ----
+            f32x4 gk = z, gq = z;
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) {
+                gk = mfma32(kt[cs], kt[cs], gk);        // lane (j, q): k_{4q+m} . k_j
+                gq = mfma32(kt[cs], o.qt[cs], gq);      // lane (i, q): k_{4q+m} . q_i
+            }
+            // X_tt[i][j] at lane (j, q), element m: i = 4q + m
+            float xv[4];
+            {
+                const int pj = 16 * t + ln;
+                const int lj = s_last[pj];
+                const float lgj = s_lg[pj];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int pi2 = 16 * t + 4 * lq + m;
+                    const bool anc = (pj < pi2) & (pi2 <= lj);
+                    const float x = s_beta[pi2] * __expf(fminf(s_lg[pi2] - lgj, 0.f)) * gk[m];
+                    xv[m] = anc ? x : 0.f;
+                }
+            }
+            // Y_tt[i][j] at lane (i, q), element m: j = 4q + m (j an ancestor of i or i)
+            s16x4 yb;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int pi = 16 * t + 4 * lq + m;
-                const bool anc = (pj < pi) & (pi <= lj);
-                const float x = bei[m] * __expf(fminf(lgi4[m] - lgj, 0.f)) * gr[m];
-                xp[m] = anc ? x : 0.f;
+                const int pj = 16 * t + 4 * lq + m;
+                const bool anc = (pj <= pi) & (pi <= (int)s_last[pj]);
+                const float y = __expf(fminf(lgi - s_lg[pj], 0.f)) * gq[m];
+                yb[m] = (short)bf16_rne(anc ? y : 0.f);
             }
-            *reinterpret_cast<float4*>(&xd[ln * 16 + 4 * lq]) = xv;      // [col j][row i]
             // fp32 forward substitution, four lanes per column: lane 4c + qd
-            // holds rows 4qd .. 4qd+3 of column c; step m broadcasts y_m from
-            // its owner within the lane quad and updates the rows below it
+            // holds rows 4qd .. 4qd+3 of column c; step m reads column m of
+            // X_tt (stored [col][row] by the lanes that hold it) and takes y_m
+            // from its owner within the lane quad
+            float* xd = &s_xd[p][0];
+            *reinterpret_cast<float4*>(&xd[ln * 16 + 4 * lq]) = make_float4(xv[0], xv[1], xv[2], xv[3]);
             const int c = lane >> 2, qd = lane & 3;
             float accd[4];
 #pragma unroll
@@ -738,157 +865,78 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 const float ym = quad_bcast(accd[m & 3], m >> 2);
                 const float xr[4] = {xc.x, xc.y, xc.z, xc.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {                 // rows below m only
+                for (int e = 0; e < 4; ++e) {               // rows below m only
                     const float upd = fmaf(-xr[e], ym, accd[e]);
                     accd[e] = 4 * qd + e > m ? upd : accd[e];
                 }
             }
+            uint16_t* dd = reinterpret_cast<uint16_t*>(&s_d[t][0]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
-        }
-        const s16x4 dt = __builtin_bit_cast(s16x4, reinterpret_cast<const uint2*>(dd)[lane]);   // A: D; B: D^T
-        // ---- the row's -X~ tiles, kChunk at a time (their reads and products
-        // independent of each other) ----
-        for (int m0 = 0; m0 < nts; m0 += kChunk) {
-            if (m0 > 0 || KLDS) load_chunk(m0);
-            int sc[kChunk];
-            f32x4 gr[kChunk];
-            int lj[kChunk];
-            float lgj[kChunk];
+            wait_ring(t);
+            ring[slot_at(base + 2 * nts) * 64 + lane] = __builtin_bit_cast(uint2, yb);
+            done = 1;
+        } else {
+            // ---- -X_ts and Y_ts for C occupied blocks s ----
+            int mm_[C], sb[C];
+            bf16x8 kx[C][4];
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) {
-                sc[e] = m0 + e < nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m0 + e]) : t;
-                lj[e] = s_last[16 * sc[e] + ln];
-                lgj[e] = s_lg[16 * sc[e] + ln];
-                gr[e] = z;
+            for (int e = 0; e < C; ++e) {
+                mm_[e] = (j - 1) * C + e;
+                sb[e] = o.sb[e];
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) {
+                    if constexpr (KLDS)
+                        kx[e][cs] = __builtin_bit_cast(bf16x8,
+                                                       *reinterpret_cast<const u32x4*>(s_k + row_chunk(o.rx[e], 4 * cs + lq)));
+                    else kx[e][cs] = o.kx[e][cs];
+                }
             }
+            f32x4 gx[C], gy[C];
+#pragma unroll
+            for (int e = 0; e < C; ++e) gx[e] = gy[e] = z;
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs)
 #pragma unroll
-                for (int e = 0; e < kChunk; ++e) gr[e] = mfma32(kt[cs], kx[e][cs], gr[e]);   // lane (j, q): [i = 4q + m][j]
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e) {
-                s16x4 xa;                               // X^T as an A operand
-#pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    const int pi = 16 * t + 4 * lq + mm;
-                    const bool anc = (sc[e] < t) & (pi <= lj[e]);   // (pj < pi: s < t)
-                    const float x = bei[mm] * __expf(fminf(lgi4[mm] - lgj[e], 0.f)) * gr[e][mm];
-                    xa[mm] = (short)bf16_rne(anc ? x : 0.f);
+                for (int e = 0; e < C; ++e) {
+                    gx[e] = mfma32(kx[e][cs], kt[cs], gx[e]);     // lane (i, q): k_{j = 4q+m} . k_i
+                    gy[e] = mfma32(kx[e][cs], o.qt[cs], gy[e]);   // lane (i, q): k_j . q_i
                 }
-                const f32x4 xt = mfma16(xa, dt, z);     // X^T D^T: lane (i, q) holds X~[i][4q + m]
-                s16x4 nx;
+            const float bi = s_beta[pi];
+            s16x4 xn[C], yv[C];
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm) nx[mm] = (short)bf16_rne(-xt[mm]);
-                if (m0 + e < nts) ring8[slot_at(base + 8 + m0 + e) * 64 + lane] = __builtin_bit_cast(uint2, nx);
-            }
-        }
-        bf16x8 qt[4];                                   // q of the row, for the outputs
+            for (int e = 0; e < C; ++e)
 #pragma unroll
-        for (int cs = 0; cs < 4; ++cs) qt[cs] = gfrag(Qb, t, cs);
-        // ---- D_t R_t of the four groups, R_t = diag(beta)(V_t - diag(e^G) K_t S0^T);
-        // V moves into the accumulator layout by an exact product with I ----
-        f32x4 rt[4];
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            f32x4 ks = z;
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs) ks = mfma32(kt[cs], s0frag(16 * gg, cs), ks);   // [node][col]
-            const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, vt[gg]), ident, z);
-            f32x4 R;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) R[m] = bei[m] * (vd[m] - __expf(lgi4[m]) * ks[m]);
-            s16x4 rh, rl;
-            split4(R, rh, rl);
-            rt[gg] = mfma16(dt, rl, mfma16(dt, rh, z));
-        }
-        // (the scratch in slots base .. base + 2 is read: D is in registers)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) ring16[slot_at(base + 2 * gg) * 32 + lane] = __builtin_bit_cast(u32x4, rt[gg]);
-        publish_set(&s_xready[t], 1, lane);
-        // (q is used only below this point: its products may not be moved
-        // ahead of the publication, which would then wait for its loads)
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs) asm volatile("" : "+v"(qt[cs]));
-        // ---- outputs O_t = e^G Q_t S0^T + sum_{s <= t} Y_ts U_s ----
-        f32x4 oc[4];
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            oc[gg] = z;
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs) oc[gg] = mfma32(s0frag(16 * gg, cs), qt[cs], oc[gg]);   // [col][node]
-        }
-        const int pi = 16 * t + ln;                     // this lane's node (column of the products)
-        const float lgi = s_lg[pi];
-        const float egi = __expf(lgi);
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) oc[gg] *= egi;
-        // Y tiles four at a time: their Gram products first, then the wait for
-        // the last of their rows of U (rows are published in order), then the
-        // products with U of every column group
-        auto y_group = [&](const int (&sc)[kChunk], int cnt, const bf16x8 (&ks)[kChunk][4]) __attribute__((always_inline)) {
-            f32x4 gr[kChunk];
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e) gr[e] = z;
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs)
-#pragma unroll
-                for (int e = 0; e < kChunk; ++e) gr[e] = mfma32(ks[e][cs], qt[cs], gr[e]);   // lane (i, q): [j = 4q + m][i]
-            s16x4 yb[kChunk];                           // Y^T as B operands
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e)
-#pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    const int pj = 16 * sc[e] + 4 * lq + mm;
-                    const int lpj = s_last[pj];
-                    const bool anc = (e < cnt) & (pj <= pi) & (pi <= lpj);
-                    const float y = __expf(fminf(lgi - s_lg[pj], 0.f)) * gr[e][mm];
-                    yb[e][mm] = (short)bf16_rne(anc ? y : 0.f);
+                for (int m = 0; m < 4; ++m) {
+                    const int pj = 16 * sb[e] + 4 * lq + m;
+                    const bool anc = pi <= (int)s_last[pj];      // (pj < pi: s < t)
+                    const float dec = __expf(fminf(lgi - s_lg[pj], 0.f));
+                    xn[e][m] = (short)bf16_rne(anc ? -bi * dec * gx[e][m] : 0.f);
+                    yv[e][m] = (short)bf16_rne(anc ? dec * gy[e][m] : 0.f);
                 }
-            int smax = sc[0];
+            wait_ring(t);
+            done = 0;
 #pragma unroll
-            for (int e = 1; e < kChunk; ++e) smax = e < cnt ? max(smax, sc[e]) : smax;
-#pragma unroll
-            for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_uready[gg], smax + 1);
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e)
-                if (e < cnt)
-#pragma unroll
-                    for (int gg = 0; gg < 4; ++gg)
-                        oc[gg] = mfma16(__builtin_bit_cast(s16x4, s_u[sc[e]][gg][lane]), yb[e], oc[gg]);
-        };
-        // the occupied blocks s < t, then the diagonal block (its wait is for
-        // the solve's row t)
-        const int nall = nts + 1;
-        for (int m0 = 0; m0 < nall; m0 += kChunk) {
-            // (a single chunk of tiles is still in registers, and past the row's
-            // blocks it holds the row's own; a diagonal block left alone in a
-            // chunk of its own takes the row's k)
-            if (nts > kChunk || (KLDS && nts == 0)) {
-                load_chunk(m0);
-            } else if (m0 > 0) {
-#pragma unroll
-                for (int e = 0; e < kChunk; ++e)
-#pragma unroll
-                    for (int cs = 0; cs < 4; ++cs) kx[e][cs] = kt[cs];
-            }
-            int sc[kChunk];
-#pragma unroll
-            for (int e = 0; e < kChunk; ++e) {
-                const int m = m0 + e;
-                sc[e] = m < nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]) : t;
-            }
-            y_group(sc, min(kChunk, nall - m0), kx);
+            for (int e = 0; e < C; ++e)
+                if (mm_[e] < nts) {
+                    ring[slot_at(base + mm_[e]) * 64 + lane] = __builtin_bit_cast(uint2, xn[e]);
+                    ring[slot_at(base + nts + mm_[e]) * 64 + lane] = __builtin_bit_cast(uint2, yv[e]);
+                    ++done;
+                }
         }
-        // (positions past the tree store outside the buffer and are dropped)
-        const int orow = pi < n ? (node_at(pi) * Hv * kD + cbase + 4 * lq) * 2 : 0x7fffffff;
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            u32x2 w;
-            w[0] = (uint32_t)bf16_rne(oc[gg][0]) | ((uint32_t)bf16_rne(oc[gg][1]) << 16);
-            w[1] = (uint32_t)bf16_rne(oc[gg][2]) | ((uint32_t)bf16_rne(oc[gg][3]) << 16);
-            __builtin_amdgcn_raw_buffer_store_b64(w, o_rsrc, orow + 32 * gg, 0, 0);
-        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane == 0) __hip_atomic_fetch_add(&s_done[t], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    ItemOps ia, ib;
+    fetch(p, ia);
+    // (as for the solve waves: only the first item's operands are in flight)
+    wait_vmem_le<KLDS ? 4 : 4 + 4 + 4 * C>();
+    for (int it = p; it < nitems; it += 2 * kProducers) {
+        fetch(it + kProducers, ib);
+        work(ia);
+        if (it + kProducers >= nitems) break;
+        fetch(it + 2 * kProducers, ia);
+        work(ib);
     }
 }
 
