@@ -98,10 +98,19 @@ struct LargeShape {
     static constexpr int C = KLDS ? 2 : 1;              // occupied column blocks per producer item
     static constexpr int WC = NP / 32;                  // words of a children row
     static constexpr int SCRATCH = ((NP + 1) * WC + (NP + 2) + 8 * NP) * 4;   // the preorder's
+    // A row's slots: when k is not in LDS, first its right-hand sides R_t and
+    // e^G Q_t S0^T (fp32, two slots per column group each) and D_t (HDR
+    // slots in all); then its -X tiles and its Y tiles (the diagonal block's
+    // last).  Rows with a header take an even number of slots, so two-slot
+    // objects never wrap.
+    static constexpr int HDR = KLDS ? 0 : 17;
+    static constexpr int NFIX = KLDS ? 1 : 2;           // items of a row before its occupied blocks'
+
     static constexpr int RING = NB <= 16 ? 84 : 112;    // 512-byte tile slots
     static constexpr int BIG = RING * 512 > SCRATCH ? RING * 512 : SCRATCH;
-    // items: per row one for the diagonal block and one per C occupied blocks
-    static constexpr int ITEMS = NB + (C == 1 ? NB * (NB - 1) / 2 : (NB / 2) * (NB / 2));
+    // items: per row one for the diagonal block, without k in LDS one for the
+    // right-hand sides, and one per C occupied blocks
+    static constexpr int ITEMS = NFIX * NB + (C == 1 ? NB * (NB - 1) / 2 : (NB / 2) * (NB / 2));
 };
 
 template <int NB>
@@ -116,14 +125,17 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     constexpr int BIG = L::BIG;
     constexpr int RING = L::RING;
     constexpr int PL = (NP + NT - 1) / NT;              // tree entries per thread
-    static_assert(2 * (NB - 1) + 1 <= RING, "a row's tiles fit the ring");
+    constexpr int HDR = L::HDR;
+    constexpr int NFIX = L::NFIX;
+    static_assert(2 * (NB - 1) + 1 + HDR <= RING && RING % 2 == 0, "a row's slots fit the ring");
     static_assert(NB <= 32 && NB % 2 == 0, "block rows in one wave's lanes");
     // the ring of tile slots (8 bytes per lane each); during the setup the
     // preorder's scratch
     __shared__ __attribute__((aligned(16))) uint2 s_big[BIG / 8];
     __shared__ __attribute__((aligned(16))) uint16_t s_k[KLDS ? NP * kD : 8];   // k rows, node order
     __shared__ __attribute__((aligned(16))) uint2 s_u[NB][kSolveWaves][64];   // U_t, bf16 B operands
-    __shared__ __attribute__((aligned(16))) uint2 s_d[NB][64];               // D_t, bf16 A operands
+    __shared__ __attribute__((aligned(16))) uint2 s_d[KLDS ? NB : 1][64];    // D_t, bf16 A operands (else in the ring)
+    __shared__ __attribute__((aligned(16))) uint16_t s_s0[KLDS ? 8 : 64 * kD];   // the slice's S0 rows, bf16
     __shared__ __attribute__((aligned(16))) float s_xd[kProducers][256];     // each producer's X_tt, fp32 [col][row]
     __shared__ __attribute__((aligned(16))) float s_lg[NP];
     __shared__ __attribute__((aligned(16))) float s_beta[NP];
@@ -138,7 +150,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     __shared__ int s_rstar[NB];                         // rows released before row t's slots are free
     __shared__ uint16_t s_items[L::ITEMS];              // producer items: row | (item of the row << 8)
     __shared__ int s_nitems;
-    __shared__ int s_done[NB];                          // row t's items finished (complete at s_tn[t] + 1)
+    __shared__ int s_done[NB];                          // row t's tiles and parts finished (complete at s_tn[t] + NFIX)
     __shared__ int s_oready[kSolveWaves];               // rows finished by each solve wave
     __shared__ int s_bad;                               // first node with an invalid parent
     __shared__ int s_notchain;                          // some node's parent is not the node before it
@@ -182,13 +194,25 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // a solve wave's 16 S0 rows (fp32; its bf16 operands are formed after the
     // setup): lane (r, q) takes row cbase + 16 wave + r, columns 32 cs + 8 q .. +7
     float4 s0_r[8];
-    if (solver) {
+    if (KLDS && solver) {
         const float* S0p =
             a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(cbase + 16 * wave + ln) * kD + 8 * lq;
 #pragma unroll
         for (int cs = 0; cs < 4; ++cs) {
             s0_r[2 * cs] = *reinterpret_cast<const float4*>(S0p + 32 * cs);
             s0_r[2 * cs + 1] = *reinterpret_cast<const float4*>(S0p + 32 * cs + 4);
+        }
+    }
+    // without k in LDS: the slice's 64 S0 rows (fp32), converted into LDS at
+    // the end of the setup for the producers
+    constexpr int S0L = KLDS ? 1 : (64 * kD / 4 + NT - 1) / NT;   // float4 loads per thread
+    float4 s0s[S0L];
+    if constexpr (!KLDS) {
+        const float* S0p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)cbase * kD;
+#pragma unroll
+        for (int k = 0; k < S0L; ++k) {                 // (float4 index in the 64 x 128 slice, clamped)
+            const int x = min(tid + k * NT, 64 * kD / 4 - 1);
+            s0s[k] = *reinterpret_cast<const float4*>(S0p + 4 * x);
         }
     }
     // k rows of the tree (node order, rows past the tree copy row n - 1) into
@@ -437,6 +461,19 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             const int u = wave + kk * kLargeWaves;
             if (u < NP / 4) *reinterpret_cast<u32x4*>(s_k + 4 * u * kD + 8 * lane) = k_r[kk];
         }
+    } else {
+        // S0 as bf16, row c at LDS row c, 16-byte chunks swizzled
+#pragma unroll
+        for (int k = 0; k < S0L; ++k) {
+            const int x = tid + k * NT;
+            if (x < 64 * kD / 4) {
+                const int r = x >> 5, c4 = x & 31;      // row, float4 within the row
+                uint2 w;
+                w.x = (uint32_t)bf16_rne(s0s[k].x) | ((uint32_t)bf16_rne(s0s[k].y) << 16);
+                w.y = (uint32_t)bf16_rne(s0s[k].z) | ((uint32_t)bf16_rne(s0s[k].w) << 16);
+                *reinterpret_cast<uint2*>(s_s0 + row_chunk(r, c4 >> 1) + 4 * (c4 & 1)) = w;
+            }
+        }
     }
     lds_barrier();
     // ancestor rows from the preorder: j is a strict ancestor of r exactly when
@@ -503,12 +540,11 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     //  * occupancy: tile (t, s), s < t, holds an ancestor pair exactly when a
     //    position of block s has its subtree reaching row t; row t's occupied
     //    blocks are listed in ascending order;
-    //  * the ring: row t takes the next 2 s_tn[t] + 1 slots (its -X tiles,
-    //    then its Y tiles, the diagonal block's last), counted over all rows
-    //    modulo RING; they may be written once every row whose slots they
-    //    reuse has been released by all solve waves;
-    //  * the producer items of row t: one for the diagonal block, then one per
-    //    C occupied blocks.
+    //  * the ring: row t takes the next HDR + 2 s_tn[t] + 1 slots, counted
+    //    over all rows modulo RING; they may be written once every row whose
+    //    slots they reuse has been released by all solve waves;
+    //  * the producer items of row t: one for the diagonal block, without k in
+    //    LDS one for the right-hand sides, then one per C occupied blocks.
     // Prefix sums over the rows go through LDS (one read of all rows' words).
     if (wave == 0) {
         int ml[NB];
@@ -528,8 +564,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             s_tn[lane] = tn;
             for (int k = 0; occ; ++k, occ &= occ - 1u) s_tcol[lane][k] = (uint8_t)__builtin_ctz(occ);
         }
-        const int sl = lane < nblk ? 2 * tn + 1 : 0;
-        const int ni = lane < nblk ? 1 + (tn + C - 1) / C : 0;
+        const int sl = lane < nblk ? 2 * tn + 1 + HDR : 0;
+        const int ni = lane < nblk ? NFIX + (tn + C - 1) / C : 0;
         // (slots and items of a row packed in one word: both totals stay
         // below 2^16)
         int* tmp = reinterpret_cast<int*>(s_big) + 16 + 3 * NP;   // (past the position tables)
@@ -572,6 +608,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                                               reinterpret_cast<const char*>(base) + off));
     };
     uint2* ring = s_big;                                // slot x: ring[64 x + lane]
+    u32x4* ring16 = reinterpret_cast<u32x4*>(s_big);    // slots x, x + 1 (x even): ring16[32 x + lane]
     auto slot_at = [&](int x) __attribute__((always_inline)) { return x < RING ? x : x - RING; };
 
     if (solver) {
@@ -581,9 +618,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         __builtin_amdgcn_s_setprio(2);
         const int g = wave;
         const int c0 = cbase + 16 * g;                  // this wave's first value column
-        // this wave's 16 S0 rows as bf16: lane (r, q) holds row c0 + r,
-        // columns 32 cs + 8 q .. +7; the A operand S0 (for S0 Q^T) and the B
-        // operand S0^T (for K S0^T)
+        // with k in LDS, this wave's 16 S0 rows as bf16: lane (r, q) holds
+        // row c0 + r, columns 32 cs + 8 q .. +7; the A operand S0 (for S0 Q^T)
+        // and the B operand S0^T (for K S0^T)
         bf16x8 s0g[4];
         s16x4 ident;
 #pragma unroll
@@ -593,20 +630,15 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             O + vo_base, (short)0, ((n - 1) * Hv + 1) * kD * 2, kBufferFlags);
         const char* Vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + vo_base + c0 + 4 * lq);
-        // a row's global operands, requested one row ahead: k (when not in
-        // LDS), q, and v of this wave's columns (lane (r, q): row r, columns
-        // 4 q .. +3)
+        // with k in LDS, a row's global operands, requested one row ahead: q,
+        // and v of this wave's columns (lane (r, q): row r, columns 4 q .. +3).
+        // Without, the producers form the row's right-hand sides.
         struct RowOps {
-            bf16x8 kt[KLDS ? 1 : 4];
             bf16x8 qt[4];
             uint2 vt;
         };
         auto fetch = [&](int t, RowOps& r) __attribute__((always_inline)) {
             t = min(t, nblk - 1);
-            if constexpr (!KLDS) {
-#pragma unroll
-                for (int cs = 0; cs < 4; ++cs) r.kt[cs] = gfrag(Kb, t, cs);
-            }
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) r.qt[cs] = gfrag(Qb, t, cs);
             const uint32_t vr = (uint32_t)node_at(16 * t + ln) * (uint32_t)(vo_row * 2);
@@ -616,11 +648,10 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         // requested first (the row's blocks, node indices, gates, this wave's
         // own U rows of the first SB occupied blocks), then the right-hand
         // side and e^G Q S0^T are formed, then the wait, then the row's tiles.
-        // The first SB occupied blocks are read and applied branch-free (the
-        // unused ones masked); rows with more take a loop.
+        // The first SB occupied blocks' operands are read together, the
+        // unused ones skipped by uniform branches; rows with more take a loop.
         constexpr int SB = 8;
         constexpr int TW = NB / 4;                      // words of a row of s_tcol
-        const s16x4 zero4 = {0, 0, 0, 0};
         auto row = [&](int t, RowOps& r) __attribute__((always_inline)) {
             const int nts = __builtin_amdgcn_readfirstlane(s_tn[t]);
             const int base = __builtin_amdgcn_readfirstlane(s_gslot[t]) % RING;
@@ -631,65 +662,70 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             const int pr = 16 * t + ln;                 // this lane's node of the products' columns
             const int no = node_at(pr);
             int nu[4];
-            float bt[4], lgr[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int i = 16 * t + 4 * lq + m;
-                nu[m] = node_at(i);
-                bt[m] = s_beta[i];
-                lgr[m] = s_lg[i];
-            }
-            const float lgc = s_lg[pr];
+            for (int m = 0; m < 4; ++m) nu[m] = node_at(16 * t + 4 * lq + m);
             s16x4 ub[SB], xa[SB], ya[SB];
 #pragma unroll
             for (int e = 0; e < SB; ++e) {
                 const int sb = e < nts ? (int)((tw[e >> 2] >> (8 * (e & 3))) & 0xffu) : t;
                 ub[e] = __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
             }
-            // R_t = diag(beta)(V_t - diag(e^G) K_t S0^T): [node 4q + m][column]
-            // (V moves into the accumulator layout by an exact product with I)
-            f32x4 ks = z;
+            f32x4 acc, oc;
+            if constexpr (KLDS) {
+                // R_t = diag(beta)(V_t - diag(e^G) K_t S0^T): [node 4q + m][column]
+                // (V moves into the accumulator layout by an exact product with I)
+                float bt[4], lgr[4];
 #pragma unroll
-            for (int cs = 0; cs < 4; ++cs) {
-                bf16x8 kk;
-                if constexpr (KLDS)
-                    kk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(no, 4 * cs + lq)));
-                else kk = r.kt[cs];
-                ks = mfma32(kk, s0g[cs], ks);
+                for (int m = 0; m < 4; ++m) {
+                    bt[m] = s_beta[16 * t + 4 * lq + m];
+                    lgr[m] = s_lg[16 * t + 4 * lq + m];
+                }
+                const float lgc = s_lg[pr];
+                f32x4 ks = z;
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs)
+                    ks = mfma32(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(no, 4 * cs + lq))),
+                                s0g[cs], ks);
+                const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, r.vt), ident, z);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) acc[m] = bt[m] * (vd[m] - __expf(lgr[m]) * ks[m]);
+                // e^G Q_t S0^T: [column 4q + m][node]
+                oc = z;
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) oc = mfma32(s0g[cs], r.qt[cs], oc);
+                oc *= __expf(lgc);
             }
-            const f32x4 vd = mfma16(__builtin_bit_cast(s16x4, r.vt), ident, z);
-            f32x4 acc;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] = bt[m] * (vd[m] - __expf(lgr[m]) * ks[m]);
-            // e^G Q_t S0^T: [column 4q + m][node]
-            f32x4 oc = z;
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs) oc = mfma32(s0g[cs], r.qt[cs], oc);
-            oc *= __expf(lgc);
-            wait_flag_ge(&s_done[t], nts + 1);
+            wait_flag_ge(&s_done[t], nts + NFIX);
+            if constexpr (!KLDS) {                      // the producers' right-hand sides
+                acc = __builtin_bit_cast(f32x4, ring16[slot_at(base + 2 * g) * 32 + lane]);
+                oc = __builtin_bit_cast(f32x4, ring16[slot_at(base + 8 + 2 * g) * 32 + lane]);
+            }
             // U_t = D_t (R_t - sum_s X_ts U_s) (the slots hold -X) and
             // O_t += sum_{s < t} Y_ts U_s as U^T Y^T; a row's Y tiles follow
             // its -X tiles, the diagonal block's last
+            const int xb = base + HDR;
 #pragma unroll
             for (int e = 0; e < SB; ++e) {
-                xa[e] = __builtin_bit_cast(s16x4, ring[slot_at(base + e) * 64 + lane]);
-                ya[e] = __builtin_bit_cast(s16x4, ring[slot_at(base + nts + e) * 64 + lane]);
+                xa[e] = __builtin_bit_cast(s16x4, ring[slot_at(xb + e) * 64 + lane]);
+                ya[e] = __builtin_bit_cast(s16x4, ring[slot_at(xb + nts + e) * 64 + lane]);
             }
-            const s16x4 dt = __builtin_bit_cast(s16x4, s_d[t][lane]);
-            const s16x4 ytt = __builtin_bit_cast(s16x4, ring[slot_at(base + 2 * nts) * 64 + lane]);
+            s16x4 dt;
+            if constexpr (KLDS) dt = __builtin_bit_cast(s16x4, s_d[t][lane]);
+            else dt = __builtin_bit_cast(s16x4, ring[slot_at(base + 16) * 64 + lane]);
+            const s16x4 ytt = __builtin_bit_cast(s16x4, ring[slot_at(xb + 2 * nts) * 64 + lane]);
             f32x4 acc2 = z, oc2 = z;
 #pragma unroll
             for (int e = 0; e < SB; ++e) {
-                // (an unused entry's operands are all zeroed: its LDS may hold
+                // (a uniform branch skips an unused entry, whose LDS may hold
                 // any bits, NaN included)
-                const bool v = e < nts;
-                const s16x4 x = v ? xa[e] : zero4, y = v ? ya[e] : zero4, u = v ? ub[e] : zero4;
-                if (e & 1) {
-                    acc2 = mfma16(x, u, acc2);
-                    oc2 = mfma16(u, y, oc2);
-                } else {
-                    acc = mfma16(x, u, acc);
-                    oc = mfma16(u, y, oc);
+                if (e < nts) {
+                    if (e & 1) {
+                        acc2 = mfma16(xa[e], ub[e], acc2);
+                        oc2 = mfma16(ub[e], ya[e], oc2);
+                    } else {
+                        acc = mfma16(xa[e], ub[e], acc);
+                        oc = mfma16(ub[e], ya[e], oc);
+                    }
                 }
             }
             for (int m0 = SB; m0 < nts; m0 += SB) {
@@ -698,21 +734,20 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                     const int m = m0 + e;
                     const int sb = m < nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]) : t;
                     ub[e] = __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
-                    xa[e] = __builtin_bit_cast(s16x4, ring[slot_at(base + m) * 64 + lane]);
-                    ya[e] = __builtin_bit_cast(s16x4, ring[slot_at(base + nts + m) * 64 + lane]);
+                    xa[e] = __builtin_bit_cast(s16x4, ring[slot_at(xb + m) * 64 + lane]);
+                    ya[e] = __builtin_bit_cast(s16x4, ring[slot_at(xb + nts + m) * 64 + lane]);
                 }
 #pragma unroll
-                for (int e = 0; e < SB; ++e) {
-                    const bool v = m0 + e < nts;
-                    const s16x4 x = v ? xa[e] : zero4, y = v ? ya[e] : zero4, u = v ? ub[e] : zero4;
-                    if (e & 1) {
-                        acc2 = mfma16(x, u, acc2);
-                        oc2 = mfma16(u, y, oc2);
-                    } else {
-                        acc = mfma16(x, u, acc);
-                        oc = mfma16(u, y, oc);
+                for (int e = 0; e < SB; ++e)
+                    if (m0 + e < nts) {
+                        if (e & 1) {
+                            acc2 = mfma16(xa[e], ub[e], acc2);
+                            oc2 = mfma16(ub[e], ya[e], oc2);
+                        } else {
+                            acc = mfma16(xa[e], ub[e], acc);
+                            oc = mfma16(ub[e], ya[e], oc);
+                        }
                     }
-                }
             }
             acc += acc2;
             s16x4 hi, lo;                               // (bf16 hi + lo parts: D_t meets R to ~16 bits)
@@ -738,18 +773,23 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             __builtin_amdgcn_raw_buffer_store_b64(w, o_rsrc, orow, 0, 0);
         };
         RowOps ra, rb;
-        fetch(0, ra);
-        // Nothing of the setup is in flight past this point but the first
-        // row's operands, so the loop's waits count only its own requests.
-        wait_vmem_le<KLDS ? 5 : 9>();
+        if constexpr (KLDS) {
+            fetch(0, ra);
+            // Nothing of the setup is in flight past this point but the first
+            // row's operands, so the loop's waits count only its own requests.
+            wait_vmem_le<5>();
 #pragma unroll
-        for (int cs = 0; cs < 4; ++cs) s0g[cs] = to_bf16x8(s0_r[2 * cs], s0_r[2 * cs + 1]);
-        for (int t = 0; t < nblk; t += 2) {
-            fetch(t + 1, rb);
-            row(t, ra);
-            if (t + 1 >= nblk) break;
-            fetch(t + 2, ra);
-            row(t + 1, rb);
+            for (int cs = 0; cs < 4; ++cs) s0g[cs] = to_bf16x8(s0_r[2 * cs], s0_r[2 * cs + 1]);
+            for (int t = 0; t < nblk; t += 2) {
+                fetch(t + 1, rb);
+                row(t, ra);
+                if (t + 1 >= nblk) break;
+                fetch(t + 2, ra);
+                row(t + 1, rb);
+            }
+        } else {
+            wait_vmem_all();
+            for (int t = 0; t < nblk; ++t) row(t, ra);
         }
         return;
     }
@@ -757,17 +797,22 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // ================= producers =================
     const int p = wave - kSolveWaves;                   // 0 .. kProducers - 1
     const int nitems = s_nitems;
+    const uint16_t* Vs = static_cast<const uint16_t*>(a.v) + vo_base + cbase;   // v of the slice's columns
     // An item's operands, requested one item ahead: its row, that row's
     // slots and occupied blocks, the node rows of its k fragments, q of its
-    // row and, when k is not in LDS, k of its row and of its column blocks.
+    // row and, when k is not in LDS, k of its row and either k of its
+    // column block (C = 1) or, for the right-hand sides' item, v of its row
+    // (the slice's 64 columns in two 32-column windows: lane (r, q) holds
+    // row r, columns 32 w + 8 q .. +7 of window w, in the same registers).
     struct ItemOps {
         int t, j, nts, base;
         int sb[C];                                      // the item's column blocks (t: none)
         int rt, rx[C];                                  // k rows (nodes) of lane ln in the row's / blocks' fragments
         bf16x8 kt[KLDS ? 1 : 4];
-        bf16x8 kx[KLDS ? 1 : C][KLDS ? 1 : 4];
+        u32x4 kx[KLDS ? 1 : C][KLDS ? 1 : 4];
         bf16x8 qt[4];
     };
+    static_assert(KLDS || C == 1, "v shares the registers of one column block's k");
     auto fetch = [&](int it, ItemOps& o) __attribute__((always_inline)) {
         const int code = __builtin_amdgcn_readfirstlane((int)s_items[min(it, nitems - 1)]);
         const int t = code & 0xff, j = code >> 8;
@@ -778,8 +823,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         o.rt = node_at(16 * t + ln);
 #pragma unroll
         for (int e = 0; e < C; ++e) {
-            const int m = (j - 1) * C + e;
-            o.sb[e] = j > 0 && m < o.nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]) : t;
+            const int m = (j - NFIX) * C + e;
+            o.sb[e] = j >= NFIX && m < o.nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]) : t;
             o.rx[e] = node_at(16 * o.sb[e] + ln);
         }
         const uint32_t qoff = (uint32_t)o.rt * (uint32_t)(kq_row * 2) + lane_col;
@@ -792,14 +837,14 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             for (int cs = 0; cs < 4; ++cs)
                 o.kt[cs] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                           reinterpret_cast<const char*>(Kb) + qoff + 64u * cs));
+            // (the same four requests for either: a branch here would make
+            // the compiler join two register sets, waiting for their loads)
+            const char* pk = reinterpret_cast<const char*>(Kb) + (uint32_t)o.rx[0] * (uint32_t)(kq_row * 2) + lane_col;
+            const char* pv = reinterpret_cast<const char*>(Vs) + (uint32_t)o.rt * (uint32_t)(vo_row * 2) + lane_col;
+            const bool isv = j == 1;
 #pragma unroll
-            for (int e = 0; e < C; ++e) {
-                const uint32_t xoff = (uint32_t)o.rx[e] * (uint32_t)(kq_row * 2) + lane_col;
-#pragma unroll
-                for (int cs = 0; cs < 4; ++cs)
-                    o.kx[e][cs] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                                 reinterpret_cast<const char*>(Kb) + xoff + 64u * cs));
-            }
+            for (int cs = 0; cs < 4; ++cs)
+                o.kx[0][cs] = *reinterpret_cast<const u32x4*>(isv ? pv + 64 * (cs & 1) : pk + 64 * cs);
         }
     };
     auto wait_ring = [&](int t) __attribute__((always_inline)) {
@@ -818,7 +863,48 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         const int pi = 16 * t + ln;                     // the Gram columns' node i
         const float lgi = s_lg[pi];
         int done;
-        if (j == 0) {
+        if (!KLDS && j == 1) {
+            if constexpr (!KLDS) {
+                // ---- the row's right-hand sides, for the four column groups ----
+                wait_ring(t);
+                const float bt0 = s_beta[16 * t + 4 * lq], bt1 = s_beta[16 * t + 4 * lq + 1];
+                const float bt2 = s_beta[16 * t + 4 * lq + 2], bt3 = s_beta[16 * t + 4 * lq + 3];
+                const float bt[4] = {bt0, bt1, bt2, bt3};
+                float eg[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) eg[m] = __expf(s_lg[16 * t + 4 * lq + m]);
+                const float egc = __expf(lgi);
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    // R_t = diag(beta)(V_t - diag(e^G) K_t S0^T): [node 4q + m][column]
+                    // (V moves into the accumulator layout by an exact product
+                    // with I); e^G Q_t S0^T: [column 4q + m][node]
+                    f32x4 ks = z, pc = z;
+#pragma unroll
+                    for (int cs = 0; cs < 4; ++cs) {
+                        const bf16x8 sf = __builtin_bit_cast(
+                            bf16x8, *reinterpret_cast<const u32x4*>(s_s0 + row_chunk(16 * gg + ln, 4 * cs + lq)));
+                        ks = mfma32(kt[cs], sf, ks);
+                        pc = mfma32(sf, o.qt[cs], pc);
+                    }
+                    // V of the group into the accumulator layout: an exact
+                    // product of its window with the columns 16 (gg % 2) ..
+                    // +15 of a 32 x 16 selection
+                    bf16x8 sel;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        sel[e] = (__bf16)((8 * lq + e == 16 * (gg & 1) + ln) ? 1.f : 0.f);
+                    const f32x4 vd = mfma32(__builtin_bit_cast(bf16x8, o.kx[0][gg >> 1]), sel, z);
+                    f32x4 R;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) R[m] = bt[m] * (vd[m] - eg[m] * ks[m]);
+                    pc *= egc;
+                    ring16[slot_at(base + 2 * gg) * 32 + lane] = __builtin_bit_cast(u32x4, R);
+                    ring16[slot_at(base + 8 + 2 * gg) * 32 + lane] = __builtin_bit_cast(u32x4, pc);
+                }
+            }
+            done = 1;
+        } else if (j == 0) {
             // ---- D_t = (I + X_tt)^-1 and Y_tt ----
             f32x4 gk = z, gq = z;
 #pragma unroll
@@ -870,11 +956,12 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                     accd[e] = 4 * qd + e > m ? upd : accd[e];
                 }
             }
-            uint16_t* dd = reinterpret_cast<uint16_t*>(&s_d[t][0]);
+            uint16_t* dd = KLDS ? reinterpret_cast<uint16_t*>(&s_d[t][0])
+                                : reinterpret_cast<uint16_t*>(&ring[slot_at(base + 16) * 64]);
+            wait_ring(t);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
-            wait_ring(t);
-            ring[slot_at(base + 2 * nts) * 64 + lane] = __builtin_bit_cast(uint2, yb);
+            ring[slot_at(base + HDR + 2 * nts) * 64 + lane] = __builtin_bit_cast(uint2, yb);
             done = 1;
         } else {
             // ---- -X_ts and Y_ts for C occupied blocks s ----
@@ -882,14 +969,14 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             bf16x8 kx[C][4];
 #pragma unroll
             for (int e = 0; e < C; ++e) {
-                mm_[e] = (j - 1) * C + e;
+                mm_[e] = (j - NFIX) * C + e;
                 sb[e] = o.sb[e];
 #pragma unroll
                 for (int cs = 0; cs < 4; ++cs) {
                     if constexpr (KLDS)
                         kx[e][cs] = __builtin_bit_cast(bf16x8,
                                                        *reinterpret_cast<const u32x4*>(s_k + row_chunk(o.rx[e], 4 * cs + lq)));
-                    else kx[e][cs] = o.kx[e][cs];
+                    else kx[e][cs] = __builtin_bit_cast(bf16x8, o.kx[e][cs]);
                 }
             }
             f32x4 gx[C], gy[C];
@@ -919,8 +1006,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
 #pragma unroll
             for (int e = 0; e < C; ++e)
                 if (mm_[e] < nts) {
-                    ring[slot_at(base + mm_[e]) * 64 + lane] = __builtin_bit_cast(uint2, xn[e]);
-                    ring[slot_at(base + nts + mm_[e]) * 64 + lane] = __builtin_bit_cast(uint2, yv[e]);
+                    ring[slot_at(base + HDR + mm_[e]) * 64 + lane] = __builtin_bit_cast(uint2, xn[e]);
+                    ring[slot_at(base + HDR + nts + mm_[e]) * 64 + lane] = __builtin_bit_cast(uint2, yv[e]);
                     ++done;
                 }
         }
@@ -930,7 +1017,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     ItemOps ia, ib;
     fetch(p, ia);
     // (as for the solve waves: only the first item's operands are in flight)
-    wait_vmem_le<KLDS ? 4 : 4 + 4 + 4 * C>();
+    wait_vmem_le<KLDS ? 4 : 4 + 4 + 4>();
     for (int it = p; it < nitems; it += 2 * kProducers) {
         fetch(it + kProducers, ib);
         work(ia);
