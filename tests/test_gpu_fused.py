@@ -195,14 +195,34 @@ def test_fused_in_place():
     run_case("in-place", steps, "bf16", 2, 4, in_place=True)
 
 
-@pytest.mark.parametrize("N,d,io", [(200, 128, "bf16"), (40, 16, "f32"), (70, 64, "bf16")])
+@pytest.mark.parametrize("N,d,io", [(40, 16, "f32"), (70, 64, "bf16")])
 def test_fused_other_sizes(N, d, io):
-    """Sizes outside the single-pass form run commit and verify as two launches."""
+    """Sizes outside the MFMA forms run commit and verify as two launches."""
     rng = np.random.default_rng(97 + N)
     ps = [[W.tree_random_recursive(rng, N), W.tree_chain(N)] for _ in range(2)]
     accs = [[W.pick_leaf(rng, p[0]), N - 1] for p in ps]
     steps = chain_steps(98 + N, ps, accs, 1, 2, d, io)
     run_case(f"other N={N} d={d}", steps, io, 1, 2)
+
+
+@pytest.mark.parametrize("N", [200, 256, 300, 512])
+def test_fused_large_trees(N):
+    """Trees of 129 .. 512 nodes: the commit runs inside the larger-tree
+    launch.  Chains whose every node is accepted (paths of N nodes, several
+    rounds of 256 path nodes at N = 300 and 512), random recursive trees with
+    a leaf accepted, a sequence with nothing accepted and one whose previous
+    tree is invalid; then the same loop in place."""
+    rng = np.random.default_rng(110 + N)
+    trees = lambda: [W.tree_chain(N), W.tree_random_recursive(rng, N), W.tree_chain(N),
+                     W.tree_random_recursive(rng, N)]
+    ps = [trees() for _ in range(3)]
+    ps[1][3] = ps[1][3].copy(); ps[1][3][N // 2] = N - 1     # forward parent: invalid tree
+    accs = [[N - 1, W.pick_leaf(rng, p[1]), -1, W.pick_leaf(rng, p[3])] for p in ps]
+    steps = chain_steps(111 + N, ps, accs, 2, 4, 128)
+    fused, ref = run_case(f"large N={N}", steps, "bf16", 2, 4)
+    assert ref[1]["tree_status"][3] != 0 and fused[1]["path_len"][3] == -1
+    assert fused[0]["path_len"][0] == N
+    run_case(f"large in-place N={N}", steps, "bf16", 2, 4, in_place=True)
 
 
 def test_fused_full_batch_shape():

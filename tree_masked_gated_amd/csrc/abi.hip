@@ -106,12 +106,13 @@ int commit_verify_impl(const gdn_tree_dims* dims, const int32_t* offsets_prev, c
     hipError_t e;
     if (verify_tiled_supported(a, dims->io_dtype)) {
         e = launch_commit_verify_tiled(a, c, dims->io_dtype, stream);
+    } else if (verify_large_supported(a, dims->io_dtype)) {
+        e = launch_commit_verify_large(a, c, dims->io_dtype, stream);
     } else {
         e = launch_commit(c, dims->io_dtype, stream);
         if (e == hipSuccess) {
             a.S0 = S_new;
-            e = verify_large_supported(a, dims->io_dtype) ? launch_verify_large(a, dims->io_dtype, stream)
-                                                           : launch_verify_generic(a, dims->io_dtype, stream);
+            e = launch_verify_generic(a, dims->io_dtype, stream);
         }
     }
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;

@@ -21,6 +21,8 @@ hipError_t launch_commit_verify_tiled(const VerifyArgs& a, const CommitArgs& c, 
 // (one launch: the tree check, its ancestor rows into the cache, the solve).
 bool verify_large_supported(const VerifyArgs& a, int io);
 hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream);
+// The same with the previous tree's commit fused in front (a.S0 = c.S_in).
+hipError_t launch_commit_verify_large(const VerifyArgs& a, const CommitArgs& c, int io, hipStream_t stream);
 
 // Deferred commit of the accepted node's state.
 hipError_t launch_commit(const CommitArgs& a, int io, hipStream_t stream);

@@ -113,8 +113,11 @@ struct LargeShape {
     static constexpr int ITEMS = NFIX * NB + (C == 1 ? NB * (NB - 1) / 2 : (NB / 2) * (NB / 2));
 };
 
-template <int NB>
-__global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyArgs a, int units) {
+// FUSED: the previous tree's commit (page "Trees from Marginals", section 3:
+// the deferred state commit) runs first in the same launch; its state rows
+// become this verification's S0 without a trip through memory.
+template <int NB, bool FUSED>
+__global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyArgs a, CommitArgs c, int units) {
     using L = LargeShape<NB>;
     constexpr int NP = L::NP;
     constexpr int NT = kLargeThreads;
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // a solve wave's 16 S0 rows (fp32; its bf16 operands are formed after the
     // setup): lane (r, q) takes row cbase + 16 wave + r, columns 32 cs + 8 q .. +7
     float4 s0_r[8];
-    if (KLDS && solver) {
+    if (!FUSED && KLDS && solver) {
         const float* S0p =
             a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)(cbase + 16 * wave + ln) * kD + 8 * lq;
 #pragma unroll
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // the end of the setup for the producers
     constexpr int S0L = KLDS ? 1 : (64 * kD / 4 + NT - 1) / NT;   // float4 loads per thread
     float4 s0s[S0L];
-    if constexpr (!KLDS) {
+    if constexpr (!KLDS && !FUSED) {
         const float* S0p = a.S0 + ((size_t)b * Hv + h) * kD * kD + (size_t)cbase * kD;
 #pragma unroll
         for (int k = 0; k < S0L; ++k) {                 // (float4 index in the 64 x 128 slice, clamped)
@@ -216,25 +219,188 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         }
     }
     // k rows of the tree (node order, rows past the tree copy row n - 1) into
-    // registers, written to LDS at the end of the setup: one 1 KB unit is
-    // four rows, lane l taking row 4u + l / 16 and its logical chunk
-    // (l % 16) ^ (row & 15), so the store is one contiguous 16-byte write per lane
+    // registers, written to LDS at the end of the setup (a direct-to-LDS
+    // load would make the compiler wait for it before the setup's first LDS
+    // access): one 1 KB unit is four rows, lane l taking row 4u + l / 16 and
+    // its logical chunk (l % 16) ^ (row & 15), so the store is one contiguous
+    // 16-byte write per lane
+    // (with the commit fused, requested after the commit's first requests:
+    // requests retire in order, so the commit would otherwise wait for them)
     constexpr int KI = KLDS ? (NP / 4 + kLargeWaves - 1) / kLargeWaves : 1;
     u32x4 k_r[KI];
-    if constexpr (KLDS) {
+    auto request_k = [&]() __attribute__((always_inline)) {
+        if constexpr (KLDS) {
 #pragma unroll
-        for (int kk = 0; kk < KI; ++kk) {
-            const int u = min(wave + kk * kLargeWaves, NP / 4 - 1);
-            const int row = 4 * u + (lane >> 4), pc = lane & 15;
-            const int srow = min(row, max(n - 1, 0));
-            k_r[kk] = *reinterpret_cast<const u32x4*>(Kb + (size_t)srow * kq_row + ((pc ^ (row & 15)) << 3));
+            for (int kk = 0; kk < KI; ++kk) {
+                const int u = min(wave + kk * kLargeWaves, NP / 4 - 1);
+                const int row = 4 * u + (lane >> 4), pc = lane & 15;
+                const int srow = min(row, max(n - 1, 0));
+                k_r[kk] = *reinterpret_cast<const u32x4*>(Kb + (size_t)srow * kq_row + ((pc ^ (row & 15)) << 3));
+            }
         }
-    }
+    };
+    if constexpr (!FUSED) request_k();
     // (the loaded values are used only below: their arithmetic may not be
     // moved up to the loads, where it would wait for them before the other
     // requests are out)
 #pragma unroll
     for (int k = 0; k < PL; ++k) asm volatile("" : "+v"(par_r[k]), "+v"(g_r[k]), "+v"(beta_r[k]));
+    // ---- the previous tree's commit (fused form) ----
+    // S_a = e^(G_a) S_prev + sum_{j on a's path} e^(G_a - G_j) u_j k_j^T for
+    // the slice's 64 state rows, a the previous tree's accepted node and G, u
+    // its cached path log-gates and writes; as in the separate commit, as
+    // D^T = e^(G_a) D_in^T + K_P^T (diag(w) U_P), with the weighted u split
+    // into bf16 hi + lo parts (about 16 mantissa bits).  Solve wave g forms
+    // its rows c0 .. c0 + 15 alone, 16 path nodes at a time, before the
+    // verification's setup: its eight accumulator tiles (lane (r, q): row
+    // c0 + r, columns 16 tc + 4 q .. +3) take K^T and W tiles that the
+    // matrix cores themselves transpose, an exact product of the tiles as
+    // read (nodes in rows) with an identity or column selection, so nothing
+    // goes through LDS and no wave waits for another.  The rows go to the
+    // new state and, as bf16, become this launch's S0 (the solve waves'
+    // operands with k in LDS, the producers' table without).
+    bf16x8 s0g[4];
+    if constexpr (FUSED) {
+        // The path comes through the scalar cache (uniform addresses in the
+        // constant address space): a vector load here would wait for every
+        // vector request above it, the k rows included.
+        typedef const __attribute__((address_space(4))) uint32_t* cu32;
+        typedef const __attribute__((address_space(4))) float* cf32;
+        typedef const __attribute__((address_space(4))) int32_t* ci32;
+        int* s_path = reinterpret_cast<int*>(reinterpret_cast<char*>(s_big) + BIG) - kLargeMaxN;
+        const int Wc = (N + 31) / 32;
+        const int acc = ((ci32)c.accepted)[b];
+        const SeqRows prow = seq_rows(c.offsets, b, N);
+        const bool cvalid = ((ci32)c.status)[b] == 0 && prow.n >= 0 && acc >= -1 && acc < prow.n;
+        const int aw = acc < 0 ? 0 : acc;
+        cu32 arow = (cu32)(c.anc_mask + ((size_t)b * N + aw) * Wc);   // the accepted node's ancestor row
+        const float* lgp = c.log_gamma + ((size_t)b * Hv + h) * N;
+        const float ga = ((cf32)lgp)[aw];
+        if (wave == 0) {
+            // strict ancestors ascending, then a: word w's set bits at
+            // positions counted from the words before it, lane l taking bit l
+            int base = 0;
+            for (int w = 0; w < Wc; ++w) {
+                const uint32_t x = arow[w];
+                if (cvalid && acc >= 0 && lane < 32 && ((x >> lane) & 1u))
+                    s_path[base + __popc(x & ((1u << lane) - 1u))] = 32 * w + lane;
+                base += __popc(x);
+            }
+            const int plen = !cvalid ? -1 : acc < 0 ? 0 : base + 1;
+            if (lane == 0) {
+                if (plen > 0) s_path[plen - 1] = acc;
+                s_more[0] = plen;                       // (shared with the other waves below)
+            }
+        }
+        lds_barrier();
+        static_assert(64 * kD * 2 + kLargeMaxN * 4 <= BIG, "the path fits past the temporary S0 rows");
+        const int plen = s_more[0];
+        if (!solver || plen <= 0) request_k();
+        if (h == 0 && slice == 0) {
+            int32_t* pb = c.path + prow.row0;
+            for (int m = tid; m < prow.n; m += NT) pb[m] = m < plen ? s_path[m] : -1;
+            if (tid == 0) c.path_len[b] = plen;
+        }
+        if (solver) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const int g = wave, c0 = cbase + 16 * g;
+            const size_t srow = ((size_t)b * Hv + h) * kD * kD + (size_t)(c0 + ln) * kD + 4 * lq;
+            f32x4 cD[8];
+            const float dec = plen > 0 ? __expf(ga) : 1.f;
+#pragma unroll
+            for (int tc = 0; tc < 8; ++tc) cD[tc] = dec * *reinterpret_cast<const f32x4*>(c.S_in + srow + 16 * tc);
+            if (plen > 0) {
+                const uint16_t* Kp = static_cast<const uint16_t*>(c.k) + (prow.row0 * Hk + hk) * kD;
+                const float* Up = c.u + ((size_t)b * Hv + h) * (size_t)N * kD + c0;
+                // a group of 16 path nodes, node ln of lane (ln, q): k columns
+                // 32 w + 8 q .. +7 (w = 0 .. 3), u columns c0 + 4 q .. +3, its
+                // log-gate (nodes past the path re-read its last, weight 0)
+                struct Grp {
+                    u32x4 k[4];
+                    float4 u;
+                    float lg;
+                };
+                auto load_grp = [&](int g0, Grp& G) __attribute__((always_inline)) {
+                    const int m = min(g0 + ln, plen - 1);
+                    const int j = s_path[m];
+                    const uint16_t* kr = Kp + (size_t)j * kq_row + 8 * lq;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) G.k[w] = *reinterpret_cast<const u32x4*>(kr + 32 * w);
+                    G.u = *reinterpret_cast<const float4*>(Up + (size_t)j * kD + 4 * lq);
+                    G.lg = lgp[j];
+                    // (no memory access may move across: the requests stay
+                    // here, a group ahead of their use, and nothing waits)
+                    asm volatile("" ::: "memory");
+                };
+                // identity (16 x 16) and the two 16-column selections of a
+                // 32-column window, as B operands
+                s16x4 ident;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
+                bf16x8 sel[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sel[hh][e] = (__bf16)((8 * lq + e == 16 * hh + ln) ? 1.f : 0.f);
+                auto apply = [&](int g0, const Grp& G) __attribute__((always_inline)) {
+                    // K^T tiles: lane (c, q) holds k of nodes 4q .. 4q+3 at column 16 tc + c
+                    s16x4 kt[8];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh)
+                            kt[2 * w + hh] = to_bf16x4(mfma32(__builtin_bit_cast(bf16x8, G.k[w]), sel[hh], z));
+                    // W tiles (weighted u, hi and lo): lane (r, q) holds nodes 4q .. 4q+3 of row c0 + r
+                    const float w = g0 + ln < plen ? __expf(ga - G.lg) : 0.f;
+                    const f32x4 wu = {w * G.u.x, w * G.u.y, w * G.u.z, w * G.u.w};
+                    s16x4 whi, wlo;
+                    split4(wu, whi, wlo);
+                    const s16x4 bh = to_bf16x4(mfma16(whi, ident, z));
+                    const s16x4 bl = to_bf16x4(mfma16(wlo, ident, z));
+#pragma unroll
+                    for (int tc = 0; tc < 8; ++tc) cD[tc] = mfma16(kt[tc], bl, mfma16(kt[tc], bh, cD[tc]));
+                };
+                // three groups in flight: each group's requests go out two
+                // groups ahead of its products
+                Grp gp0, gp1, gp2;
+                load_grp(0, gp0);
+                load_grp(min(16, plen - 1), gp1);
+                request_k();
+                for (int g0 = 0; g0 < plen; g0 += 48) {
+                    load_grp(min(g0 + 32, plen - 1), gp2);
+                    apply(g0, gp0);
+                    if (g0 + 16 >= plen) break;
+                    load_grp(min(g0 + 48, plen - 1), gp0);
+                    apply(g0 + 16, gp1);
+                    if (g0 + 32 >= plen) break;
+                    load_grp(min(g0 + 64, plen - 1), gp1);
+                    apply(g0 + 32, gp2);
+                }
+            }
+            // (in place, S_in = S_out: each workgroup reads its rows before writing them)
+            if (plen > 0 || c.S_in != c.S_out) {
+#pragma unroll
+                for (int tc = 0; tc < 8; ++tc) *reinterpret_cast<f32x4*>(c.S_out + srow + 16 * tc) = cD[tc];
+            }
+            // this wave's rows as bf16 through LDS (its own rows: no barrier
+            // needed; the other waves touch the area only after the next
+            // barrier, which this wave reaches only once done with it)
+            uint16_t* s0t = KLDS ? reinterpret_cast<uint16_t*>(s_big) : s_s0;   // [64][128] bf16, chunks swizzled
+#pragma unroll
+            for (int tc = 0; tc < 8; ++tc) {
+                uint2 w;
+                w.x = (uint32_t)bf16_rne(cD[tc][0]) | ((uint32_t)bf16_rne(cD[tc][1]) << 16);
+                w.y = (uint32_t)bf16_rne(cD[tc][2]) | ((uint32_t)bf16_rne(cD[tc][3]) << 16);
+                *reinterpret_cast<uint2*>(s0t + row_chunk(16 * g + ln, 2 * tc + (lq >> 1)) + 4 * (lq & 1)) = w;
+            }
+            if constexpr (KLDS) {
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs)
+                    s0g[cs] = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4*>(s0t + row_chunk(16 * g + ln, 4 * cs + lq)));
+            }
+        }
+    }
     // (Every barrier of the setup orders LDS only: the global loads above and
     // the cache rows stored below stay in flight across it.)
     // tree check, the same in every workgroup of the tree: 0, or one plus the
@@ -266,9 +432,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         const float qnan = __uint_as_float(0x7fc00000u);
         if (solver)
             for (int x = lane; x < N * 16; x += 64) {
-                const int i = x >> 4, c = cbase + 16 * wave + (x & 15);
-                if (i < n) O[vo_base + (size_t)i * vo_row + c] = 0x7fc0;
-                Ug[(size_t)i * kD + c] = qnan;
+                const int i = x >> 4, col = cbase + 16 * wave + (x & 15);
+                if (i < n) O[vo_base + (size_t)i * vo_row + col] = 0x7fc0;
+                Ug[(size_t)i * kD + col] = qnan;
             }
         if (slice == 0)
             for (int i = tid; i < N; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = qnan;
@@ -461,7 +627,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             const int u = wave + kk * kLargeWaves;
             if (u < NP / 4) *reinterpret_cast<u32x4*>(s_k + 4 * u * kD + 8 * lane) = k_r[kk];
         }
-    } else {
+    } else if constexpr (!FUSED) {
         // S0 as bf16, row c at LDS row c, 16-byte chunks swizzled
 #pragma unroll
         for (int k = 0; k < S0L; ++k) {
@@ -618,10 +784,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         __builtin_amdgcn_s_setprio(2);
         const int g = wave;
         const int c0 = cbase + 16 * g;                  // this wave's first value column
-        // with k in LDS, this wave's 16 S0 rows as bf16: lane (r, q) holds
-        // row c0 + r, columns 32 cs + 8 q .. +7; the A operand S0 (for S0 Q^T)
-        // and the B operand S0^T (for K S0^T)
-        bf16x8 s0g[4];
+        // with k in LDS, s0g: this wave's 16 S0 rows as bf16, lane (r, q)
+        // holding row c0 + r, columns 32 cs + 8 q .. +7; the A operand S0 (for
+        // S0 Q^T) and the B operand S0^T (for K S0^T)
         s16x4 ident;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
@@ -778,8 +943,10 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             // Nothing of the setup is in flight past this point but the first
             // row's operands, so the loop's waits count only its own requests.
             wait_vmem_le<5>();
+            if constexpr (!FUSED) {
 #pragma unroll
-            for (int cs = 0; cs < 4; ++cs) s0g[cs] = to_bf16x8(s0_r[2 * cs], s0_r[2 * cs + 1]);
+                for (int cs = 0; cs < 4; ++cs) s0g[cs] = to_bf16x8(s0_r[2 * cs], s0_r[2 * cs + 1]);
+            }
             for (int t = 0; t < nblk; t += 2) {
                 fetch(t + 1, rb);
                 row(t, ra);
@@ -798,7 +965,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     const int p = wave - kSolveWaves;                   // 0 .. kProducers - 1
     const int nitems = s_nitems;
     const uint16_t* Vs = static_cast<const uint16_t*>(a.v) + vo_base + cbase;   // v of the slice's columns
-    // An item's operands, requested one item ahead: its row, that row's
+    // An item's operands, requested during the previous item: its row, that row's
     // slots and occupied blocks, the node rows of its k fragments, q of its
     // row and, when k is not in LDS, k of its row and either k of its
     // column block (C = 1) or, for the right-hand sides' item, v of its row
@@ -851,67 +1018,92 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
 #pragma unroll
         for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_oready[gg], s_rstar[t]);
     };
-    auto work = [&](ItemOps& o) __attribute__((always_inline)) {
+    // One item: its products from o, then o is refilled with the item nxt's
+    // operands (so their requests overlap this item's remaining work: masks,
+    // substitution, the ring wait and stores), then the rest.
+    auto work = [&](ItemOps& o, int nxt) __attribute__((always_inline)) {
         const int t = o.t, j = o.j, nts = o.nts, base = o.base;
-        bf16x8 kt[4];
+        int sb[C];
 #pragma unroll
-        for (int cs = 0; cs < 4; ++cs) {
-            if constexpr (KLDS)
-                kt[cs] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(o.rt, 4 * cs + lq)));
-            else kt[cs] = o.kt[cs];
-        }
+        for (int e = 0; e < C; ++e) sb[e] = o.sb[e];
         const int pi = 16 * t + ln;                     // the Gram columns' node i
         const float lgi = s_lg[pi];
-        int done;
-        if (!KLDS && j == 1) {
-            if constexpr (!KLDS) {
-                // ---- the row's right-hand sides, for the four column groups ----
-                wait_ring(t);
-                const float bt0 = s_beta[16 * t + 4 * lq], bt1 = s_beta[16 * t + 4 * lq + 1];
-                const float bt2 = s_beta[16 * t + 4 * lq + 2], bt3 = s_beta[16 * t + 4 * lq + 3];
-                const float bt[4] = {bt0, bt1, bt2, bt3};
-                float eg[4];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) eg[m] = __expf(s_lg[16 * t + 4 * lq + m]);
-                const float egc = __expf(lgi);
-#pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    // R_t = diag(beta)(V_t - diag(e^G) K_t S0^T): [node 4q + m][column]
-                    // (V moves into the accumulator layout by an exact product
-                    // with I); e^G Q_t S0^T: [column 4q + m][node]
-                    f32x4 ks = z, pc = z;
-#pragma unroll
-                    for (int cs = 0; cs < 4; ++cs) {
-                        const bf16x8 sf = __builtin_bit_cast(
-                            bf16x8, *reinterpret_cast<const u32x4*>(s_s0 + row_chunk(16 * gg + ln, 4 * cs + lq)));
-                        ks = mfma32(kt[cs], sf, ks);
-                        pc = mfma32(sf, o.qt[cs], pc);
-                    }
-                    // V of the group into the accumulator layout: an exact
-                    // product of its window with the columns 16 (gg % 2) ..
-                    // +15 of a 32 x 16 selection
-                    bf16x8 sel;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        sel[e] = (__bf16)((8 * lq + e == 16 * (gg & 1) + ln) ? 1.f : 0.f);
-                    const f32x4 vd = mfma32(__builtin_bit_cast(bf16x8, o.kx[0][gg >> 1]), sel, z);
-                    f32x4 R;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) R[m] = bt[m] * (vd[m] - eg[m] * ks[m]);
-                    pc *= egc;
-                    ring16[slot_at(base + 2 * gg) * 32 + lane] = __builtin_bit_cast(u32x4, R);
-                    ring16[slot_at(base + 8 + 2 * gg) * 32 + lane] = __builtin_bit_cast(u32x4, pc);
-                }
-            }
-            done = 1;
-        } else if (j == 0) {
-            // ---- D_t = (I + X_tt)^-1 and Y_tt ----
-            f32x4 gk = z, gq = z;
+        const bool rhs_item = !KLDS && j == 1, diag = j == 0;
+        // ---- products ----
+        f32x4 gA[C], gB[C];    // diagonal item: X_tt, Y_tt Grams; else -X_ts, Y_ts Grams of its blocks
+        {
+            bf16x8 kt[4];
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) {
-                gk = mfma32(kt[cs], kt[cs], gk);        // lane (j, q): k_{4q+m} . k_j
-                gq = mfma32(kt[cs], o.qt[cs], gq);      // lane (i, q): k_{4q+m} . q_i
+                if constexpr (KLDS)
+                    kt[cs] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(o.rt, 4 * cs + lq)));
+                else kt[cs] = o.kt[cs];
             }
+#pragma unroll
+            for (int e = 0; e < C; ++e) gA[e] = gB[e] = z;
+            if (rhs_item) {
+                if constexpr (!KLDS) {
+                    // ---- the row's right-hand sides, for the four column groups ----
+                    wait_ring(t);
+                    float bt[4], eg[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        bt[m] = s_beta[16 * t + 4 * lq + m];
+                        eg[m] = __expf(s_lg[16 * t + 4 * lq + m]);
+                    }
+                    const float egc = __expf(lgi);
+#pragma unroll
+                    for (int gg = 0; gg < 4; ++gg) {
+                        // R_t = diag(beta)(V_t - diag(e^G) K_t S0^T): [node 4q + m][column];
+                        // e^G Q_t S0^T: [column 4q + m][node]
+                        f32x4 ks = z, pc = z;
+#pragma unroll
+                        for (int cs = 0; cs < 4; ++cs) {
+                            const bf16x8 sf = __builtin_bit_cast(
+                                bf16x8, *reinterpret_cast<const u32x4*>(s_s0 + row_chunk(16 * gg + ln, 4 * cs + lq)));
+                            ks = mfma32(kt[cs], sf, ks);
+                            pc = mfma32(sf, o.qt[cs], pc);
+                        }
+                        // V of the group into the accumulator layout: an exact
+                        // product of its window with the columns 16 (gg % 2) ..
+                        // +15 of a 32 x 16 selection
+                        bf16x8 sel;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            sel[e] = (__bf16)((8 * lq + e == 16 * (gg & 1) + ln) ? 1.f : 0.f);
+                        const f32x4 vd = mfma32(__builtin_bit_cast(bf16x8, o.kx[0][gg >> 1]), sel, z);
+                        f32x4 R;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) R[m] = bt[m] * (vd[m] - eg[m] * ks[m]);
+                        pc *= egc;
+                        ring16[slot_at(base + 2 * gg) * 32 + lane] = __builtin_bit_cast(u32x4, R);
+                        ring16[slot_at(base + 8 + 2 * gg) * 32 + lane] = __builtin_bit_cast(u32x4, pc);
+                    }
+                }
+            } else if (diag) {
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) {
+                    gA[0] = mfma32(kt[cs], kt[cs], gA[0]);     // lane (j, q): k_{4q+m} . k_j
+                    gB[0] = mfma32(kt[cs], o.qt[cs], gB[0]);   // lane (i, q): k_{4q+m} . q_i
+                }
+            } else {
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs)
+#pragma unroll
+                    for (int e = 0; e < C; ++e) {
+                        bf16x8 kx;
+                        if constexpr (KLDS)
+                            kx = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(o.rx[e], 4 * cs + lq)));
+                        else kx = __builtin_bit_cast(bf16x8, o.kx[e][cs]);
+                        gA[e] = mfma32(kx, kt[cs], gA[e]);     // lane (i, q): k_{j = 4q+m} . k_i
+                        gB[e] = mfma32(kx, o.qt[cs], gB[e]);   // lane (i, q): k_j . q_i
+                    }
+            }
+        }
+        fetch(nxt, o);
+        int done = 1;
+        if (diag) {
+            // ---- D_t = (I + X_tt)^-1 and Y_tt ----
             // X_tt[i][j] at lane (j, q), element m: i = 4q + m
             float xv[4];
             {
@@ -922,7 +1114,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 for (int m = 0; m < 4; ++m) {
                     const int pi2 = 16 * t + 4 * lq + m;
                     const bool anc = (pj < pi2) & (pi2 <= lj);
-                    const float x = s_beta[pi2] * __expf(fminf(s_lg[pi2] - lgj, 0.f)) * gk[m];
+                    const float x = s_beta[pi2] * __expf(fminf(s_lg[pi2] - lgj, 0.f)) * gA[0][m];
                     xv[m] = anc ? x : 0.f;
                 }
             }
@@ -932,7 +1124,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             for (int m = 0; m < 4; ++m) {
                 const int pj = 16 * t + 4 * lq + m;
                 const bool anc = (pj <= pi) & (pi <= (int)s_last[pj]);
-                const float y = __expf(fminf(lgi - s_lg[pj], 0.f)) * gq[m];
+                const float y = __expf(fminf(lgi - s_lg[pj], 0.f)) * gB[0][m];
                 yb[m] = (short)bf16_rne(anc ? y : 0.f);
             }
             // fp32 forward substitution, four lanes per column: lane 4c + qd
@@ -962,33 +1154,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
 #pragma unroll
             for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
             ring[slot_at(base + HDR + 2 * nts) * 64 + lane] = __builtin_bit_cast(uint2, yb);
-            done = 1;
-        } else {
+        } else if (!rhs_item) {
             // ---- -X_ts and Y_ts for C occupied blocks s ----
-            int mm_[C], sb[C];
-            bf16x8 kx[C][4];
-#pragma unroll
-            for (int e = 0; e < C; ++e) {
-                mm_[e] = (j - NFIX) * C + e;
-                sb[e] = o.sb[e];
-#pragma unroll
-                for (int cs = 0; cs < 4; ++cs) {
-                    if constexpr (KLDS)
-                        kx[e][cs] = __builtin_bit_cast(bf16x8,
-                                                       *reinterpret_cast<const u32x4*>(s_k + row_chunk(o.rx[e], 4 * cs + lq)));
-                    else kx[e][cs] = __builtin_bit_cast(bf16x8, o.kx[e][cs]);
-                }
-            }
-            f32x4 gx[C], gy[C];
-#pragma unroll
-            for (int e = 0; e < C; ++e) gx[e] = gy[e] = z;
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs)
-#pragma unroll
-                for (int e = 0; e < C; ++e) {
-                    gx[e] = mfma32(kx[e][cs], kt[cs], gx[e]);     // lane (i, q): k_{j = 4q+m} . k_i
-                    gy[e] = mfma32(kx[e][cs], o.qt[cs], gy[e]);   // lane (i, q): k_j . q_i
-                }
             const float bi = s_beta[pi];
             s16x4 xn[C], yv[C];
 #pragma unroll
@@ -998,33 +1165,29 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                     const int pj = 16 * sb[e] + 4 * lq + m;
                     const bool anc = pi <= (int)s_last[pj];      // (pj < pi: s < t)
                     const float dec = __expf(fminf(lgi - s_lg[pj], 0.f));
-                    xn[e][m] = (short)bf16_rne(anc ? -bi * dec * gx[e][m] : 0.f);
-                    yv[e][m] = (short)bf16_rne(anc ? dec * gy[e][m] : 0.f);
+                    xn[e][m] = (short)bf16_rne(anc ? -bi * dec * gA[e][m] : 0.f);
+                    yv[e][m] = (short)bf16_rne(anc ? dec * gB[e][m] : 0.f);
                 }
             wait_ring(t);
             done = 0;
 #pragma unroll
-            for (int e = 0; e < C; ++e)
-                if (mm_[e] < nts) {
-                    ring[slot_at(base + HDR + mm_[e]) * 64 + lane] = __builtin_bit_cast(uint2, xn[e]);
-                    ring[slot_at(base + HDR + nts + mm_[e]) * 64 + lane] = __builtin_bit_cast(uint2, yv[e]);
+            for (int e = 0; e < C; ++e) {
+                const int mm = (j - NFIX) * C + e;
+                if (mm < nts) {
+                    ring[slot_at(base + HDR + mm) * 64 + lane] = __builtin_bit_cast(uint2, xn[e]);
+                    ring[slot_at(base + HDR + nts + mm) * 64 + lane] = __builtin_bit_cast(uint2, yv[e]);
                     ++done;
                 }
+            }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (lane == 0) __hip_atomic_fetch_add(&s_done[t], done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
-    ItemOps ia, ib;
-    fetch(p, ia);
+    ItemOps io;
+    fetch(p, io);
     // (as for the solve waves: only the first item's operands are in flight)
     wait_vmem_le<KLDS ? 4 : 4 + 4 + 4>();
-    for (int it = p; it < nitems; it += 2 * kProducers) {
-        fetch(it + kProducers, ib);
-        work(ia);
-        if (it + kProducers >= nitems) break;
-        fetch(it + 2 * kProducers, ia);
-        work(ib);
-    }
+    for (int it = p; it < nitems; it += kProducers) work(io, it + kProducers);
 }
 
 }  // namespace
@@ -1033,16 +1196,32 @@ bool verify_large_supported(const VerifyArgs& a, int io) {
     return io == GDN_BF16 && a.dk == kD && a.dv == kD && a.N > 128 && a.N <= kLargeMaxN;
 }
 
-hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream) {
-    (void)io;
+namespace {
+
+hipError_t launch_large(const VerifyArgs& a, const CommitArgs* c, hipStream_t stream) {
     VerifyArgs copy = a;
+    CommitArgs ccopy{};
+    if (c) ccopy = *c;
     // two 64-column slices per (sequence, value head); a unit's slices are
     // 8 workgroups apart, so both run on one XCD
     int units = a.B * a.Hv;
     const unsigned grid = 16u * (unsigned)((units + 7) / 8);
-    const void* fn = a.N <= 256 ? (const void*)verify_large_kernel<16> : (const void*)verify_large_kernel<32>;
-    void* args[] = {&copy, &units};
+    const void* fn = a.N <= 256 ? (c ? (const void*)verify_large_kernel<16, true> : (const void*)verify_large_kernel<16, false>)
+                                : (c ? (const void*)verify_large_kernel<32, true> : (const void*)verify_large_kernel<32, false>);
+    void* args[] = {&copy, &ccopy, &units};
     return hipLaunchKernel(fn, dim3(grid), dim3(kLargeThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_verify_large(const VerifyArgs& a, int io, hipStream_t stream) {
+    (void)io;
+    return launch_large(a, nullptr, stream);
+}
+
+hipError_t launch_commit_verify_large(const VerifyArgs& a, const CommitArgs& c, int io, hipStream_t stream) {
+    (void)io;
+    return launch_large(a, &c, stream);
 }
 
 }  // namespace gdn
