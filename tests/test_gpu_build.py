@@ -41,6 +41,7 @@ def gpu_build(lp, tk, N, w):
 
 @pytest.mark.parametrize("B,N,K,w", [
     (4, 128, 8, 8),        # the 8-wide, 16-step shape of the 128-node drafts
+    (8, 512, 8, 8),        # 512-node drafts, 64 steps
     (2, 1024, 16, 64),     # the largest tree, wide steps
     (3, 1, 1, 1),
     (2, 33, 3, 5),

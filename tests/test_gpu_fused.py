@@ -225,14 +225,17 @@ def test_fused_large_trees(N):
     run_case(f"large in-place N={N}", steps, "bf16", 2, 4, in_place=True)
 
 
-def test_fused_full_batch_shape():
-    """The benchmark's launch configuration: 64 sequences of 8-ary, 16-deep
-    trees (128 nodes), 16 key / 32 value heads, d = 128, so that the persistent
-    fused launch takes four items per workgroup and every item hand-off (the
-    next item's S rows, k / q rows and previous-tree path read ahead) runs.
-    Three decode steps, every (sequence, value head) unit compared."""
-    rng = np.random.default_rng(97)
-    B, M, depth = 64, 8, 16
+@pytest.mark.parametrize("B,M", [(64, 8), (32, 4)])
+def test_fused_full_batch_shape(B, M):
+    """The benchmark's launch configurations: 64 sequences of 8-ary, 16-deep
+    trees (128 nodes), and 32 sequences of 4-ary ones (64 nodes, each item's
+    value columns split over two workgroups), 16 key / 32 value heads,
+    d = 128, so that the persistent fused launch takes several items per
+    workgroup and every item hand-off (the next item's S rows, k / q rows and
+    previous-tree path read ahead) runs.  Three decode steps, every
+    (sequence, value head) unit compared."""
+    rng = np.random.default_rng(97 + M)
+    depth = 16
     ps = [[W.tree_mary(rng, M, depth) for _ in range(B)] for _ in range(3)]
     accs = [[W.pick_leaf(rng, p) for p in pp] for pp in ps]
     steps = chain_steps(98, ps, accs, 16, 32, 128)

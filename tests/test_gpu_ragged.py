@@ -291,13 +291,15 @@ def test_ragged_fused_decode_loop():
                     [[128, 64, 0, 33, 100], [16, 128, 77, 0, 1], [64, 64, 64, 64, 64]])
 
 
-def test_ragged_fused_full_batch():
+@pytest.mark.parametrize("N,B,lo", [(128, 64, 16), (64, 32, 0)])
+def test_ragged_fused_full_batch(N, B, lo):
     """The same loop in the ragged benchmark's launch configuration: 64
     sequences with trees of 16 .. 128 nodes, 16 key / 32 value heads, so the
-    persistent fused launch takes several items per workgroup."""
-    rng = np.random.default_rng(365)
-    sizes = [[int(x) for x in rng.integers(16, 129, 64)] for _ in range(3)]
-    fused_loop_case(366, 128, 16, 32, 128, sizes)
+    persistent fused launch takes several items per workgroup, largest tree
+    first; and 32 sequences of 0 .. 64 nodes on the split-column form."""
+    rng = np.random.default_rng(365 + N)
+    sizes = [[int(x) for x in rng.integers(lo, N + 1, B)] for _ in range(3)]
+    fused_loop_case(366 + N, N, 16, 32, 128, sizes)
 
 
 def fused_loop_case(seed, N, Hk, Hv, d, sizes):

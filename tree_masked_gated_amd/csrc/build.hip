@@ -10,15 +10,18 @@
 // score(prefix) = 0; a step takes the min(w, nodes left, candidates) best,
 // ordered by score, then parent, then rank, as nodes n, n + 1, ...
 //
-// One wave per sequence.  The sequence's log-probability table is staged in
-// LDS once.  A candidate is one 64-bit key whose unsigned order is the
-// selection order (order-preserving score bits, then 0xffff - (p + 1), then
-// 0xffff - c); keys are distinct, so no tie needs a rule of its own.  The
-// open candidates are one list sorted in descending key order.  A step's new
-// children are bitonic-sorted and merged into the list by rank (each key's
-// place is its index in its own list plus the number of larger keys in the
-// other, a binary search), and the list is cut to the nodes still to place:
-// a candidate with that many better ones can never be chosen.
+// One workgroup of eight waves per sequence: a step's work is spread over
+// all its threads, so a step costs about one binary search per thread.  The
+// sequence's log-probability table is staged in LDS once.  A candidate is one
+// 64-bit key whose unsigned order is the selection order (order-preserving
+// score bits, then 0xffff - (p + 1), then 0xffff - c); keys are distinct, so
+// no tie needs a rule of its own.  The open candidates are one list sorted in
+// descending key order.  A step's new children are sorted by rank (a key's
+// place is the number of larger keys) and merged into the list by rank (a
+// key's place is its index in its own list plus the number of larger keys in
+// the other, a binary search, one key per thread), and the list is cut to
+// the nodes still to place: a candidate with that many better ones can never
+// be chosen.
 #include "gdn_common.hpp"
 #include "launch.hpp"
 
@@ -26,7 +29,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int kBuildThreads = 64;
+constexpr int kBuildThreads = 512;
 
 // order-preserving 32-bit image of a finite (or infinite) float; -0 counts as +0
 __device__ __forceinline__ uint32_t score_bits(float s) {
@@ -56,116 +59,107 @@ __device__ __forceinline__ int count_larger(const uint64_t* x, int n, uint64_t k
 }
 
 struct BuildLds {
-    int N, K, P;              // nodes, continuations per row, child keys per step (power of 2)
+    int N, K, P;              // nodes, continuations per row, child keys per step
     __host__ __device__ BuildLds(int n, int k, int p) : N(n), K(k), P(p) {}
-    // byte offsets: two lists of N keys, P child keys, then the table and per-node words
+    // byte offsets: two lists of N keys, P child keys twice (as formed, then
+    // sorted), then the table and per-node words
     __host__ __device__ size_t list(int i) const { return (size_t)i * N * 8; }
-    __host__ __device__ size_t child() const { return list(2); }
-    __host__ __device__ size_t table() const { return child() + (size_t)P * 8; }
+    __host__ __device__ size_t child(int i) const { return list(2) + (size_t)i * P * 8; }
+    __host__ __device__ size_t table() const { return child(2); }
     __host__ __device__ size_t score() const { return table() + (size_t)(N + 1) * K * 4; }
     __host__ __device__ size_t parent() const { return score() + (size_t)N * 4; }
     __host__ __device__ size_t rank() const { return parent() + (size_t)N * 4; }
     __host__ __device__ size_t bytes() const { return rank() + (size_t)N * 4; }
 };
 
-__host__ __device__ inline int pow2_at_least(int x) {
-    int p = 1;
-    while (p < x) p <<= 1;
-    return p;
-}
-
 __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int N = a.N, K = a.K, w = a.w;
     const int wn = w < N ? w : N;
-    const BuildLds L(N, K, pow2_at_least(wn * K));
-    uint64_t* lists[2] = {reinterpret_cast<uint64_t*>(smem + L.list(0)),
-                          reinterpret_cast<uint64_t*>(smem + L.list(1))};
-    uint64_t* ck = reinterpret_cast<uint64_t*>(smem + L.child());
+    const BuildLds L(N, K, wn * K);
+    // (the lists are addressed from one LDS base: a pointer picked from an
+    // array would lose its address space and turn every access into a flat one)
+    uint64_t* lists = reinterpret_cast<uint64_t*>(smem + L.list(0));    // [2][N]
+    uint64_t* cu = reinterpret_cast<uint64_t*>(smem + L.child(0));    // this step's children
+    uint64_t* ck = reinterpret_cast<uint64_t*>(smem + L.child(1));    // the same, sorted
     float* lp = reinterpret_cast<float*>(smem + L.table());
     float* sc = reinterpret_cast<float*>(smem + L.score());
     int32_t* par = reinterpret_cast<int32_t*>(smem + L.parent());
     int32_t* rk = reinterpret_cast<int32_t*>(smem + L.rank());
-    const int b = blockIdx.x, lane = threadIdx.x;
+    const int b = blockIdx.x, tid = threadIdx.x;
     const size_t rows = (size_t)(N + 1) * K;
 
     const float* g_lp = a.logp + (size_t)b * rows;
-    for (size_t x = lane; x < rows; x += kBuildThreads) lp[x] = g_lp[x];
-    for (int i = lane; i < N; i += kBuildThreads) {
+    for (size_t x = tid; x < rows; x += kBuildThreads) lp[x] = g_lp[x];
+    for (int i = tid; i < N; i += kBuildThreads) {
         par[i] = -1;
         rk[i] = 0;
         sc[i] = 0.0f;
     }
     __syncthreads();
 
-    int cur = 0, head = 0, len = 0;        // open candidates: lists[cur][head .. len)
+    int cur = 0, head = 0, len = 0;        // open candidates: lists[cur N + head .. cur N + len)
     int n = 0, e0 = -1, ne = 1;            // the nodes to expand: e0 .. e0 + ne - 1 (-1: the prefix)
     for (;;) {
-        // 1. the expanded nodes' children, as keys, sorted descending
-        const int nc = ne * K, P = pow2_at_least(nc);
+        // 1. the expanded nodes' children, as keys, sorted descending: each
+        // key's place is the number of larger ones.  Up to 64 children: one
+        // wave, key x in lane x, every other lane's key taken by a lane read
+        // into scalar registers (no LDS round trip); more: a scan of the keys
+        // in LDS, every lane of a wave reading the same key at once.
+        const int nc = ne * K;
         auto child_key = [&](int x) {
-            uint64_t key = 0;              // padding: below every candidate
-            if (x < nc) {
-                const int t = x / K, c = x - t * K;
-                const int p = e0 < 0 ? -1 : e0 + t;
-                const float base = p < 0 ? 0.0f : sc[p];
-                key = cand_key(base + lp[(size_t)(p + 1) * K + c], p, c);
-            }
-            return key;
+            const int t = x / K, c = x - t * K;
+            const int p = e0 < 0 ? -1 : e0 + t;
+            const float base = p < 0 ? 0.0f : sc[p];
+            return cand_key(base + lp[(size_t)(p + 1) * K + c], p, c);
         };
-        if (P <= kBuildThreads) {
-            // one key per lane, the same bitonic network in registers: the
-            // pair (i, i ^ j) keeps its larger key at i when block i & k
-            // runs descending, its smaller key otherwise
-            uint64_t key = child_key(lane);
-            for (int k = 2; k <= P; k <<= 1)
-                for (int j = k >> 1; j > 0; j >>= 1) {
-                    const uint32_t lo = __shfl_xor((unsigned int)key, j);
-                    const uint32_t hi = __shfl_xor((unsigned int)(key >> 32), j);
-                    const uint64_t other = ((uint64_t)hi << 32) | lo;
-                    const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
-                    key = keep_max ? (key > other ? key : other) : (key < other ? key : other);
+        if (nc <= 64) {
+            if (tid < 64) {
+                const uint64_t key = tid < nc ? child_key(tid) : 0;
+                const uint32_t klo = (uint32_t)key, khi = (uint32_t)(key >> 32);
+                int r = 0;
+#pragma unroll
+                for (int y = 0; y < 64; ++y) {
+                    const uint64_t ky = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, y) << 32) |
+                                        (uint32_t)__builtin_amdgcn_readlane((int)klo, y);
+                    r += ky > key ? 1 : 0;     // (lanes past nc hold 0: never larger)
                 }
-            if (lane < P) ck[lane] = key;
-            __syncthreads();
+                if (tid < nc) ck[r] = key;
+            }
         } else {
-            for (int x = lane; x < P; x += kBuildThreads) ck[x] = child_key(x);
+            for (int x = tid; x < nc; x += kBuildThreads) cu[x] = child_key(x);
             __syncthreads();
-            for (int k = 2; k <= P; k <<= 1)
-                for (int j = k >> 1; j > 0; j >>= 1) {
-                    for (int i = lane; i < P; i += kBuildThreads) {
-                        const int ij = i ^ j;
-                        if (ij > i) {
-                            const uint64_t x = ck[i], y = ck[ij];
-                            const bool desc = (i & k) == 0;
-                            if (desc ? x < y : x > y) {
-                                ck[i] = y;
-                                ck[ij] = x;
-                            }
-                        }
-                    }
-                    __syncthreads();
-                }
+            for (int x = tid; x < nc; x += kBuildThreads) {
+                const uint64_t key = cu[x];
+                int r = 0;
+#pragma unroll 8
+                for (int y = 0; y < nc; ++y) r += cu[y] > key ? 1 : 0;
+                ck[r] = key;
+            }
         }
-        // 2. merge into the open list, keeping the best N - n; 3. the step:
-        // the best m open candidates become nodes n .. n + m - 1, recorded by
+        __syncthreads();
+        // 2. merge into the open list, keeping the best N - n (a key's place:
+        // its index in its own list plus the number of larger keys in the
+        // other, a binary search; one key per thread); 3. the step: the best
+        // m open candidates become nodes n .. n + m - 1, recorded by
         // whichever thread places them
         const int R = N - n;
-        const uint64_t* A = lists[cur] + head;
+        const uint64_t* A = lists + (size_t)cur * N + head;
         const int na = len - head;
-        uint64_t* out = lists[cur ^ 1];
+        uint64_t* out = lists + (size_t)(cur ^ 1) * N;
         len = min(na + nc, R);
         const int m = min(min(w, R), len);
-        auto place = [&](int pos, uint64_t key) {
+        for (int x = tid; x < na + nc; x += kBuildThreads) {
+            const bool open = x < na;
+            const uint64_t key = open ? A[x] : ck[x - na];
+            const int pos = open ? x + count_larger(ck, nc, key) : x - na + count_larger(A, na, key);
             if (pos < R) out[pos] = key;
             if (pos < m) {
                 sc[n + pos] = bits_score((uint32_t)(key >> 32));
                 par[n + pos] = key_parent(key);
                 rk[n + pos] = key_rank(key);
             }
-        };
-        for (int x = lane; x < na; x += kBuildThreads) place(x + count_larger(ck, nc, A[x]), A[x]);
-        for (int x = lane; x < nc; x += kBuildThreads) place(x + count_larger(A, na, ck[x]), ck[x]);
+        }
         cur ^= 1;
         head = 0;
         __syncthreads();
@@ -178,7 +172,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
     }
     // the tree, with each node's token from its parent's row
     const int32_t* g_tok = a.tok + (size_t)b * rows;
-    for (int i = lane; i < N; i += kBuildThreads) {
+    for (int i = tid; i < N; i += kBuildThreads) {
         const int p = par[i];
         a.parent[(size_t)b * N + i] = p;
         a.token[(size_t)b * N + i] = g_tok[(size_t)(p + 1) * K + rk[i]];
@@ -190,7 +184,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
 
 size_t tree_build_lds_bytes(int N, int K, int w) {
     const int wn = w < N ? w : N;
-    return BuildLds(N, K, pow2_at_least(wn * K)).bytes();
+    return BuildLds(N, K, wn * K).bytes();
 }
 
 hipError_t launch_tree_build(const BuildArgs& a, hipStream_t stream) {
