@@ -58,6 +58,22 @@ __device__ __forceinline__ int count_larger(const uint64_t* x, int n, uint64_t k
     return lo;
 }
 
+// Number of lanes y < CNT of the calling wave whose key is larger than this
+// lane's (every other lane's key read into scalar registers; no LDS).  Lanes
+// without a key hold 0, which is below every key.
+template <int CNT>
+__device__ __forceinline__ int lanes_larger(uint64_t key) {
+    const uint32_t klo = (uint32_t)key, khi = (uint32_t)(key >> 32);
+    int r = 0;
+#pragma unroll
+    for (int y = 0; y < CNT; ++y) {
+        const uint64_t ky = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, y) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)klo, y);
+        r += ky > key ? 1 : 0;
+    }
+    return r;
+}
+
 struct BuildLds {
     int N, K, P;              // nodes, continuations per row, child keys per step
     __host__ __device__ BuildLds(int n, int k, int p) : N(n), K(k), P(p) {}
@@ -69,7 +85,8 @@ struct BuildLds {
     __host__ __device__ size_t score() const { return table() + (size_t)(N + 1) * K * 4; }
     __host__ __device__ size_t parent() const { return score() + (size_t)N * 4; }
     __host__ __device__ size_t rank() const { return parent() + (size_t)N * 4; }
-    __host__ __device__ size_t bytes() const { return rank() + (size_t)N * 4; }
+    __host__ __device__ size_t top() const { return rank() + (size_t)N * 4; }   // 32 keys (8-byte aligned)
+    __host__ __device__ size_t bytes() const { return top() + 32 * 8; }
 };
 
 __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) {
@@ -100,75 +117,150 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
 
     int cur = 0, head = 0, len = 0;        // open candidates: lists[cur N + head .. cur N + len)
     int n = 0, e0 = -1, ne = 1;            // the nodes to expand: e0 .. e0 + ne - 1 (-1: the prefix)
-    for (;;) {
-        // 1. the expanded nodes' children, as keys, sorted descending: each
-        // key's place is the number of larger ones.  Up to 64 children: one
-        // wave, key x in lane x, every other lane's key taken by a lane read
-        // into scalar registers (no LDS round trip); more: a scan of the keys
-        // in LDS, every lane of a wave reading the same key at once.
-        const int nc = ne * K;
-        auto child_key = [&](int x) {
-            const int t = x / K, c = x - t * K;
-            const int p = e0 < 0 ? -1 : e0 + t;
-            const float base = p < 0 ? 0.0f : sc[p];
-            return cand_key(base + lp[(size_t)(p + 1) * K + c], p, c);
-        };
-        if (nc <= 64) {
+    if (L.P <= 64 && wn <= 32) {
+        // Steps of up to 64 children, pipelined: once a step's children are
+        // sorted, its new nodes are the best m of the heads of the two sorted
+        // lists (the first m open candidates and the first m children), so
+        // wave 0 finds them and sorts the next step's children while the
+        // other waves merge the whole lists.  One barrier per step.
+        uint64_t* cks = reinterpret_cast<uint64_t*>(smem + L.child(0));   // [2][P] sorted children
+        uint64_t* top = reinterpret_cast<uint64_t*>(smem + L.top());       // a step's new nodes
+        int cb = 0;                        // this step's children: cks[cb P ..]
+        if (tid < 64) {                    // the prefix's children
+            const uint64_t key = tid < K ? cand_key(0.0f + lp[tid], -1, tid) : 0;
+            const int r = lanes_larger<64>(key);
+            if (tid < K) cks[r] = key;
+        }
+        __syncthreads();
+        for (;;) {
+            const int nc = ne * K;
+            const uint64_t* ck = cks + (size_t)cb * L.P;
+            const int R = N - n;
+            const uint64_t* A = lists + (size_t)cur * N + head;
+            const int na = len - head;
+            uint64_t* out = lists + (size_t)(cur ^ 1) * N;
+            len = min(na + nc, R);
+            const int m = min(min(w, R), len);
             if (tid < 64) {
-                const uint64_t key = tid < nc ? child_key(tid) : 0;
-                const uint32_t klo = (uint32_t)key, khi = (uint32_t)(key >> 32);
-                int r = 0;
-#pragma unroll
-                for (int y = 0; y < 64; ++y) {
-                    const uint64_t ky = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, y) << 32) |
-                                        (uint32_t)__builtin_amdgcn_readlane((int)klo, y);
-                    r += ky > key ? 1 : 0;     // (lanes past nc hold 0: never larger)
+                if (n + m < N) {
+                    // this step's new nodes: lanes 0 .. m-1 hold the first m
+                    // open candidates, lanes m .. 2m-1 the first m children
+                    // (0 past either list: below every key)
+                    uint64_t key = 0;
+                    if (tid < m) key = tid < na ? A[tid] : 0;
+                    else if (tid < 2 * m) key = tid - m < nc ? ck[tid - m] : 0;
+                    const int r = 2 * m <= 16 ? lanes_larger<16>(key)
+                                  : 2 * m <= 32 ? lanes_larger<32>(key) : lanes_larger<64>(key);
+                    if (key != 0 && r < m) top[r] = key;
+                    // their children, the next step's, sorted into the other buffer
+                    const int nc2 = m * K;
+                    uint64_t k2 = 0;
+                    if (tid < nc2) {
+                        const int t = tid / K, c = tid - t * K;
+                        const uint64_t kt = top[t];
+                        const int pn = n + t;
+                        k2 = cand_key(bits_score((uint32_t)(kt >> 32)) + lp[(size_t)(pn + 1) * K + c], pn, c);
+                    }
+                    const int r2 = lanes_larger<64>(k2);
+                    if (tid < nc2) cks[(size_t)(cb ^ 1) * L.P + r2] = k2;
                 }
-                if (tid < nc) ck[r] = key;
+            } else {
+                // the merge by rank (a key's place: its index in its own list
+                // plus the number of larger keys in the other, a binary
+                // search), keeping the best N - n; the thread placing one of
+                // the best m records it as node n + pos
+                for (int x = tid - 64; x < na + nc; x += kBuildThreads - 64) {
+                    const bool open = x < na;
+                    const uint64_t key = open ? A[x] : ck[x - na];
+                    const int pos = open ? x + count_larger(ck, nc, key) : x - na + count_larger(A, na, key);
+                    if (pos < R) out[pos] = key;
+                    if (pos < m) {
+                        sc[n + pos] = bits_score((uint32_t)(key >> 32));
+                        par[n + pos] = key_parent(key);
+                        rk[n + pos] = key_rank(key);
+                    }
+                }
             }
-        } else {
-            for (int x = tid; x < nc; x += kBuildThreads) cu[x] = child_key(x);
             __syncthreads();
-            for (int x = tid; x < nc; x += kBuildThreads) {
-                const uint64_t key = cu[x];
-                int r = 0;
-#pragma unroll 8
-                for (int y = 0; y < nc; ++y) r += cu[y] > key ? 1 : 0;
-                ck[r] = key;
-            }
+            if (m == 0 || n + m >= N) break;   // (m = 0 never: every step adds K >= 1 candidates)
+            cur ^= 1;
+            cb ^= 1;
+            e0 = n;
+            ne = m;
+            head = m;
+            n += m;
         }
-        __syncthreads();
-        // 2. merge into the open list, keeping the best N - n (a key's place:
-        // its index in its own list plus the number of larger keys in the
-        // other, a binary search; one key per thread); 3. the step: the best
-        // m open candidates become nodes n .. n + m - 1, recorded by
-        // whichever thread places them
-        const int R = N - n;
-        const uint64_t* A = lists + (size_t)cur * N + head;
-        const int na = len - head;
-        uint64_t* out = lists + (size_t)(cur ^ 1) * N;
-        len = min(na + nc, R);
-        const int m = min(min(w, R), len);
-        for (int x = tid; x < na + nc; x += kBuildThreads) {
-            const bool open = x < na;
-            const uint64_t key = open ? A[x] : ck[x - na];
-            const int pos = open ? x + count_larger(ck, nc, key) : x - na + count_larger(A, na, key);
-            if (pos < R) out[pos] = key;
-            if (pos < m) {
-                sc[n + pos] = bits_score((uint32_t)(key >> 32));
-                par[n + pos] = key_parent(key);
-                rk[n + pos] = key_rank(key);
+    } else {
+        for (;;) {
+            // 1. the expanded nodes' children, as keys, sorted descending: each
+            // key's place is the number of larger ones.  Up to 64 children: one
+            // wave, key x in lane x, every other lane's key taken by a lane read
+            // into scalar registers (no LDS round trip); more: a scan of the keys
+            // in LDS, every lane of a wave reading the same key at once.
+            const int nc = ne * K;
+            auto child_key = [&](int x) {
+                const int t = x / K, c = x - t * K;
+                const int p = e0 < 0 ? -1 : e0 + t;
+                const float base = p < 0 ? 0.0f : sc[p];
+                return cand_key(base + lp[(size_t)(p + 1) * K + c], p, c);
+            };
+            if (nc <= 64) {
+                if (tid < 64) {
+                    const uint64_t key = tid < nc ? child_key(tid) : 0;
+                    const uint32_t klo = (uint32_t)key, khi = (uint32_t)(key >> 32);
+                    int r = 0;
+    #pragma unroll
+                    for (int y = 0; y < 64; ++y) {
+                        const uint64_t ky = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, y) << 32) |
+                                            (uint32_t)__builtin_amdgcn_readlane((int)klo, y);
+                        r += ky > key ? 1 : 0;     // (lanes past nc hold 0: never larger)
+                    }
+                    if (tid < nc) ck[r] = key;
+                }
+            } else {
+                for (int x = tid; x < nc; x += kBuildThreads) cu[x] = child_key(x);
+                __syncthreads();
+                for (int x = tid; x < nc; x += kBuildThreads) {
+                    const uint64_t key = cu[x];
+                    int r = 0;
+    #pragma unroll 8
+                    for (int y = 0; y < nc; ++y) r += cu[y] > key ? 1 : 0;
+                    ck[r] = key;
+                }
             }
+            __syncthreads();
+            // 2. merge into the open list, keeping the best N - n (a key's place:
+            // its index in its own list plus the number of larger keys in the
+            // other, a binary search; one key per thread); 3. the step: the best
+            // m open candidates become nodes n .. n + m - 1, recorded by
+            // whichever thread places them
+            const int R = N - n;
+            const uint64_t* A = lists + (size_t)cur * N + head;
+            const int na = len - head;
+            uint64_t* out = lists + (size_t)(cur ^ 1) * N;
+            len = min(na + nc, R);
+            const int m = min(min(w, R), len);
+            for (int x = tid; x < na + nc; x += kBuildThreads) {
+                const bool open = x < na;
+                const uint64_t key = open ? A[x] : ck[x - na];
+                const int pos = open ? x + count_larger(ck, nc, key) : x - na + count_larger(A, na, key);
+                if (pos < R) out[pos] = key;
+                if (pos < m) {
+                    sc[n + pos] = bits_score((uint32_t)(key >> 32));
+                    par[n + pos] = key_parent(key);
+                    rk[n + pos] = key_rank(key);
+                }
+            }
+            cur ^= 1;
+            head = 0;
+            __syncthreads();
+            if (m == 0) break;                 // (never: every step adds K >= 1 candidates)
+            e0 = n;
+            ne = m;
+            head = m;
+            n += m;
+            if (n >= N) break;
         }
-        cur ^= 1;
-        head = 0;
-        __syncthreads();
-        if (m == 0) break;                 // (never: every step adds K >= 1 candidates)
-        e0 = n;
-        ne = m;
-        head = m;
-        n += m;
-        if (n >= N) break;
     }
     // the tree, with each node's token from its parent's row
     const int32_t* g_tok = a.tok + (size_t)b * rows;
