@@ -58,15 +58,15 @@ __device__ __forceinline__ int count_larger(const uint64_t* x, int n, uint64_t k
     return lo;
 }
 
-// Number of lanes y < CNT of the calling wave whose key is larger than this
-// lane's (every other lane's key read into scalar registers; no LDS).  Lanes
-// without a key hold 0, which is below every key.
-template <int CNT>
+// Number of lanes Y0 <= y < Y0 + CNT of the calling wave whose key is
+// larger than this lane's (every other lane's key read into scalar
+// registers; no LDS).  Lanes without a key hold 0, below every key.
+template <int CNT, int Y0 = 0>
 __device__ __forceinline__ int lanes_larger(uint64_t key) {
     const uint32_t klo = (uint32_t)key, khi = (uint32_t)(key >> 32);
     int r = 0;
 #pragma unroll
-    for (int y = 0; y < CNT; ++y) {
+    for (int y = Y0; y < Y0 + CNT; ++y) {
         const uint64_t ky = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, y) << 32) |
                             (uint32_t)__builtin_amdgcn_readlane((int)klo, y);
         r += ky > key ? 1 : 0;
@@ -85,8 +85,10 @@ struct BuildLds {
     __host__ __device__ size_t score() const { return table() + (size_t)(N + 1) * K * 4; }
     __host__ __device__ size_t parent() const { return score() + (size_t)N * 4; }
     __host__ __device__ size_t rank() const { return parent() + (size_t)N * 4; }
-    __host__ __device__ size_t top() const { return rank() + (size_t)N * 4; }   // 32 keys (8-byte aligned)
-    __host__ __device__ size_t bytes() const { return top() + 32 * 8; }
+    // a step's new nodes (two copies of 32 keys), then 64 partial ranks and a flag
+    __host__ __device__ size_t top() const { return rank() + (size_t)N * 4; }
+    __host__ __device__ size_t part() const { return top() + 2 * 32 * 8; }
+    __host__ __device__ size_t bytes() const { return part() + 65 * 4; }
 };
 
 __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) {
@@ -124,8 +126,11 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
         // wave 0 finds them and sorts the next step's children while the
         // other waves merge the whole lists.  One barrier per step.
         uint64_t* cks = reinterpret_cast<uint64_t*>(smem + L.child(0));   // [2][P] sorted children
-        uint64_t* top = reinterpret_cast<uint64_t*>(smem + L.top());       // a step's new nodes
+        uint64_t* top = reinterpret_cast<uint64_t*>(smem + L.top());       // [2][32] a step's new nodes
+        int* part = reinterpret_cast<int*>(smem + L.part());               // [64] counts, [64] flag
         int cb = 0;                        // this step's children: cks[cb P ..]
+        int nstep = 0;                     // this step's number, from 1 (the flag's value)
+        if (tid == 0) part[64] = 0;
         if (tid < 64) {                    // the prefix's children
             const uint64_t key = tid < K ? cand_key(0.0f + lp[tid], -1, tid) : 0;
             const int r = lanes_larger<64>(key);
@@ -133,6 +138,7 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
         }
         __syncthreads();
         for (;;) {
+            ++nstep;
             const int nc = ne * K;
             const uint64_t* ck = cks + (size_t)cb * L.P;
             const int R = N - n;
@@ -141,35 +147,48 @@ __global__ __launch_bounds__(kBuildThreads) void tree_build_kernel(BuildArgs a) 
             uint64_t* out = lists + (size_t)(cur ^ 1) * N;
             len = min(na + nc, R);
             const int m = min(min(w, R), len);
-            if (tid < 64) {
+            if (tid < 128) {
+                // waves 0 and 1 both: this step's new nodes, lanes 0 .. m-1
+                // holding the first m open candidates and lanes m .. 2m-1 the
+                // first m children (0 past either list: below every key);
+                // then their children, the next step's, ranked by wave 0 over
+                // lanes 0 .. 31 and wave 1 over lanes 32 .. 63, wave 1's
+                // counts handed over through LDS under a step-numbered flag
                 if (n + m < N) {
-                    // this step's new nodes: lanes 0 .. m-1 hold the first m
-                    // open candidates, lanes m .. 2m-1 the first m children
-                    // (0 past either list: below every key)
+                    const int ln = tid & 63, wv = tid >> 6;
                     uint64_t key = 0;
-                    if (tid < m) key = tid < na ? A[tid] : 0;
-                    else if (tid < 2 * m) key = tid - m < nc ? ck[tid - m] : 0;
+                    if (ln < m) key = ln < na ? A[ln] : 0;
+                    else if (ln < 2 * m) key = ln - m < nc ? ck[ln - m] : 0;
                     const int r = 2 * m <= 16 ? lanes_larger<16>(key)
                                   : 2 * m <= 32 ? lanes_larger<32>(key) : lanes_larger<64>(key);
-                    if (key != 0 && r < m) top[r] = key;
-                    // their children, the next step's, sorted into the other buffer
+                    uint64_t* topw = top + 32 * wv;
+                    if (key != 0 && r < m) topw[r] = key;
                     const int nc2 = m * K;
                     uint64_t k2 = 0;
-                    if (tid < nc2) {
-                        const int t = tid / K, c = tid - t * K;
-                        const uint64_t kt = top[t];
+                    if (ln < nc2) {
+                        const int t = ln / K, c = ln - t * K;
+                        const uint64_t kt = topw[t];
                         const int pn = n + t;
                         k2 = cand_key(bits_score((uint32_t)(kt >> 32)) + lp[(size_t)(pn + 1) * K + c], pn, c);
                     }
-                    const int r2 = lanes_larger<64>(k2);
-                    if (tid < nc2) cks[(size_t)(cb ^ 1) * L.P + r2] = k2;
+                    if (wv == 1) {
+                        part[ln] = lanes_larger<32, 32>(k2);
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        if (ln == 0) __hip_atomic_store(&part[64], nstep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    } else {
+                        const int r0 = lanes_larger<32>(k2);
+                        while (__hip_atomic_load(&part[64], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != nstep)
+                            __builtin_amdgcn_s_sleep(1);
+                        asm volatile("" ::: "memory");
+                        if (ln < nc2) cks[(size_t)(cb ^ 1) * L.P + r0 + part[ln]] = k2;
+                    }
                 }
             } else {
                 // the merge by rank (a key's place: its index in its own list
                 // plus the number of larger keys in the other, a binary
                 // search), keeping the best N - n; the thread placing one of
                 // the best m records it as node n + pos
-                for (int x = tid - 64; x < na + nc; x += kBuildThreads - 64) {
+                for (int x = tid - 128; x < na + nc; x += kBuildThreads - 128) {
                     const bool open = x < na;
                     const uint64_t key = open ? A[x] : ck[x - na];
                     const int pos = open ? x + count_larger(ck, nc, key) : x - na + count_larger(A, na, key);
