@@ -21,7 +21,9 @@
 // key's place is its index in its own list plus the number of larger keys in
 // the other, a binary search, one key per thread), and the list is cut to
 // the nodes still to place: a candidate with that many better ones can never
-// be chosen.
+// be chosen.  Steps of up to 64 children overlap: the step's new nodes are
+// the best of the two lists' heads, so two waves rank the next step's
+// children while the others merge (one barrier per step).
 #include "gdn_common.hpp"
 #include "launch.hpp"
 
