@@ -30,21 +30,18 @@ __device__ __forceinline__ float bf16_val(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);
 }
 
-// 4 fp32 accumulator values -> bf16 hi part and bf16 lo part (x - hi).
-__device__ __forceinline__ void split4(f32x4 x, s16x4& hi, s16x4& lo) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        uint16_t h = bf16_rne(x[m]);
-        hi[m] = (short)h;
-        lo[m] = (short)bf16_rne(x[m] - bf16_val(h));
-    }
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 4 fp32 -> bf16 (RNE), two values per conversion instruction.
+__device__ __forceinline__ s16x4 to_bf16x4(f32x4 x) {
+    return __builtin_bit_cast(s16x4, __builtin_convertvector(x, bf16x4));
 }
 
-__device__ __forceinline__ s16x4 to_bf16x4(f32x4 x) {
-    s16x4 r;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) r[m] = (short)bf16_rne(x[m]);
-    return r;
+// 4 fp32 accumulator values -> bf16 hi part and bf16 lo part (x - hi).
+__device__ __forceinline__ void split4(f32x4 x, s16x4& hi, s16x4& lo) {
+    const bf16x4 h = __builtin_convertvector(x, bf16x4);
+    hi = __builtin_bit_cast(s16x4, h);
+    lo = to_bf16x4(x - __builtin_convertvector(h, f32x4));
 }
 
 // 8 fp32 -> bf16x8 (RNE).

@@ -53,8 +53,10 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* m, int blk, int cs, i
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-// Persistent workgroups, one per CU, each looping over (sequence, key head,
-// head group) work items with the next item's inputs in flight:
+// Persistent workgroups, one per CU (two per CU for one-head workgroups on
+// trees of up to 64 nodes, whose register budget is capped at 256 per lane for
+// that), each looping over (sequence, key head, head group) work items with the
+// next item's inputs in flight:
 //  - at the start of item n's solve (before its output stores, since loads
 //    and stores retire in order): item n+1's parent / g / beta words and S0
 //    rows into registers;
@@ -75,7 +77,7 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // Loads never leave a tree's rows: rows past n re-read row n - 1, and an empty
 // tree's loads read the first line of S0 instead.
 template <int NB, int HPW, bool FUSED, bool RAGGED>
-__global__ __launch_bounds__(256 * HPW, 1) void verify_tiled_kernel(VerifyArgs a, CommitArgs c, int nitems) {
+__global__ __launch_bounds__(256 * HPW, HPW == 1 && NB == 4 ? 2 : 1) void verify_tiled_kernel(VerifyArgs a, CommitArgs c, int nitems) {
     constexpr int WPH = 4;                      // waves per value head
     constexpr int CG = 2;                       // 16-column groups per wave
     constexpr int NW = WPH * HPW;               // waves
@@ -889,18 +891,24 @@ static const void* tiled_kernel(int N, int hpw) {
 template <bool FUSED>
 static hipError_t launch_tiled(const VerifyArgs& a, const CommitArgs& c, hipStream_t stream) {
     const int G = a.Hv / a.Hk;
-    const int hpw = (G % 2 == 0) ? 2 : 1;
-    // ragged: the new tree's offsets, and (fused) the previous tree's as well
-    const bool ragged = a.offsets != nullptr;
-    if (FUSED && ragged != (c.offsets != nullptr)) return hipErrorInvalidValue;
-    const void* fn = ragged ? tiled_kernel<FUSED, true>(a.N, hpw) : tiled_kernel<FUSED, false>(a.N, hpw);
-    int nitems = a.B * a.Hk * (G / hpw);
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)(nitems < cus ? nitems : cus);
+    // Two value heads per workgroup where G allows it, except for trees of up
+    // to 64 nodes when that would leave compute units idle: there one head per
+    // workgroup, two workgroups per compute unit (49 KB of LDS and at most 256
+    // registers per lane each), spreads a small batch over twice the units.
+    const bool small = a.N <= 64 && a.B * a.Hk * (G / 2) < cus;
+    const int hpw = (G % 2 == 0 && !small) ? 2 : 1;
+    // ragged: the new tree's offsets, and (fused) the previous tree's as well
+    const bool ragged = a.offsets != nullptr;
+    if (FUSED && ragged != (c.offsets != nullptr)) return hipErrorInvalidValue;
+    const void* fn = ragged ? tiled_kernel<FUSED, true>(a.N, hpw) : tiled_kernel<FUSED, false>(a.N, hpw);
+    int nitems = a.B * a.Hk * (G / hpw);
+    const int slots = (a.N <= 64 && hpw == 1) ? 2 * cus : cus;
+    const unsigned grid = (unsigned)(nitems < slots ? nitems : slots);
     VerifyArgs va = a;
     CommitArgs ca = c;
     void* args[] = {&va, &ca, &nitems};
