@@ -777,6 +777,311 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     u32x4* ring16 = reinterpret_cast<u32x4*>(s_big);    // slots x, x + 1 (x even): ring16[32 x + lane]
     auto slot_at = [&](int x) __attribute__((always_inline)) { return x < RING ? x : x - RING; };
 
+    // The diagonal block's D_t = (I + X_tt)^-1 and Y_tt from its Grams gK (lane
+    // (j, q), element m: k_(4q+m) . k_j) and gQ (lane (i, q): k_(4q+m) . q_i),
+    // with producer pr's LDS scratch: D_t in fp32, lane 4c + qd holding rows
+    // 4qd .. +3 of column c; Y_tt (lane (i, q), element m: j = 4q + m, an
+    // ancestor of i or i) as bf16.
+    auto diag_block = [&](int t, int pr, f32x4 gK, f32x4 gQ, float (&accd)[4], s16x4& yb)
+                          __attribute__((always_inline)) {
+        const int pi = 16 * t + ln;
+        const float lgi = s_lg[pi];
+        // X_tt[i][j] at lane (j, q), element m: i = 4q + m
+        float xv[4];
+        {
+            const int pj = 16 * t + ln;
+            const int lj = s_last[pj];
+            const float lgj = s_lg[pj];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int pi2 = 16 * t + 4 * lq + m;
+                const bool anc = (pj < pi2) & (pi2 <= lj);
+                const float x = s_beta[pi2] * __expf(fminf(s_lg[pi2] - lgj, 0.f)) * gK[m];
+                xv[m] = anc ? x : 0.f;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int pj = 16 * t + 4 * lq + m;
+            const bool anc = (pj <= pi) & (pi <= (int)s_last[pj]);
+            const float y = __expf(fminf(lgi - s_lg[pj], 0.f)) * gQ[m];
+            yb[m] = (short)bf16_rne(anc ? y : 0.f);
+        }
+        // fp32 forward substitution, four lanes per column: lane 4c + qd
+        // holds rows 4qd .. 4qd+3 of column c; step m reads column m of
+        // X_tt (stored [col][row] by the lanes that hold it) and takes y_m
+        // from its owner within the lane quad
+        float* xd = &s_xd[pr][0];
+        *reinterpret_cast<float4*>(&xd[ln * 16 + 4 * lq]) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+        const int c = lane >> 2, qd = lane & 3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accd[e] = (4 * qd + e == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 15; ++m) {
+            const float4 xc = *reinterpret_cast<const float4*>(&xd[m * 16 + 4 * qd]);
+            const float ym = quad_bcast(accd[m & 3], m >> 2);
+            const float xr[4] = {xc.x, xc.y, xc.z, xc.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {               // rows below m only
+                const float upd = fmaf(-xr[e], ym, accd[e]);
+                accd[e] = 4 * qd + e > m ? upd : accd[e];
+            }
+        }
+    };
+
+    // ================= chains =================
+    // A chain (node i's parent is i - 1) is the gated delta rule's linear
+    // recurrence, and the chunked form of it applies (page "Trees from
+    // Marginals", section 3: the chunked linear recurrence): all nodes of
+    // block row t descend from node 16 t - 1, so every ancestor outside the
+    // row is folded into that node's state S_t, and no off-diagonal tile is
+    // formed.  With E_t = G_(16t-1) (E_0 = 0, S_0 = S0):
+    //   R_t = diag(beta)(V_t - diag(e^(G - E_t)) K_t S_t^T),  U_t = D_t R_t,
+    //   O_t = diag(e^(G - E_t)) Q_t S_t^T + Y_tt U_t,
+    //   S_(t+1) = e^(E_(t+1) - E_t) S_t + sum_(j in row t) e^(E_(t+1) - G_j) u_j k_j^T.
+    // The producers form D_t and Y_tt and stage each row's operands in a
+    // four-row LDS ring (q, v, k when it is not in LDS, K_t^T node-packed,
+    // and per-node factors), so the solve waves read no global memory and
+    // take no exponentials; each solve wave carries its 16 state rows in
+    // fp32 as matrix-core accumulators from row to row (as the commit does)
+    // and feeds their bf16 rounding straight to the next row's products.
+    // The products run over 16-key tiles tc (keys 16 tc .. +15), lane (x, q)
+    // holding keys 16 tc + 4 q .. +3 of its row or column x, the layout of
+    // the state accumulators, two tiles (or a bf16 hi and lo pair) per
+    // 16x16x32 product: the 32 summed indices may come in any order as long
+    // as both operands agree, and lane q's eight are its four of each tile.
+    // Every exponent is at most 0 (G only falls along the chain).
+    if (nt == 0) {
+        constexpr int CR = 4;                           // ring rows; row t uses entry t % CR
+        uint2* const dtab = s_big;                      // D_t at slot t (A operand)
+        uint2* const ytab = s_big + 64 * NB;            // Y_tt at slot t (B operand)
+        // entry r: v of the slice's 64 columns ([node][column], 2 KB), then
+        // per node (beta, beta e^(G - E_t), e^(G - E_t), e^(E_(t+1) - G)) and
+        // e^(E_(t+1) - E_t), in 2.5 KB; q and k rows as s_k (16 x 128,
+        // swizzled) and the K^T tiles (tile tc: 512 bytes, lane-major) in s_u
+        constexpr int VE = 5 * 256;                     // halfwords per entry in the ring area
+        uint16_t* const vring = reinterpret_cast<uint16_t*>(s_big + 64 * 2 * NB);
+        constexpr int QE = (KLDS ? 2 : 3) * 16 * kD;    // halfwords per entry in s_u
+        uint16_t* const qring = reinterpret_cast<uint16_t*>(&s_u[0][0][0]);
+        static_assert(2 * NB * 512 + CR * VE * 2 <= BIG, "chain tables and ring entries fit the ring area");
+        static_assert(NB * kSolveWaves * 512 >= CR * QE * 2, "ring entries fit s_u");
+        auto vent = [&](int r) __attribute__((always_inline)) { return vring + r * VE; };
+        auto fent = [&](int r) __attribute__((always_inline)) { return reinterpret_cast<float*>(vring + r * VE + 16 * 64); };
+        auto qent = [&](int r) __attribute__((always_inline)) { return qring + r * QE; };
+        auto knent = [&](int r) __attribute__((always_inline)) { return qring + r * QE + 16 * kD; };
+        auto kent = [&](int r) __attribute__((always_inline)) { return qring + r * QE + 2 * 16 * kD; };
+        const int clast = n - 1;
+        // k / q fragment of block t (node = position), as gfrag
+        auto cfrag = [&](const uint16_t* base, int t, int cs) __attribute__((always_inline)) {
+            const uint32_t off = (uint32_t)min(16 * t + ln, clast) * (uint32_t)(kq_row * 2) + lane_col + 64u * cs;
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                  reinterpret_cast<const char*>(base) + off));
+        };
+        if (!solver) {
+            // producer p: rows p, p + 8, ..., each row's global operands
+            // requested one row ahead
+            const int p = wave - kSolveWaves;
+            const uint16_t* Vs = static_cast<const uint16_t*>(a.v) + vo_base + cbase;
+            bf16x8 sel[2];                              // columns 16 hh .. +15 of a 32-column window
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sel[hh][e] = (__bf16)((8 * lq + e == 16 * hh + ln) ? 1.f : 0.f);
+            struct DiagOps {
+                bf16x8 kt[KLDS ? 1 : 4];
+                bf16x8 qt[4];
+                u32x4 vt[2];                            // lane (r, q): node r, columns 16 q .. +15
+            };
+            auto dfetch = [&](int t, DiagOps& o) __attribute__((always_inline)) {
+                t = min(t, nblk - 1);
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) {
+                    o.qt[cs] = cfrag(Qb, t, cs);
+                    if constexpr (!KLDS) o.kt[cs] = cfrag(Kb, t, cs);
+                }
+                const uint16_t* vr = Vs + (size_t)min(16 * t + ln, clast) * vo_row + 16 * lq;
+                o.vt[0] = *reinterpret_cast<const u32x4*>(vr);
+                o.vt[1] = *reinterpret_cast<const u32x4*>(vr + 8);
+            };
+            auto diag = [&](int t, const DiagOps& o) __attribute__((always_inline)) {
+                bf16x8 kt[4];
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) {
+                    if constexpr (KLDS)
+                        kt[cs] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s_k + row_chunk(16 * t + ln, 4 * cs + lq)));
+                    else kt[cs] = o.kt[cs];
+                }
+                f32x4 gK = z, gQ = z;
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) {
+                    gK = mfma32(kt[cs], kt[cs], gK);
+                    gQ = mfma32(kt[cs], o.qt[cs], gQ);
+                }
+                float accd[4];
+                s16x4 yb;
+                diag_block(t, p, gK, gQ, accd, yb);
+                const int c = lane >> 2, qd = lane & 3;
+                uint16_t* dd = reinterpret_cast<uint16_t*>(dtab + 64 * t);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
+                ytab[64 * t + lane] = __builtin_bit_cast(uint2, yb);
+                // K_t^T tiles (keys 32 w + 16 hh .. +15 by the row's nodes), exact products
+                s16x4 kn[8];
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) kn[2 * w + hh] = to_bf16x4(mfma32(kt[w], sel[hh], z));
+                // per-node factors (lanes 0 .. 15: node 16 t + lane; lane 16: the decay)
+                const float E0 = t > 0 ? s_lg[16 * t - 1] : 0.f;
+                const float E1 = s_lg[min(16 * t + 15, NP - 1)];
+                const bool more = t + 1 < nblk;
+                const float gi = s_lg[16 * t + ln], bi = s_beta[16 * t + ln];
+                const float ei = __expf(gi - E0);
+                const float4 fac = lane < 16 ? make_float4(bi, bi * ei, ei, more ? __expf(E1 - gi) : 0.f)
+                                             : make_float4(more ? __expf(E1 - E0) : 0.f, 0.f, 0.f, 0.f);
+                // entry t % CR is free once every solve wave is done with row t - CR
+                const int r = t % CR;
+                if (t >= CR)
+#pragma unroll
+                    for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_oready[gg], t - CR + 1);
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) {
+                    *reinterpret_cast<u32x4*>(qent(r) + row_chunk(ln, 4 * cs + lq)) = __builtin_bit_cast(u32x4, o.qt[cs]);
+                    if constexpr (!KLDS)
+                        *reinterpret_cast<u32x4*>(kent(r) + row_chunk(ln, 4 * cs + lq)) = __builtin_bit_cast(u32x4, o.kt[cs]);
+                }
+#pragma unroll
+                for (int tc = 0; tc < 8; ++tc)
+                    *reinterpret_cast<uint2*>(knent(r) + tc * 256 + 4 * lane) = __builtin_bit_cast(uint2, kn[tc]);
+                uint16_t* vw = vent(r) + ln * 64 + 16 * lq;
+                *reinterpret_cast<u32x4*>(vw) = o.vt[0];
+                *reinterpret_cast<u32x4*>(vw + 8) = o.vt[1];
+                if (lane <= 16) reinterpret_cast<float4*>(fent(r))[lane] = fac;
+                publish_set(&s_done[t], 1, lane);
+            };
+            DiagOps da, db;
+            dfetch(p, da);
+            for (int t = p; t < nblk; t += 2 * kProducers) {
+                dfetch(t + kProducers, db);
+                diag(t, da);
+                if (t + kProducers >= nblk) break;
+                dfetch(t + 2 * kProducers, da);
+                diag(t + kProducers, db);
+            }
+            return;
+        }
+        __builtin_amdgcn_s_setprio(2);
+        const int g = wave;
+        const int c0 = cbase + 16 * g;
+        // the wave's state rows c0 .. c0 + 15, fp32: lane (r, q) holds row
+        // c0 + r, keys 16 tc + 4 q .. +3 in st[tc].  Fused: the rows this
+        // wave committed above (the fence orders its own stores before the
+        // loads).
+        if constexpr (FUSED) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        const float* Sp = (FUSED ? c.S_out : a.S0) + ((size_t)b * Hv + h) * kD * kD + (size_t)(c0 + ln) * kD + 4 * lq;
+        f32x4 st[8];
+#pragma unroll
+        for (int tc = 0; tc < 8; ++tc) st[tc] = *reinterpret_cast<const f32x4*>(Sp + 16 * tc);
+        s16x4 ident;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
+        const __amdgpu_buffer_rsrc_t u_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(Ug, (short)0, N * kD * 4, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            O + vo_base, (short)0, ((n - 1) * Hv + 1) * kD * 2, kBufferFlags);
+        // 16-key tile tc of row r of a 16 x 128 block swizzled as s_k: lane q
+        // holds keys 16 tc + 4 q .. +3 (an 8-byte read)
+        auto tile_row = [&](const uint16_t* blk, int r, int tc) __attribute__((always_inline)) {
+            return __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(
+                                                 blk + row_chunk(r, 2 * tc + (lq >> 1)) + 4 * (lq & 1)));
+        };
+        // two 4-index halves as one 16x16x32 operand
+        auto cat = [](s16x4 x, s16x4 y) __attribute__((always_inline)) {
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // K_t S_t^T: [node 4q + m][column], from the row's k rows in LDS
+        // (s_k itself, or the ring entry) and the state's bf16 rounding sb
+        s16x4 sb[8];
+        f32x4 ks;
+        auto kst = [&](const uint16_t* kb) __attribute__((always_inline)) {
+            f32x4 k1 = z, k2 = z;
+#pragma unroll
+            for (int tc = 0; tc < 8; tc += 4) {
+                k1 = mfma32(cat(tile_row(kb, ln, tc), tile_row(kb, ln, tc + 1)), cat(sb[tc], sb[tc + 1]), k1);
+                k2 = mfma32(cat(tile_row(kb, ln, tc + 2), tile_row(kb, ln, tc + 3)), cat(sb[tc + 2], sb[tc + 3]), k2);
+            }
+            return k1 + k2;
+        };
+#pragma unroll
+        for (int tc = 0; tc < 8; ++tc) sb[tc] = to_bf16x4(st[tc]);
+        if constexpr (KLDS) ks = kst(s_k);
+        // Row t.  With k in LDS the next row's K S^T is formed in the same
+        // step as this row's outputs.
+        for (int t = 0; t < nblk; ++t) {
+            const int pr = 16 * t + ln;
+            const int r = t % CR;
+            wait_flag_ge(&s_done[t], 1);
+            if constexpr (!KLDS) ks = kst(kent(r));
+            const float4* fr = reinterpret_cast<const float4*>(fent(r));
+            float4 fn[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) fn[m] = fr[4 * lq + m];
+            const float eo = fr[ln].z, dec = fr[16].x;
+            const s16x4 vt = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(vent(r) + ln * 64 + 16 * g + 4 * lq));
+            const f32x4 vd = mfma16(vt, ident, z);
+            f32x4 acc;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = fn[m].x * vd[m] - fn[m].y * ks[m];
+            const s16x4 dt = __builtin_bit_cast(s16x4, dtab[64 * t + lane]);
+            const s16x4 ytt = __builtin_bit_cast(s16x4, ytab[64 * t + lane]);
+            s16x4 hi, lo;
+            split4(acc, hi, lo);
+            const f32x4 uf = mfma32(cat(dt, dt), cat(hi, lo), z);   // lane (c, q): nodes 4q + m, column c
+            const s16x4 ut = to_bf16x4(uf);
+            // the next row's state (the chain every row waits for; after
+            // the last row the factors are 0 and it is not used)
+            {
+                f32x4 wu;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) wu[m] = fn[m].w * uf[m];
+                s16x4 wh, wl;
+                split4(wu, wh, wl);
+                const uint16_t* knb = knent(r) + 4 * lane;
+#pragma unroll
+                for (int tc = 0; tc < 8; ++tc) {
+                    const s16x4 kn = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(knb + tc * 256));
+                    st[tc] = mfma32(cat(kn, kn), cat(wh, wl), st[tc] * dec);
+                }
+            }
+            // e^(G - E_t) Q_t S_t^T + Y_tt U_t: [column 4q + m][node]
+            const uint16_t* qb = qent(r);
+            f32x4 oc = z, oc2 = z;
+#pragma unroll
+            for (int tc = 0; tc < 8; tc += 4) {
+                oc = mfma32(cat(sb[tc], sb[tc + 1]), cat(tile_row(qb, ln, tc), tile_row(qb, ln, tc + 1)), oc);
+                oc2 = mfma32(cat(sb[tc + 2], sb[tc + 3]), cat(tile_row(qb, ln, tc + 2), tile_row(qb, ln, tc + 3)), oc2);
+            }
+#pragma unroll
+            for (int tc = 0; tc < 8; ++tc) sb[tc] = to_bf16x4(st[tc]);
+            if constexpr (KLDS) ks = kst(s_k + 16 * min(t + 1, nblk - 1) * kD);
+            oc = (oc + oc2) * eo;
+            oc = mfma16(ut, ytt, oc);
+            publish_set(&s_oready[g], t + 1, lane);     // the row's ring entry is read
+            // the cache rows (lane (n, q): nodes 4q .. 4q+3 of column n) and
+            // outputs; positions past the tree store outside the buffers
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm) {
+                const int i = 16 * t + 4 * lq + mm;
+                const int off = i < n ? (i * kD + c0 + ln) * 4 : 0x7fffffff;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(uf[mm]), u_rsrc, off, 0, 0);
+            }
+            const int orow = pr < n ? (pr * Hv * kD + c0 + 4 * lq) * 2 : 0x7fffffff;
+            const s16x4 ob = to_bf16x4(oc);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), o_rsrc, orow, 0, 0);
+        }
+        return;
+    }
+
     if (solver) {
         // ================= solve waves =================
         // (the solve is the chain every row waits for: its waves issue ahead
@@ -1104,50 +1409,10 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         int done = 1;
         if (diag) {
             // ---- D_t = (I + X_tt)^-1 and Y_tt ----
-            // X_tt[i][j] at lane (j, q), element m: i = 4q + m
-            float xv[4];
-            {
-                const int pj = 16 * t + ln;
-                const int lj = s_last[pj];
-                const float lgj = s_lg[pj];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int pi2 = 16 * t + 4 * lq + m;
-                    const bool anc = (pj < pi2) & (pi2 <= lj);
-                    const float x = s_beta[pi2] * __expf(fminf(s_lg[pi2] - lgj, 0.f)) * gA[0][m];
-                    xv[m] = anc ? x : 0.f;
-                }
-            }
-            // Y_tt[i][j] at lane (i, q), element m: j = 4q + m (j an ancestor of i or i)
-            s16x4 yb;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int pj = 16 * t + 4 * lq + m;
-                const bool anc = (pj <= pi) & (pi <= (int)s_last[pj]);
-                const float y = __expf(fminf(lgi - s_lg[pj], 0.f)) * gB[0][m];
-                yb[m] = (short)bf16_rne(anc ? y : 0.f);
-            }
-            // fp32 forward substitution, four lanes per column: lane 4c + qd
-            // holds rows 4qd .. 4qd+3 of column c; step m reads column m of
-            // X_tt (stored [col][row] by the lanes that hold it) and takes y_m
-            // from its owner within the lane quad
-            float* xd = &s_xd[p][0];
-            *reinterpret_cast<float4*>(&xd[ln * 16 + 4 * lq]) = make_float4(xv[0], xv[1], xv[2], xv[3]);
-            const int c = lane >> 2, qd = lane & 3;
             float accd[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) accd[e] = (4 * qd + e == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < 15; ++m) {
-                const float4 xc = *reinterpret_cast<const float4*>(&xd[m * 16 + 4 * qd]);
-                const float ym = quad_bcast(accd[m & 3], m >> 2);
-                const float xr[4] = {xc.x, xc.y, xc.z, xc.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {               // rows below m only
-                    const float upd = fmaf(-xr[e], ym, accd[e]);
-                    accd[e] = 4 * qd + e > m ? upd : accd[e];
-                }
-            }
+            s16x4 yb;
+            diag_block(t, p, gA[0], gB[0], accd, yb);
+            const int c = lane >> 2, qd = lane & 3;
             uint16_t* dd = KLDS ? reinterpret_cast<uint16_t*>(&s_d[t][0])
                                 : reinterpret_cast<uint16_t*>(&ring[slot_at(base + 16) * 64]);
             wait_ring(t);
