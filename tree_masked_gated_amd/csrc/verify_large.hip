@@ -196,6 +196,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     }
     // a solve wave's 16 S0 rows (fp32; its bf16 operands are formed after the
     // setup): lane (r, q) takes row cbase + 16 wave + r, columns 32 cs + 8 q .. +7
+    // (For a chain the same registers bring each producer's first q and v
+    // rows during the setup: see the chain path.)
     float4 s0_r[8];
     if (!FUSED && KLDS && solver) {
         const float* S0p =
@@ -480,6 +482,35 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     if (not_chain) s_notchain = 1;
     lds_barrier();
     const int nt = s_notchain ? n : 0;
+    // A chain's first operands (the chain path below) are requested during
+    // the setup, so that they arrive meanwhile: each producer's first row,
+    // each solve wave's state rows.
+    const int clast = max(n - 1, 0);
+    const uint32_t lane_col = 16u * lq;
+    // k / q fragment of block t of a chain (node = position): lane (r, q)
+    // holds row 16 t + r (clamped), columns 32 cs + 8 q .. +7
+    auto cfrag = [&](const uint16_t* base, int t, int cs) __attribute__((always_inline)) {
+        const uint32_t off = (uint32_t)min(16 * t + ln, clast) * (uint32_t)(kq_row * 2) + lane_col + 64u * cs;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                              reinterpret_cast<const char*>(base) + off));
+    };
+    struct DiagOps {
+        bf16x8 kt[KLDS ? 1 : 4];                        // (without k in LDS) k of the row
+        bf16x8 qt[4];
+        u32x4 vt[2];                                    // lane (r, q): node r, columns 16 q .. +15
+    };
+    const uint16_t* const Vsl = static_cast<const uint16_t*>(a.v) + vo_base + cbase;
+    auto dfetch = [&](int t, DiagOps& o) __attribute__((always_inline)) {
+        t = min(t, max((n + 15) / 16 - 1, 0));
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs) {
+            o.qt[cs] = cfrag(Qb, t, cs);
+            if constexpr (!KLDS) o.kt[cs] = cfrag(Kb, t, cs);
+        }
+        const uint16_t* vr = Vsl + (size_t)min(16 * t + ln, clast) * vo_row + 16 * lq;
+        o.vt[0] = *reinterpret_cast<const u32x4*>(vr);
+        o.vt[1] = *reinterpret_cast<const u32x4*>(vr + 8);
+    };
     for (int i = tid; i < nt; i += NT) {                // bit i of its parent's children row; first child
         const int p = s_jump[i];
         const int pr = p < 0 ? NP : p;
@@ -603,6 +634,15 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         }
     }
     if (nt == 0) {
+        if (!solver) {
+            // the producer's first row: q into s0_r[0 .. 3], v into [4 .. 5]
+            const int t0 = min(wave - kSolveWaves, (n + 15) / 16 - 1);
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) s0_r[cs] = __builtin_bit_cast(float4, cfrag(Qb, t0, cs));
+            const uint16_t* vr = Vsl + (size_t)min(16 * t0 + ln, clast) * vo_row + 16 * lq;
+            s0_r[4] = *reinterpret_cast<const float4*>(vr);
+            s0_r[5] = *reinterpret_cast<const float4*>(vr + 8);
+        }
         // a chain's path log-gates are prefix sums: a scan within each wave
         // (lane shifts) and the preceding waves' totals
         static_assert(NP <= NT, "one chain node per thread");
@@ -657,10 +697,11 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         }
         pk[j] = v;
     }
-    for (int sb = tid; sb < NB; sb += NT) {
-        int m = -1;
-        for (int e = 0; e < 16; ++e) m = max(m, (int)s_last[16 * sb + e]);
-        s_mlast[sb] = m;
+    if (nt && tid < NP) {                               // (a max over each block's 16 lanes)
+        int m = s_last[tid];
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d));
+        if ((tid & 15) == 0) s_mlast[tid >> 4] = m;
     }
     if (slice == 0)
         for (int i = tid; i < n; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
@@ -712,7 +753,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     //  * the producer items of row t: one for the diagonal block, without k in
     //    LDS one for the right-hand sides, then one per C occupied blocks.
     // Prefix sums over the rows go through LDS (one read of all rows' words).
-    if (wave == 0) {
+    // (A chain takes none of it.)
+    if (wave == 0 && nt) {
         int ml[NB];
 #pragma unroll
         for (int sb = 0; sb < NB; sb += 4) {
@@ -766,7 +808,6 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // row 16 blk + r (clamped), columns 32 cs + 8 q .. +7, from global
     // memory (a uniform base and a 32-bit lane offset); from LDS the same
     // lanes read the row's chunk 4 cs + q.
-    const uint32_t lane_col = 16u * lq;
     auto gfrag = [&](const uint16_t* base, int blk, int cs) __attribute__((always_inline)) {
         const uint32_t row = (uint32_t)node_at(16 * blk + ln);
         const uint32_t off = row * (uint32_t)(kq_row * 2) + lane_col + 64u * cs;
@@ -845,12 +886,14 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // take no exponentials; each solve wave carries its 16 state rows in
     // fp32 as matrix-core accumulators from row to row (as the commit does)
     // and feeds their bf16 rounding straight to the next row's products.
-    // The products run over 16-key tiles tc (keys 16 tc .. +15), lane (x, q)
-    // holding keys 16 tc + 4 q .. +3 of its row or column x, the layout of
-    // the state accumulators, two tiles (or a bf16 hi and lo pair) per
-    // 16x16x32 product: the 32 summed indices may come in any order as long
-    // as both operands agree, and lane q's eight are its four of each tile.
-    // Every exponent is at most 0 (G only falls along the chain).
+    // The state's key columns are taken in 16-key tiles tc = 2 w + hh (keys
+    // 32 w + 8 (i / 4) + 4 hh + i % 4, i = 0 .. 15), so that lane (r, q) of
+    // tiles 2w and 2w + 1 holds keys 32 w + 8 q .. +7 of row r: the S0
+    // registers' layout, and as bf16 one 16x16x32 operand over a 32-key
+    // window; the update pairs a tile with itself against a bf16 hi and lo
+    // part (the summed indices may come in any order as long as both
+    // operands agree).  Every exponent is at most 0 (G only falls along the
+    // chain).
     if (nt == 0) {
         constexpr int CR = 4;                           // ring rows; row t uses entry t % CR
         uint2* const dtab = s_big;                      // D_t at slot t (A operand)
@@ -870,39 +913,18 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         auto qent = [&](int r) __attribute__((always_inline)) { return qring + r * QE; };
         auto knent = [&](int r) __attribute__((always_inline)) { return qring + r * QE + 16 * kD; };
         auto kent = [&](int r) __attribute__((always_inline)) { return qring + r * QE + 2 * 16 * kD; };
-        const int clast = n - 1;
-        // k / q fragment of block t (node = position), as gfrag
-        auto cfrag = [&](const uint16_t* base, int t, int cs) __attribute__((always_inline)) {
-            const uint32_t off = (uint32_t)min(16 * t + ln, clast) * (uint32_t)(kq_row * 2) + lane_col + 64u * cs;
-            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                  reinterpret_cast<const char*>(base) + off));
-        };
         if (!solver) {
             // producer p: rows p, p + 8, ..., each row's global operands
             // requested one row ahead
             const int p = wave - kSolveWaves;
-            const uint16_t* Vs = static_cast<const uint16_t*>(a.v) + vo_base + cbase;
-            bf16x8 sel[2];                              // columns 16 hh .. +15 of a 32-column window
+            // selection of the keys of tile 2 w + hh from a 32-key window:
+            // column c takes key 8 (c / 4) + 4 hh + c % 4
+            bf16x8 sel[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sel[hh][e] = (__bf16)((8 * lq + e == 16 * hh + ln) ? 1.f : 0.f);
-            struct DiagOps {
-                bf16x8 kt[KLDS ? 1 : 4];
-                bf16x8 qt[4];
-                u32x4 vt[2];                            // lane (r, q): node r, columns 16 q .. +15
-            };
-            auto dfetch = [&](int t, DiagOps& o) __attribute__((always_inline)) {
-                t = min(t, nblk - 1);
-#pragma unroll
-                for (int cs = 0; cs < 4; ++cs) {
-                    o.qt[cs] = cfrag(Qb, t, cs);
-                    if constexpr (!KLDS) o.kt[cs] = cfrag(Kb, t, cs);
-                }
-                const uint16_t* vr = Vs + (size_t)min(16 * t + ln, clast) * vo_row + 16 * lq;
-                o.vt[0] = *reinterpret_cast<const u32x4*>(vr);
-                o.vt[1] = *reinterpret_cast<const u32x4*>(vr + 8);
-            };
+                for (int e = 0; e < 8; ++e)
+                    sel[hh][e] = (__bf16)((8 * lq + e == 8 * (ln >> 2) + 4 * hh + (ln & 3)) ? 1.f : 0.f);
             auto diag = [&](int t, const DiagOps& o) __attribute__((always_inline)) {
                 bf16x8 kt[4];
 #pragma unroll
@@ -925,7 +947,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
                 ytab[64 * t + lane] = __builtin_bit_cast(uint2, yb);
-                // K_t^T tiles (keys 32 w + 16 hh .. +15 by the row's nodes), exact products
+                // K_t^T tiles (tile 2 w + hh: its keys by the row's nodes), exact products
                 s16x4 kn[8];
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
@@ -959,8 +981,14 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 if (lane <= 16) reinterpret_cast<float4*>(fent(r))[lane] = fac;
                 publish_set(&s_done[t], 1, lane);
             };
-            DiagOps da, db;
-            dfetch(p, da);
+            DiagOps da, db;                             // (row p's q and v: requested in the setup)
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs) {
+                da.qt[cs] = __builtin_bit_cast(bf16x8, s0_r[cs]);
+                if constexpr (!KLDS) da.kt[cs] = cfrag(Kb, p, cs);
+            }
+            da.vt[0] = __builtin_bit_cast(u32x4, s0_r[4]);
+            da.vt[1] = __builtin_bit_cast(u32x4, s0_r[5]);
             for (int t = p; t < nblk; t += 2 * kProducers) {
                 dfetch(t + kProducers, db);
                 diag(t, da);
@@ -973,15 +1001,20 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         __builtin_amdgcn_s_setprio(2);
         const int g = wave;
         const int c0 = cbase + 16 * g;
-        // the wave's state rows c0 .. c0 + 15, fp32: lane (r, q) holds row
-        // c0 + r, keys 16 tc + 4 q .. +3 in st[tc].  Fused: the rows this
-        // wave committed above (the fence orders its own stores before the
-        // loads).
-        if constexpr (FUSED) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        const float* Sp = (FUSED ? c.S_out : a.S0) + ((size_t)b * Hv + h) * kD * kD + (size_t)(c0 + ln) * kD + 4 * lq;
+        // the wave's state rows: lane (r, q) of tile 2 w + hh holds row
+        // c0 + r, keys 32 w + 8 q + 4 hh .. +3 (S0's as requested before the
+        // setup; fused: the rows this wave committed, re-read after a fence
+        // that orders its own stores before the loads)
         f32x4 st[8];
+        if constexpr (FUSED || !KLDS) {
+            if constexpr (FUSED) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            const float* Sp = (FUSED ? c.S_out : a.S0) + ((size_t)b * Hv + h) * kD * kD + (size_t)(c0 + ln) * kD + 8 * lq;
 #pragma unroll
-        for (int tc = 0; tc < 8; ++tc) st[tc] = *reinterpret_cast<const f32x4*>(Sp + 16 * tc);
+            for (int tc = 0; tc < 8; ++tc) st[tc] = *reinterpret_cast<const f32x4*>(Sp + 32 * (tc >> 1) + 4 * (tc & 1));
+        } else {
+#pragma unroll
+            for (int tc = 0; tc < 8; ++tc) st[tc] = __builtin_bit_cast(f32x4, s0_r[tc]);
+        }
         s16x4 ident;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ident[e] = (4 * lq + e == ln) ? (short)0x3f80 : (short)0;
@@ -989,11 +1022,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             __builtin_amdgcn_make_buffer_rsrc(Ug, (short)0, N * kD * 4, kBufferFlags);
         const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             O + vo_base, (short)0, ((n - 1) * Hv + 1) * kD * 2, kBufferFlags);
-        // 16-key tile tc of row r of a 16 x 128 block swizzled as s_k: lane q
-        // holds keys 16 tc + 4 q .. +3 (an 8-byte read)
-        auto tile_row = [&](const uint16_t* blk, int r, int tc) __attribute__((always_inline)) {
-            return __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(
-                                                 blk + row_chunk(r, 2 * tc + (lq >> 1)) + 4 * (lq & 1)));
+        // keys 32 w + 8 q .. +7 of row r of a 16 x 128 block swizzled as s_k
+        auto win = [&](const uint16_t* blk, int r, int w) __attribute__((always_inline)) {
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(blk + row_chunk(r, 4 * w + lq)));
         };
         // two 4-index halves as one 16x16x32 operand
         auto cat = [](s16x4 x, s16x4 y) __attribute__((always_inline)) {
@@ -1006,9 +1037,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         auto kst = [&](const uint16_t* kb) __attribute__((always_inline)) {
             f32x4 k1 = z, k2 = z;
 #pragma unroll
-            for (int tc = 0; tc < 8; tc += 4) {
-                k1 = mfma32(cat(tile_row(kb, ln, tc), tile_row(kb, ln, tc + 1)), cat(sb[tc], sb[tc + 1]), k1);
-                k2 = mfma32(cat(tile_row(kb, ln, tc + 2), tile_row(kb, ln, tc + 3)), cat(sb[tc + 2], sb[tc + 3]), k2);
+            for (int w = 0; w < 4; w += 2) {
+                k1 = mfma32(win(kb, ln, w), cat(sb[2 * w], sb[2 * w + 1]), k1);
+                k2 = mfma32(win(kb, ln, w + 1), cat(sb[2 * w + 2], sb[2 * w + 3]), k2);
             }
             return k1 + k2;
         };
@@ -1057,9 +1088,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             const uint16_t* qb = qent(r);
             f32x4 oc = z, oc2 = z;
 #pragma unroll
-            for (int tc = 0; tc < 8; tc += 4) {
-                oc = mfma32(cat(sb[tc], sb[tc + 1]), cat(tile_row(qb, ln, tc), tile_row(qb, ln, tc + 1)), oc);
-                oc2 = mfma32(cat(sb[tc + 2], sb[tc + 3]), cat(tile_row(qb, ln, tc + 2), tile_row(qb, ln, tc + 3)), oc2);
+            for (int w = 0; w < 4; w += 2) {
+                oc = mfma32(cat(sb[2 * w], sb[2 * w + 1]), win(qb, ln, w), oc);
+                oc2 = mfma32(cat(sb[2 * w + 2], sb[2 * w + 3]), win(qb, ln, w + 1), oc2);
             }
 #pragma unroll
             for (int tc = 0; tc < 8; ++tc) sb[tc] = to_bf16x4(st[tc]);
