@@ -900,19 +900,26 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         uint2* const ytab = s_big + 64 * NB;            // Y_tt at slot t (B operand)
         // entry r: v of the slice's 64 columns ([node][column], 2 KB), then
         // per node (beta, beta e^(G - E_t), e^(G - E_t), e^(E_(t+1) - G)) and
-        // e^(E_(t+1) - E_t), in 2.5 KB; q and k rows as s_k (16 x 128,
-        // swizzled) and the K^T tiles (tile tc: 512 bytes, lane-major) in s_u
+        // e^(E_(t+1) - E_t), in 2.5 KB, in the ring area; the K^T tiles (tile
+        // tc: 1 KB, lane-major, each lane's four values twice: one 16x16x32
+        // operand) in s_u; q and k rows as s_k (16 x 128, swizzled), q in
+        // the ring area with k in LDS, else both in s_u
         constexpr int VE = 5 * 256;                     // halfwords per entry in the ring area
         uint16_t* const vring = reinterpret_cast<uint16_t*>(s_big + 64 * 2 * NB);
-        constexpr int QE = (KLDS ? 2 : 3) * 16 * kD;    // halfwords per entry in s_u
+        constexpr int KNE = 2 * 16 * kD;                // halfwords of an entry's K^T tiles
+        constexpr int QE = KNE + (KLDS ? 0 : 2 * 16 * kD);   // halfwords per entry in s_u
         uint16_t* const qring = reinterpret_cast<uint16_t*>(&s_u[0][0][0]);
-        static_assert(2 * NB * 512 + CR * VE * 2 <= BIG, "chain tables and ring entries fit the ring area");
+        uint16_t* const qring2 = vring + CR * VE;       // (with k in LDS)
+        static_assert(2 * NB * 512 + CR * VE * 2 + (KLDS ? CR * 16 * kD * 2 : 0) <= BIG,
+                      "chain tables and ring entries fit the ring area");
         static_assert(NB * kSolveWaves * 512 >= CR * QE * 2, "ring entries fit s_u");
         auto vent = [&](int r) __attribute__((always_inline)) { return vring + r * VE; };
         auto fent = [&](int r) __attribute__((always_inline)) { return reinterpret_cast<float*>(vring + r * VE + 16 * 64); };
-        auto qent = [&](int r) __attribute__((always_inline)) { return qring + r * QE; };
-        auto knent = [&](int r) __attribute__((always_inline)) { return qring + r * QE + 16 * kD; };
-        auto kent = [&](int r) __attribute__((always_inline)) { return qring + r * QE + 2 * 16 * kD; };
+        auto knent = [&](int r) __attribute__((always_inline)) { return qring + r * QE; };
+        auto qent = [&](int r) __attribute__((always_inline)) {
+            return KLDS ? qring2 + r * 16 * kD : qring + r * QE + KNE;
+        };
+        auto kent = [&](int r) __attribute__((always_inline)) { return qring + r * QE + KNE + 16 * kD; };
         if (!solver) {
             // producer p: rows p, p + 8, ..., each row's global operands
             // requested one row ahead
@@ -974,7 +981,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 }
 #pragma unroll
                 for (int tc = 0; tc < 8; ++tc)
-                    *reinterpret_cast<uint2*>(knent(r) + tc * 256 + 4 * lane) = __builtin_bit_cast(uint2, kn[tc]);
+                    *reinterpret_cast<u32x4*>(knent(r) + tc * 512 + 8 * lane) =
+                        __builtin_bit_cast(u32x4, __builtin_shufflevector(kn[tc], kn[tc], 0, 1, 2, 3, 4, 5, 6, 7));
                 uint16_t* vw = vent(r) + ln * 64 + 16 * lq;
                 *reinterpret_cast<u32x4*>(vw) = o.vt[0];
                 *reinterpret_cast<u32x4*>(vw + 8) = o.vt[1];
@@ -1047,11 +1055,15 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         for (int tc = 0; tc < 8; ++tc) sb[tc] = to_bf16x4(st[tc]);
         if constexpr (KLDS) ks = kst(s_k);
         // Row t.  With k in LDS the next row's K S^T is formed in the same
-        // step as this row's outputs.
+        // step as this row's outputs.  Each row's flag is read during the row
+        // before (its latency under that row's stores) and waited on only
+        // when it was not yet set.
+        int fl = __hip_atomic_load(&s_done[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         for (int t = 0; t < nblk; ++t) {
             const int pr = 16 * t + ln;
             const int r = t % CR;
-            wait_flag_ge(&s_done[t], 1);
+            if (__builtin_amdgcn_readfirstlane(fl) < 1) wait_flag_ge(&s_done[t], 1);
+            asm volatile("" ::: "memory");
             if constexpr (!KLDS) ks = kst(kent(r));
             const float4* fr = reinterpret_cast<const float4*>(fent(r));
             float4 fn[4];
@@ -1077,11 +1089,11 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 for (int m = 0; m < 4; ++m) wu[m] = fn[m].w * uf[m];
                 s16x4 wh, wl;
                 split4(wu, wh, wl);
-                const uint16_t* knb = knent(r) + 4 * lane;
+                const uint16_t* knb = knent(r) + 8 * lane;
 #pragma unroll
                 for (int tc = 0; tc < 8; ++tc) {
-                    const s16x4 kn = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(knb + tc * 256));
-                    st[tc] = mfma32(cat(kn, kn), cat(wh, wl), st[tc] * dec);
+                    const bf16x8 kn = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(knb + tc * 512));
+                    st[tc] = mfma32(kn, cat(wh, wl), st[tc] * dec);
                 }
             }
             // e^(G - E_t) Q_t S_t^T + Y_tt U_t: [column 4q + m][node]
@@ -1098,6 +1110,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             oc = (oc + oc2) * eo;
             oc = mfma16(ut, ytt, oc);
             publish_set(&s_oready[g], t + 1, lane);     // the row's ring entry is read
+            fl = __hip_atomic_load(&s_done[min(t + 1, nblk - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             // the cache rows (lane (n, q): nodes 4q .. 4q+3 of column n) and
             // outputs; positions past the tree store outside the buffers
 #pragma unroll
