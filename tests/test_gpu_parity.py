@@ -224,6 +224,33 @@ def test_gate_and_beta_extremes():
     check_case(parent, accepted, lay, "bf16", 1, 1, name="beta=1")
 
 
+@pytest.mark.parametrize("N", [200, 300])
+def test_chain_path_extremes(N):
+    """Chains in the larger-tree kernel take the chunked recurrence (each
+    16-node block row starts from the state at the node before it); a chain
+    with one extra branch, in the same launch, takes the tile path.  Gates and
+    write strengths at their extremes: pure decay (beta = 0), no decay with
+    full writes (g = 1, beta = 1), and gates so small that the factors of
+    distant nodes underflow to zero in fp32."""
+    rng = np.random.default_rng(60 + N)
+    near = W.tree_chain(N)
+    near[N - 1] = N - 3                                   # a sibling of node N - 2
+    parents = [W.tree_chain(N), near]
+    parent, lay = custom(61 + N, parents, 2, 4, 128)
+    accepted = np.array([N - 1, N - 2], np.int32)
+    check_case(parent, accepted, lay, "bf16", 2, 4, name=f"chain path N={N}")
+    lay0 = {k: v.copy() for k, v in lay.items()}
+    lay["beta"][:] = 0.0
+    check_case(parent, accepted, lay, "bf16", 2, 4, name=f"chain path N={N}, beta=0")
+    lay = {k: v.copy() for k, v in lay0.items()}
+    lay["beta"][:] = 1.0
+    lay["g"][:] = 1.0
+    check_case(parent, accepted, lay, "bf16", 2, 4, name=f"chain path N={N}, beta=1, g=1")
+    lay = {k: v.copy() for k, v in lay0.items()}
+    lay["g"][:] = 1e-3
+    check_case(parent, accepted, lay, "bf16", 2, 4, name=f"chain path N={N}, g=1e-3")
+
+
 def test_invalid_trees():
     rng = np.random.default_rng(59)
     N = 20
