@@ -153,6 +153,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     __shared__ int s_rstar[NB];                         // rows released before row t's slots are free
     __shared__ uint16_t s_items[L::ITEMS];              // producer items: row | (item of the row << 8)
     __shared__ int s_nitems;
+    __shared__ int s_claim;                             // producer items claimed past the first kProducers
     __shared__ int s_done[NB];                          // row t's tiles and parts finished (complete at s_tn[t] + NFIX)
     __shared__ int s_oready[kSolveWaves];               // rows finished by each solve wave
     __shared__ int s_bad;                               // first node with an invalid parent
@@ -476,6 +477,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     for (int x = tid; x < (NP + 1) * WC; x += NT) s_cm[x] = 0u;
     for (int x = tid; x <= NP; x += NT) s_fc[x] = NP;
     if (tid < NB) s_done[tid] = 0;
+    if (tid == 0) s_claim = 0;
     if (tid < kSolveWaves) s_oready[tid] = 0;
     if (tid < 3) s_more[tid] = 0;
     // a chain skips the construction (nt = 0): the identity and last = n - 1
@@ -1496,7 +1498,15 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     fetch(p, io);
     // (as for the solve waves: only the first item's operands are in flight)
     wait_vmem_le<KLDS ? 4 : 4 + 4 + 4>();
-    for (int it = p; it < nitems; it += kProducers) work(io, it + kProducers);
+    // Items after each producer's first are claimed in list order from an LDS
+    // counter, one item ahead, so that a producer done early takes the next.
+    for (int it = p; it < nitems;) {
+        int nxt = 0;
+        if (lane == 0) nxt = __hip_atomic_fetch_add(&s_claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        nxt = __builtin_amdgcn_readfirstlane(nxt) + kProducers;
+        work(io, nxt);
+        it = nxt;
+    }
 }
 
 }  // namespace
