@@ -18,10 +18,11 @@
 //    LDS at its end), so their latency overlaps it; its barriers order LDS
 //    only.
 //  * producers (waves 4 .. 11): the work of all block rows as one row-major
-//    list of items dealt round robin, each item's global operands requested
-//    one item ahead.  A row's first item forms the diagonal block's inverse
+//    list of items, each producer's first dealt round robin and the rest
+//    claimed in order, each item's global operands requested one item
+//    ahead.  A row's first item forms the diagonal block's inverse
 //    D_t = (I + X_tt)^-1 (fp32 substitution, kept bf16) and its output tile
-//    Y_tt; the others form, for a few occupied column blocks s, the tiles
+//    Y_tt (and, without k in LDS, the row's right-hand sides); the others form, for a few occupied column blocks s, the tiles
 //    -X_ts and Y_ts from one read of k_s.  Tiles go to a ring of LDS slots,
 //    D_t to a table; a per-row counter says when the row is complete.
 //  * solve (waves 0 .. 3, 16 value columns each): row by row, the
@@ -104,7 +105,7 @@ struct LargeShape {
     // last).  Rows with a header take an even number of slots, so two-slot
     // objects never wrap.
     static constexpr int HDR = KLDS ? 0 : 17;
-    static constexpr int NFIX = KLDS ? 1 : 2;           // items of a row before its occupied blocks'
+    static constexpr int NFIX = 1;                      // items of a row before its occupied blocks'
 
     static constexpr int RING = NB <= 16 ? 84 : 112;    // 512-byte tile slots
     static constexpr int BIG = RING * 512 > SCRATCH ? RING * 512 : SCRATCH;
@@ -752,8 +753,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     //  * the ring: row t takes the next HDR + 2 s_tn[t] + 1 slots, counted
     //    over all rows modulo RING; they may be written once every row whose
     //    slots they reuse has been released by all solve waves;
-    //  * the producer items of row t: one for the diagonal block, without k in
-    //    LDS one for the right-hand sides, then one per C occupied blocks.
+    //  * the producer items of row t: one for the diagonal block (without k
+    //    in LDS also the right-hand sides), then one per C occupied blocks.
     // Prefix sums over the rows go through LDS (one read of all rows' words).
     // (A chain takes none of it.)
     if (wave == 0 && nt) {
@@ -1319,7 +1320,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // An item's operands, requested during the previous item: its row, that row's
     // slots and occupied blocks, the node rows of its k fragments, q of its
     // row and, when k is not in LDS, k of its row and either k of its
-    // column block (C = 1) or, for the right-hand sides' item, v of its row
+    // column block (C = 1) or, for the diagonal item, v of its row
     // (the slice's 64 columns in two 32-column windows: lane (r, q) holds
     // row r, columns 32 w + 8 q .. +7 of window w, in the same registers).
     struct ItemOps {
@@ -1359,7 +1360,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             // the compiler join two register sets, waiting for their loads)
             const char* pk = reinterpret_cast<const char*>(Kb) + (uint32_t)o.rx[0] * (uint32_t)(kq_row * 2) + lane_col;
             const char* pv = reinterpret_cast<const char*>(Vs) + (uint32_t)o.rt * (uint32_t)(vo_row * 2) + lane_col;
-            const bool isv = j == 1;
+            const bool isv = j == 0;
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs)
                 o.kx[0][cs] = *reinterpret_cast<const u32x4*>(isv ? pv + 64 * (cs & 1) : pk + 64 * cs);
@@ -1379,7 +1380,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         for (int e = 0; e < C; ++e) sb[e] = o.sb[e];
         const int pi = 16 * t + ln;                     // the Gram columns' node i
         const float lgi = s_lg[pi];
-        const bool rhs_item = !KLDS && j == 1, diag = j == 0;
+        // (without k in LDS the diagonal item also forms the row's right-hand sides)
+        const bool diag = j == 0;
         // ---- products ----
         f32x4 gA[C], gB[C];    // diagonal item: X_tt, Y_tt Grams; else -X_ts, Y_ts Grams of its blocks
         {
@@ -1392,7 +1394,12 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             }
 #pragma unroll
             for (int e = 0; e < C; ++e) gA[e] = gB[e] = z;
-            if (rhs_item) {
+            if (diag) {
+#pragma unroll
+                for (int cs = 0; cs < 4; ++cs) {
+                    gA[0] = mfma32(kt[cs], kt[cs], gA[0]);     // lane (j, q): k_{4q+m} . k_j
+                    gB[0] = mfma32(kt[cs], o.qt[cs], gB[0]);   // lane (i, q): k_{4q+m} . q_i
+                }
                 if constexpr (!KLDS) {
                     // ---- the row's right-hand sides, for the four column groups ----
                     wait_ring(t);
@@ -1431,12 +1438,6 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                         ring16[slot_at(base + 8 + 2 * gg) * 32 + lane] = __builtin_bit_cast(u32x4, pc);
                     }
                 }
-            } else if (diag) {
-#pragma unroll
-                for (int cs = 0; cs < 4; ++cs) {
-                    gA[0] = mfma32(kt[cs], kt[cs], gA[0]);     // lane (j, q): k_{4q+m} . k_j
-                    gB[0] = mfma32(kt[cs], o.qt[cs], gB[0]);   // lane (i, q): k_{4q+m} . q_i
-                }
             } else {
 #pragma unroll
                 for (int cs = 0; cs < 4; ++cs)
@@ -1465,7 +1466,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
 #pragma unroll
             for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
             ring[slot_at(base + HDR + 2 * nts) * 64 + lane] = __builtin_bit_cast(uint2, yb);
-        } else if (!rhs_item) {
+        } else {
             // ---- -X_ts and Y_ts for C occupied blocks s ----
             const float bi = s_beta[pi];
             s16x4 xn[C], yv[C];
