@@ -168,7 +168,7 @@ def tree_of_depth(rng, n, depth):
     return parent
 
 
-@pytest.mark.parametrize("N", [200, 300])
+@pytest.mark.parametrize("N", [200, 300, 1000])
 def test_large_tree_depths(N):
     """The larger-tree path (one launch that checks the tree, builds its
     preorder and path log-gates by pointer doubling, whose round count follows
@@ -176,6 +176,8 @@ def test_large_tree_depths(N):
     powers of two, up to a chain."""
     rng = np.random.default_rng(900 + N)
     depths = [0, 1, 2, 3, 4, 7, 8, 9, 15, 16, 17, 63, 64, 65, 128, N - 1]
+    if N > 512:                                  # past the last rows of U kept in LDS
+        depths = [0, 1, 9, 16, 65, 128, 129, 255, 256, 300, 511, 512, 513, 700, N - 2, N - 1]
     parents = [tree_of_depth(rng, N, dd) for dd in depths]
     parent, lay = custom(901 + N, parents, 1, 2, 128)
     # accept node `depth`, the end of the chain: the longest committed path
@@ -224,7 +226,7 @@ def test_gate_and_beta_extremes():
     check_case(parent, accepted, lay, "bf16", 1, 1, name="beta=1")
 
 
-@pytest.mark.parametrize("N", [200, 300])
+@pytest.mark.parametrize("N", [200, 300, 1024])
 def test_chain_path_extremes(N):
     """Chains in the larger-tree kernel take the chunked recurrence (each
     16-node block row starts from the state at the node before it); a chain
@@ -309,11 +311,11 @@ def test_deterministic_and_non_ancestor_independent():
     assert np.array_equal(r3["S_commit"], r1["S_commit"])
 
 
-def test_invalid_trees_large():
-    """Tree errors on the path for 129 .. 512 nodes (found by the setup of the
-    single larger-tree launch, before it builds the preorder)."""
+@pytest.mark.parametrize("N", [200, 700])
+def test_invalid_trees_large(N):
+    """Tree errors on the path for 129 .. 1024 nodes (found by the setup of
+    the single larger-tree launch, before it builds the preorder)."""
     rng = np.random.default_rng(66)
-    N = 200
     good = W.tree_random_recursive(rng, N)
     bad1 = good.copy(); bad1[150] = 150         # self parent
     bad2 = good.copy(); bad2[130] = 199         # forward parent
@@ -370,7 +372,7 @@ def random_topological_order(rng, parent):
     return np.array(order, np.int64)
 
 
-@pytest.mark.parametrize("N", [64, 300, 512])
+@pytest.mark.parametrize("N", [64, 300, 512, 1000])
 def test_topological_relabel(N):
     """Re-ordering the caller's nodes into another topological order permutes
     o, u, the path log-gates, depths and ancestor rows, and leaves the

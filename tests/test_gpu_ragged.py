@@ -190,6 +190,7 @@ def test_ragged_tiled(N, Hk, Hv, sizes):
 @pytest.mark.parametrize("N,sizes", [
     (256, [256, 129, 0, 30, 200, 1, 5, 16]),         # chains of 129, 200, 16 and 1 nodes
     (512, [512, 300, 17, 0, 511, 40, 3, 9]),         # chains of 300, 511 and 9 nodes
+    (1024, [1024, 600, 0, 1023, 513, 130, 7, 1]),    # chains of 600, 513 and 1 nodes
 ])
 def test_ragged_large(N, sizes):
     rng = np.random.default_rng(310 + N)

@@ -1,5 +1,5 @@
 // verify_large.hip -- MFMA tree verification for d_k = d_v = 128, bf16
-// q/k/v/o and trees of 129 .. 16 * NB nodes (NB = 16 or 32 blocks of 16 nodes).
+// q/k/v/o and trees of 129 .. 16 * NB nodes (NB = 16, 32 or 64 blocks of 16 nodes).
 //
 // Same method as the small-tree kernel (page "Trees from Marginals:
 // Autoregressive drafting with factorized priors", section 3: the Gram matrix,
@@ -42,7 +42,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int kLargeMaxN = 512;      // largest tree of this path
+constexpr int kLargeMaxN = 1024;     // largest tree of this path
 constexpr int kLargeWaves = 12;
 constexpr int kLargeThreads = 64 * kLargeWaves;
 constexpr int kSolveWaves = 4;       // one 16-column group each: 64 columns per workgroup
@@ -97,7 +97,9 @@ struct LargeShape {
     static constexpr int NP = 16 * NB;
     static constexpr bool KLDS = NB <= 16;              // the k rows sit in LDS
     static constexpr int C = KLDS ? 2 : 1;              // occupied column blocks per producer item
-    static constexpr int WC = NP / 32;                  // words of a children row
+    // words of a children row (past 512 nodes there is no children table: a
+    // node's next sibling comes from a scan of the later nodes' parents)
+    static constexpr int WC = NB <= 32 ? NP / 32 : 0;
     static constexpr int SCRATCH = ((NP + 1) * WC + (NP + 2) + 8 * NP) * 4;   // the preorder's
     // A row's slots: when k is not in LDS, first its right-hand sides R_t and
     // e^G Q_t S0^T (fp32, two slots per column group each) and D_t (HDR
@@ -107,7 +109,11 @@ struct LargeShape {
     static constexpr int HDR = KLDS ? 0 : 17;
     static constexpr int NFIX = 1;                      // items of a row before its occupied blocks'
 
-    static constexpr int RING = NB <= 16 ? 84 : 112;    // 512-byte tile slots
+    static constexpr int RING = NB <= 16 ? 84 : NB <= 32 ? 112 : 156;   // 512-byte tile slots
+    // block rows of U kept in LDS by each solve wave: all of them up to 512
+    // nodes; past that the last UW, older rows re-read from the wave's own
+    // fp32 U stores
+    static constexpr int UW = NB <= 32 ? NB : 8;
     static constexpr int BIG = RING * 512 > SCRATCH ? RING * 512 : SCRATCH;
     // items: per row one for the diagonal block, without k in LDS one for the
     // right-hand sides, and one per C occupied blocks
@@ -132,12 +138,13 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     constexpr int HDR = L::HDR;
     constexpr int NFIX = L::NFIX;
     static_assert(2 * (NB - 1) + 1 + HDR <= RING && RING % 2 == 0, "a row's slots fit the ring");
-    static_assert(NB <= 32 && NB % 2 == 0, "block rows in one wave's lanes");
+    static_assert(NB <= 64 && NB % 2 == 0, "block rows in one wave's lanes");
+    constexpr int UW = L::UW;
     // the ring of tile slots (8 bytes per lane each); during the setup the
     // preorder's scratch
     __shared__ __attribute__((aligned(16))) uint2 s_big[BIG / 8];
     __shared__ __attribute__((aligned(16))) uint16_t s_k[KLDS ? NP * kD : 8];   // k rows, node order
-    __shared__ __attribute__((aligned(16))) uint2 s_u[NB][kSolveWaves][64];   // U_t, bf16 B operands
+    __shared__ __attribute__((aligned(16))) uint2 s_u[UW][kSolveWaves][64];   // U_t (t mod UW), bf16 B operands
     __shared__ __attribute__((aligned(16))) uint2 s_d[KLDS ? NB : 1][64];    // D_t, bf16 A operands (else in the ring)
     __shared__ __attribute__((aligned(16))) uint16_t s_s0[KLDS ? 8 : 64 * kD];   // the slice's S0 rows, bf16
     __shared__ __attribute__((aligned(16))) float s_xd[kProducers][256];     // each producer's X_tt, fp32 [col][row]
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         typedef const __attribute__((address_space(4))) uint32_t* cu32;
         typedef const __attribute__((address_space(4))) float* cf32;
         typedef const __attribute__((address_space(4))) int32_t* ci32;
-        int* s_path = reinterpret_cast<int*>(reinterpret_cast<char*>(s_big) + BIG) - kLargeMaxN;
+        int* s_path = reinterpret_cast<int*>(reinterpret_cast<char*>(s_big) + BIG) - NP;
         const int Wc = (N + 31) / 32;
         const int acc = ((ci32)c.accepted)[b];
         const SeqRows prow = seq_rows(c.offsets, b, N);
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             }
         }
         lds_barrier();
-        static_assert(64 * kD * 2 + kLargeMaxN * 4 <= BIG, "the path fits past the temporary S0 rows");
+        static_assert(64 * kD * 2 + NP * 4 <= BIG, "the path fits past the temporary S0 rows");
         const int plen = s_more[0];
         if (!solver || plen <= 0) request_k();
         if (h == 0 && slice == 0) {
@@ -517,10 +524,33 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     for (int i = tid; i < nt; i += NT) {                // bit i of its parent's children row; first child
         const int p = s_jump[i];
         const int pr = p < 0 ? NP : p;
-        atomicOr(&s_cm[pr * WC + (i >> 5)], 1u << (i & 31));
+        if constexpr (WC > 0) atomicOr(&s_cm[pr * WC + (i >> 5)], 1u << (i & 31));
         atomicMin(&s_fc[pr], i);
     }
     lds_barrier();
+    if constexpr (WC == 0) {
+        // next sibling by a scan of the later nodes' parents, four at a time:
+        // a wave's lanes hold consecutive nodes and read the same words (one
+        // broadcast each); the scan ends once every lane has its sibling
+        for (int i0 = tid - lane; i0 < nt; i0 += NT) {
+            const int i = i0 + lane;
+            const int p = i < nt ? s_jump[i] : -2;
+            bool pend = i < nt;
+            int nsib = -1;
+            for (int j = i0; j < nt; j += 4) {
+                if (__builtin_amdgcn_ballot_w64(pend) == 0) break;
+                const int4 x4 = *reinterpret_cast<const int4*>(&s_jump[j]);
+                const int pj[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool hit = pend && j + e > i && j + e < nt && pj[e] == p;
+                    nsib = hit ? j + e : nsib;
+                    pend = pend && !hit;
+                }
+            }
+            if (i < nt) s_na[i] = make_int2(nsib >= 0 ? nsib : (p < 0 ? n : -1), p);
+        }
+    } else
     for (int i = tid; i < nt; i += NT) {                // next sibling, else pending
         // (the parent's whole children row is read at once: no dependent
         // loads however far the next sibling is)
@@ -546,10 +576,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         }
         s_na[i] = make_int2(nsib >= 0 ? nsib : (p < 0 ? n : -1), p);
     }
-    static_assert(NP <= NT, "one tree entry per thread");
-    if (nt && tid < NP) {
-        const int j = s_jump[tid];
-        s_gj[tid] = make_int2((j & 0xffff) | ((int)s_hop[tid] << 16), __float_as_int(s_lg[tid]));
+    for (int i = tid; nt && i < NP; i += NT) {
+        const int j = s_jump[i];
+        s_gj[i] = make_int2((j & 0xffff) | ((int)s_hop[i] << 16), __float_as_int(s_lg[i]));
     }
     lds_barrier();
     // Pointer jumping, one node per thread and one barrier per round.  The
@@ -569,7 +598,6 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         return s_more[rd % 3] != 0;
     };
     if (nt) {
-        const int i = tid;
         int rd = 0;                                     // rounds so far, both loops
         // (1) the node after each subtree: the subtree root's next sibling,
         // else its parent's (a root-level node always has one); the link is
@@ -578,6 +606,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         // its link's sums and jumps to the link's link.
         for (;; ++rd) {
             bool more = false;
+#pragma unroll
+            for (int k = 0; k < PL; ++k) {
+            const int i = tid + k * NT;
             if (i < nt) {
                 const int2 a = s_na[i];
                 if (a.x < 0) {
@@ -600,18 +631,23 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 }
                 s_gj[((rd + 1) & 1) * NP + i] = r;
             }
+            }
             if (!round_more(rd, more)) {
-                if (i < NP) {                           // the last round's copy
-                    const int2 a = s_gj[((rd + 1) & 1) * NP + i];
-                    s_lg[i] = __int_as_float(a.y);
-                    s_hop[i] = (int16_t)(a.x >> 16);
+#pragma unroll
+                for (int k = 0; k < PL; ++k) {
+                    const int i = tid + k * NT;
+                    if (i < NP) {                       // the last round's copy
+                        const int2 a = s_gj[((rd + 1) & 1) * NP + i];
+                        s_lg[i] = __int_as_float(a.y);
+                        s_hop[i] = (int16_t)(a.x >> 16);
+                    }
                 }
                 break;
             }
         }
         // preorder successor: the first child, else the node after; then each
         // node's distance to the list's end (list ranking)
-        if (i < nt) {
+        for (int i = tid; i < nt; i += NT) {
             const int f = s_fc[i];
             const int sc = f < NP ? f : s_na[i].x;
             s_rs[i] = make_int2(sc < n ? 1 : 0, sc);
@@ -619,7 +655,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         lds_barrier();
         for (++rd;; ++rd) {
             bool more = false;
-            if (i < nt) {
+            for (int i = tid; i < nt; i += NT) {
                 const int2 a = s_rs[i];
                 if (a.y < n) {
                     const int2 b = s_rs[a.y];
@@ -629,7 +665,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             }
             if (!round_more(rd, more)) break;
         }
-        if (i < nt) {                                   // position n - 1 - rank
+        for (int i = tid; i < nt; i += NT) {            // position n - 1 - rank
             const int pi = min(max(n - 1 - s_rs[i].x, 0), n - 1);
             const int nx = s_na[i].x;
             s_perm[pi] = (uint16_t)i;
@@ -648,20 +684,29 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         }
         // a chain's path log-gates are prefix sums: a scan within each wave
         // (lane shifts) and the preceding waves' totals
-        static_assert(NP <= NT, "one chain node per thread");
-        float x = tid < NP ? s_lg[tid] : 0.f;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float y = __shfl_up(x, d);
-            if (lane >= d) x += y;
-        }
+        // (PL chunks of NT nodes, the chunks' wave sums in order)
+        float x[PL];
         float* wsum = reinterpret_cast<float*>(s_big);
-        if (lane == 63) wsum[wave] = x;
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const int i = tid + k * NT;
+            x[k] = i < NP ? s_lg[i] : 0.f;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const float y = __shfl_up(x[k], d);
+                if (lane >= d) x[k] += y;
+            }
+            if (lane == 63) wsum[k * kLargeWaves + wave] = x[k];
+        }
         lds_barrier();
-        for (int w = 0; w < wave; ++w) x += wsum[w];
-        if (tid < NP) {
-            s_lg[tid] = x;
-            s_hop[tid] = (int16_t)(tid < n ? tid + 1 : 0);
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const int i = tid + k * NT;
+            for (int w = 0; w < k * kLargeWaves + wave; ++w) x[k] += wsum[w];
+            if (i < NP) {
+                s_lg[i] = x[k];
+                s_hop[i] = (int16_t)(i < n ? i + 1 : 0);
+            }
         }
     }
     if constexpr (KLDS) {
@@ -700,11 +745,15 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         }
         pk[j] = v;
     }
-    if (nt && tid < NP) {                               // (a max over each block's 16 lanes)
-        int m = s_last[tid];
 #pragma unroll
-        for (int d = 8; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d));
-        if ((tid & 15) == 0) s_mlast[tid >> 4] = m;
+    for (int k = 0; k < PL; ++k) {                      // (a max over each block's 16 lanes)
+        const int i = tid + k * NT;
+        if (nt && i < NP) {
+            int m = s_last[i];
+#pragma unroll
+            for (int d = 8; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d));
+            if ((i & 15) == 0) s_mlast[i >> 4] = m;
+        }
     }
     if (slice == 0)
         for (int i = tid; i < n; i += NT) a.log_gamma[((size_t)b * Hv + h) * N + i] = s_lg[i];
@@ -758,22 +807,19 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // Prefix sums over the rows go through LDS (one read of all rows' words).
     // (A chain takes none of it.)
     if (wave == 0 && nt) {
-        int ml[NB];
+        uint64_t occ = 0u;
 #pragma unroll
         for (int sb = 0; sb < NB; sb += 4) {
             const int4 x4 = *reinterpret_cast<const int4*>(&s_mlast[sb]);
-            ml[sb] = x4.x;
-            ml[sb + 1] = x4.y;
-            ml[sb + 2] = x4.z;
-            ml[sb + 3] = x4.w;
-        }
-        uint32_t occ = 0u;
+            const int ml[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
-        for (int sb = 0; sb < NB; ++sb) occ |= (sb < lane && lane < nblk && ml[sb] >= 16 * lane) ? 1u << sb : 0u;
-        const int tn = __popc(occ);
+            for (int e = 0; e < 4; ++e)
+                occ |= (sb + e < lane && lane < nblk && ml[e] >= 16 * lane) ? 1ull << (sb + e) : 0ull;
+        }
+        const int tn = __popcll(occ);
         if (lane < NB) {
             s_tn[lane] = tn;
-            for (int k = 0; occ; ++k, occ &= occ - 1u) s_tcol[lane][k] = (uint8_t)__builtin_ctz(occ);
+            for (int k = 0; occ; ++k, occ &= occ - 1u) s_tcol[lane][k] = (uint8_t)__builtin_ctzll(occ);
         }
         const int sl = lane < nblk ? 2 * tn + 1 + HDR : 0;
         const int ni = lane < nblk ? NFIX + (tn + C - 1) / C : 0;
@@ -789,10 +835,11 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             ex += (r < lane ? x4.x : 0) + (r + 1 < lane ? x4.y : 0) + (r + 2 < lane ? x4.z : 0) +
                   (r + 3 < lane ? x4.w : 0);
         }
-        const int gsl = ex & 0xffff;                    // first slot of row lane; lane NB: the total
-        const int ib = ex >> 16;                        // first item of row lane; lane NB: the total
+        const int gsl = ex & 0xffff;                    // first slot of row lane
+        const int ib = ex >> 16;                        // first item of row lane
         const int target = gsl + sl - RING;             // rows starting below it must be released
-        if (lane <= NB) s_gslot[lane] = gsl;
+        if (lane < NB) s_gslot[lane] = gsl;
+        if (lane == NB - 1) s_gslot[NB] = gsl + sl;     // the total
         int cnt = 0;
 #pragma unroll
         for (int r = 0; r < NB; r += 4) {
@@ -802,7 +849,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         }
         if (lane < NB) s_rstar[lane] = cnt;
         for (int j = 0; j < ni; ++j) s_items[ib + j] = (uint16_t)(lane | (j << 8));
-        if (lane == NB) s_nitems = ib;
+        if (lane == NB - 1) s_nitems = ib + ni;
     }
     lds_barrier();
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -899,8 +946,12 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // chain).
     if (nt == 0) {
         constexpr int CR = 4;                           // ring rows; row t uses entry t % CR
-        uint2* const dtab = s_big;                      // D_t at slot t (A operand)
-        uint2* const ytab = s_big + 64 * NB;            // Y_tt at slot t (B operand)
+        // D_t (A operand) and Y_tt (B operand) at slot t, past 512 nodes at
+        // slot t % CR (written once the entry is free)
+        constexpr int DT = NB <= 32 ? NB : CR;
+        auto dslot = [&](int t) __attribute__((always_inline)) { return NB <= 32 ? t : t % CR; };
+        uint2* const dtab = s_big;
+        uint2* const ytab = s_big + 64 * DT;
         // entry r: v of the slice's 64 columns ([node][column], 2 KB), then
         // per node (beta, beta e^(G - E_t), e^(G - E_t), e^(E_(t+1) - G)) and
         // e^(E_(t+1) - E_t), in 2.5 KB, in the ring area; the K^T tiles (tile
@@ -908,14 +959,15 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         // operand) in s_u; q and k rows as s_k (16 x 128, swizzled), q in
         // the ring area with k in LDS, else both in s_u
         constexpr int VE = 5 * 256;                     // halfwords per entry in the ring area
-        uint16_t* const vring = reinterpret_cast<uint16_t*>(s_big + 64 * 2 * NB);
+        uint16_t* const vring = reinterpret_cast<uint16_t*>(s_big + 64 * 2 * DT);
         constexpr int KNE = 2 * 16 * kD;                // halfwords of an entry's K^T tiles
         constexpr int QE = KNE + (KLDS ? 0 : 2 * 16 * kD);   // halfwords per entry in s_u
-        uint16_t* const qring = reinterpret_cast<uint16_t*>(&s_u[0][0][0]);
+        // (past 512 nodes in the ring area, after the v entries)
+        uint16_t* const qring = NB <= 32 ? reinterpret_cast<uint16_t*>(&s_u[0][0][0]) : vring + CR * VE;
         uint16_t* const qring2 = vring + CR * VE;       // (with k in LDS)
-        static_assert(2 * NB * 512 + CR * VE * 2 + (KLDS ? CR * 16 * kD * 2 : 0) <= BIG,
+        static_assert(2 * DT * 512 + CR * VE * 2 + (KLDS ? CR * 16 * kD * 2 : 0) + (NB <= 32 ? 0 : CR * QE * 2) <= BIG,
                       "chain tables and ring entries fit the ring area");
-        static_assert(NB * kSolveWaves * 512 >= CR * QE * 2, "ring entries fit s_u");
+        static_assert(NB > 32 || UW * kSolveWaves * 512 >= CR * QE * 2, "ring entries fit s_u");
         auto vent = [&](int r) __attribute__((always_inline)) { return vring + r * VE; };
         auto fent = [&](int r) __attribute__((always_inline)) { return reinterpret_cast<float*>(vring + r * VE + 16 * 64); };
         auto knent = [&](int r) __attribute__((always_inline)) { return qring + r * QE; };
@@ -953,10 +1005,13 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 s16x4 yb;
                 diag_block(t, p, gK, gQ, accd, yb);
                 const int c = lane >> 2, qd = lane & 3;
-                uint16_t* dd = reinterpret_cast<uint16_t*>(dtab + 64 * t);
+                auto put_dy = [&]() __attribute__((always_inline)) {
+                    uint16_t* dd = reinterpret_cast<uint16_t*>(dtab + 64 * dslot(t));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
-                ytab[64 * t + lane] = __builtin_bit_cast(uint2, yb);
+                    for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
+                    ytab[64 * dslot(t) + lane] = __builtin_bit_cast(uint2, yb);
+                };
+                if constexpr (NB <= 32) put_dy();
                 // K_t^T tiles (tile 2 w + hh: its keys by the row's nodes), exact products
                 s16x4 kn[8];
 #pragma unroll
@@ -976,6 +1031,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 if (t >= CR)
 #pragma unroll
                     for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_oready[gg], t - CR + 1);
+                if constexpr (NB > 32) put_dy();
 #pragma unroll
                 for (int cs = 0; cs < 4; ++cs) {
                     *reinterpret_cast<u32x4*>(qent(r) + row_chunk(ln, 4 * cs + lq)) = __builtin_bit_cast(u32x4, o.qt[cs]);
@@ -1078,8 +1134,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             f32x4 acc;
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[m] = fn[m].x * vd[m] - fn[m].y * ks[m];
-            const s16x4 dt = __builtin_bit_cast(s16x4, dtab[64 * t + lane]);
-            const s16x4 ytt = __builtin_bit_cast(s16x4, ytab[64 * t + lane]);
+            const s16x4 dt = __builtin_bit_cast(s16x4, dtab[64 * dslot(t) + lane]);
+            const s16x4 ytt = __builtin_bit_cast(s16x4, ytab[64 * dslot(t) + lane]);
             s16x4 hi, lo;
             split4(acc, hi, lo);
             const f32x4 uf = mfma32(cat(dt, dt), cat(hi, lo), z);   // lane (c, q): nodes 4q + m, column c
@@ -1169,6 +1225,26 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         // unused ones skipped by uniform branches; rows with more take a loop.
         constexpr int SB = 8;
         constexpr int TW = NB / 4;                      // words of a row of s_tcol
+        // U_sb as the B operand of row t: from LDS when kept there; past 512
+        // nodes a block more than UW rows back is re-read from this lane's
+        // own fp32 stores of it (rows 4q .. 4q+3 of column c0 + n, past L1),
+        // rounded as LDS keeps it, and positions past the tree read as zero
+        auto uget = [&](int sb, int t) __attribute__((always_inline)) {
+            if constexpr (NB <= 32) {
+                return __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
+            } else {
+                if (sb + UW > t) return __builtin_bit_cast(s16x4, s_u[sb % UW][g][lane]);
+                f32x4 x;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int i = 16 * sb + 4 * lq + m;
+                    const int off = (node_at(i) * kD + c0 + ln) * 4;
+                    const float y = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(u_rsrc, off, 0, 1));
+                    x[m] = i < n ? y : 0.f;
+                }
+                return to_bf16x4(x);
+            }
+        };
         auto row = [&](int t, RowOps& r) __attribute__((always_inline)) {
             const int nts = __builtin_amdgcn_readfirstlane(s_tn[t]);
             const int base = __builtin_amdgcn_readfirstlane(s_gslot[t]) % RING;
@@ -1185,7 +1261,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
 #pragma unroll
             for (int e = 0; e < SB; ++e) {
                 const int sb = e < nts ? (int)((tw[e >> 2] >> (8 * (e & 3))) & 0xffu) : t;
-                ub[e] = __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
+                ub[e] = uget(sb, t);
             }
             f32x4 acc, oc;
             if constexpr (KLDS) {
@@ -1250,7 +1326,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 for (int e = 0; e < SB; ++e) {
                     const int m = m0 + e;
                     const int sb = m < nts ? __builtin_amdgcn_readfirstlane((int)s_tcol[t][m]) : t;
-                    ub[e] = __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
+                    ub[e] = uget(sb, t);
                     xa[e] = __builtin_bit_cast(s16x4, ring[slot_at(xb + m) * 64 + lane]);
                     ya[e] = __builtin_bit_cast(s16x4, ring[slot_at(xb + nts + m) * 64 + lane]);
                 }
@@ -1271,7 +1347,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             split4(acc, hi, lo);
             const f32x4 uf = mfma16(dt, lo, mfma16(dt, hi, z));
             const s16x4 ut = to_bf16x4(uf);
-            s_u[t][g][lane] = __builtin_bit_cast(uint2, ut);
+            s_u[NB <= 32 ? t : t % UW][g][lane] = __builtin_bit_cast(uint2, ut);
             // the cache row: lane (n, q) holds rows 4q .. 4q+3 of column n;
             // positions past the tree store outside the buffer and are dropped
 #pragma unroll
@@ -1526,8 +1602,9 @@ hipError_t launch_large(const VerifyArgs& a, const CommitArgs* c, hipStream_t st
     // 8 workgroups apart, so both run on one XCD
     int units = a.B * a.Hv;
     const unsigned grid = 16u * (unsigned)((units + 7) / 8);
-    const void* fn = a.N <= 256 ? (c ? (const void*)verify_large_kernel<16, true> : (const void*)verify_large_kernel<16, false>)
-                                : (c ? (const void*)verify_large_kernel<32, true> : (const void*)verify_large_kernel<32, false>);
+    const void* fn = a.N <= 256   ? (c ? (const void*)verify_large_kernel<16, true> : (const void*)verify_large_kernel<16, false>)
+                     : a.N <= 512 ? (c ? (const void*)verify_large_kernel<32, true> : (const void*)verify_large_kernel<32, false>)
+                                  : (c ? (const void*)verify_large_kernel<64, true> : (const void*)verify_large_kernel<64, false>);
     void* args[] = {&copy, &ccopy, &units};
     return hipLaunchKernel(fn, dim3(grid), dim3(kLargeThreads), args, 0, stream);
 }

@@ -93,6 +93,11 @@ WORKLOADS: Dict[str, Spec] = {
     # 8 sequences, 16 heads, 512-node random recursive trees, beta toward 1.
     "rrt512_b8": Spec("rrt512_b8", 8, 512, 16, 16, 128, "bf16", 1, "rrt", 5,
                       beta_mu=2.0),
+    # The same two shapes at the largest supported tree, 1024 nodes.
+    "chain1024_b8": Spec("chain1024_b8", 8, 1024, 16, 16, 128, "bf16", 1, "chain", 7,
+                         beta_mu=2.0),
+    "rrt1024_b8": Spec("rrt1024_b8", 8, 1024, 16, 16, 128, "bf16", 1, "rrt", 8,
+                       beta_mu=2.0),
 }
 
 
