@@ -111,9 +111,9 @@ struct LargeShape {
 
     static constexpr int RING = NB <= 16 ? 84 : NB <= 32 ? 112 : 156;   // 512-byte tile slots
     // block rows of U kept in LDS by each solve wave: all of them up to 512
-    // nodes; past that the last UW, older rows re-read from the wave's own
-    // fp32 U stores
-    static constexpr int UW = NB <= 32 ? NB : 8;
+    // nodes; past that UW slots, each held from its row until the last row
+    // that reads it
+    static constexpr int UW = NB <= 32 ? NB : 15;
     static constexpr int BIG = RING * 512 > SCRATCH ? RING * 512 : SCRATCH;
     // items: per row one for the diagonal block, without k in LDS one for the
     // right-hand sides, and one per C occupied blocks
@@ -144,7 +144,8 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     // preorder's scratch
     __shared__ __attribute__((aligned(16))) uint2 s_big[BIG / 8];
     __shared__ __attribute__((aligned(16))) uint16_t s_k[KLDS ? NP * kD : 8];   // k rows, node order
-    __shared__ __attribute__((aligned(16))) uint2 s_u[UW][kSolveWaves][64];   // U_t (t mod UW), bf16 B operands
+    __shared__ __attribute__((aligned(16))) uint2 s_u[UW][kSolveWaves][64];   // U_t, bf16 B operands
+    __shared__ int s_uslot[NB > 32 ? NB : 1];           // (past 512 nodes) row t's slot of s_u, -1: none
     __shared__ __attribute__((aligned(16))) uint2 s_d[KLDS ? NB : 1][64];    // D_t, bf16 A operands (else in the ring)
     __shared__ __attribute__((aligned(16))) uint16_t s_s0[KLDS ? 8 : 64 * kD];   // the slice's S0 rows, bf16
     __shared__ __attribute__((aligned(16))) float s_xd[kProducers][256];     // each producer's X_tt, fp32 [col][row]
@@ -484,6 +485,12 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     }
     for (int x = tid; x < (NP + 1) * WC; x += NT) s_cm[x] = 0u;
     for (int x = tid; x <= NP; x += NT) s_fc[x] = NP;
+    // (without the children table: per parent, NP for the roots, its number
+    // of children, then where they start in a list of the nodes by parent;
+    // before the pointer jumping, in its area)
+    int* const s_cnt = reinterpret_cast<int*>(s_gj);    // [NP + 2]
+    if constexpr (WC == 0)
+        for (int x = tid; x <= NP + 1; x += NT) s_cnt[x] = 0;
     if (tid < NB) s_done[tid] = 0;
     if (tid == 0) s_claim = 0;
     if (tid < kSolveWaves) s_oready[tid] = 0;
@@ -521,36 +528,82 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         o.vt[0] = *reinterpret_cast<const u32x4*>(vr);
         o.vt[1] = *reinterpret_cast<const u32x4*>(vr + 8);
     };
+    if constexpr (WC == 0) {
+        // Next siblings from a counting sort of the nodes by parent: each
+        // node takes a place in its parent's bucket in any order, then its
+        // rank by index among the bucket's nodes (all of which read the
+        // bucket's same words) fixes the order; the next sibling is the
+        // bucket's next node.
+        int* const s_tmp = s_cnt + NP + 2;              // [NP] nodes by parent, any order
+        int* const s_srt = s_tmp + NP;                  // [NP] nodes by parent, ascending
+        int* const s_ws = reinterpret_cast<int*>(s_rs); // the scan's wave totals
+        static_assert(3 * NP + 2 <= 4 * NP, "the sort fits the pointer-jumping area");
+        int slot[PL], pp[PL];
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const int i = tid + k * NT;
+            pp[k] = NP;
+            slot[k] = 0;
+            if (i < nt) {
+                const int p = s_jump[i];
+                pp[k] = p < 0 ? NP : p;
+                slot[k] = atomicAdd(&s_cnt[pp[k]], 1);
+                atomicMin(&s_fc[pp[k]], i);
+            }
+        }
+        lds_barrier();
+        {                                               // bucket starts: two buckets per thread
+            const int x0 = 2 * tid;
+            const int c0 = x0 <= NP ? s_cnt[x0] : 0, c1 = x0 + 1 <= NP ? s_cnt[x0 + 1] : 0;
+            int incl = c0 + c1;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(incl, d);
+                if (lane >= d) incl += y;
+            }
+            if (lane == 63) s_ws[wave] = incl;
+            lds_barrier();
+            int before = incl - c0 - c1;
+            for (int w = 0; w < wave; ++w) before += s_ws[w];
+            if (x0 <= NP + 1) s_cnt[x0] = before;       // (entry NP + 1: the total)
+            if (x0 + 1 <= NP + 1) s_cnt[x0 + 1] = before + c0;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const int i = tid + k * NT;
+            if (i < nt) s_tmp[s_cnt[pp[k]] + slot[k]] = i;
+        }
+        lds_barrier();
+        int b0[PL], b1[PL], rk[PL];
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const int i = tid + k * NT;
+            b0[k] = s_cnt[pp[k]];
+            b1[k] = s_cnt[pp[k] + 1];
+            rk[k] = 0;
+            if (i < nt) {
+                for (int x = b0[k]; x < b1[k]; ++x) rk[k] += s_tmp[x] < i ? 1 : 0;
+                s_srt[b0[k] + rk[k]] = i;
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+            const int i = tid + k * NT;
+            if (i < nt) {
+                const int nsib = b0[k] + rk[k] + 1 < b1[k] ? s_srt[b0[k] + rk[k] + 1] : -1;
+                s_na[i] = make_int2(nsib >= 0 ? nsib : (pp[k] == NP ? n : -1), pp[k] == NP ? -1 : pp[k]);
+            }
+        }
+    } else {
     for (int i = tid; i < nt; i += NT) {                // bit i of its parent's children row; first child
         const int p = s_jump[i];
         const int pr = p < 0 ? NP : p;
-        if constexpr (WC > 0) atomicOr(&s_cm[pr * WC + (i >> 5)], 1u << (i & 31));
+        atomicOr(&s_cm[pr * WC + (i >> 5)], 1u << (i & 31));
         atomicMin(&s_fc[pr], i);
     }
     lds_barrier();
-    if constexpr (WC == 0) {
-        // next sibling by a scan of the later nodes' parents, four at a time:
-        // a wave's lanes hold consecutive nodes and read the same words (one
-        // broadcast each); the scan ends once every lane has its sibling
-        for (int i0 = tid - lane; i0 < nt; i0 += NT) {
-            const int i = i0 + lane;
-            const int p = i < nt ? s_jump[i] : -2;
-            bool pend = i < nt;
-            int nsib = -1;
-            for (int j = i0; j < nt; j += 4) {
-                if (__builtin_amdgcn_ballot_w64(pend) == 0) break;
-                const int4 x4 = *reinterpret_cast<const int4*>(&s_jump[j]);
-                const int pj[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool hit = pend && j + e > i && j + e < nt && pj[e] == p;
-                    nsib = hit ? j + e : nsib;
-                    pend = pend && !hit;
-                }
-            }
-            if (i < nt) s_na[i] = make_int2(nsib >= 0 ? nsib : (p < 0 ? n : -1), p);
-        }
-    } else
     for (int i = tid; i < nt; i += NT) {                // next sibling, else pending
         // (the parent's whole children row is read at once: no dependent
         // loads however far the next sibling is)
@@ -575,6 +628,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             nsib = x ? lo + __builtin_ctz(x) : nsib;
         }
         s_na[i] = make_int2(nsib >= 0 ? nsib : (p < 0 ? n : -1), p);
+    }
     }
     for (int i = tid; nt && i < NP; i += NT) {
         const int j = s_jump[i];
@@ -850,6 +904,25 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         if (lane < NB) s_rstar[lane] = cnt;
         for (int j = 0; j < ni; ++j) s_items[ib + j] = (uint16_t)(lane | (j << 8));
         if (lane == NB - 1) s_nitems = ib + ni;
+    }
+    if constexpr (NB > 32) {
+        // (meanwhile, past 512 nodes) the slots of s_u: block row t is read
+        // by the rows up to the one holding its last descendant; rows take
+        // slots in order, each the lowest one whose holder's last reader has
+        // passed, and a row that finds none is re-read from its U stores
+        if (wave == 1 && nt) {
+            const int ml = lane < NB ? s_mlast[lane] : 0;   // (row t's from lane t)
+            int hold = -1;                              // lane x < UW: last reader of slot x's row
+            int mine = -1;                              // lane t: row t's slot
+            for (int t = 0; t < nblk; ++t) {
+                const int endt = max(t, min(__builtin_amdgcn_readlane(ml, t) >> 4, nblk - 1));
+                const uint64_t fr = __builtin_amdgcn_ballot_w64(lane < UW && hold < t);
+                const int x = fr ? (int)__builtin_ctzll(fr) : -1;
+                if (lane == x) hold = endt;
+                if (lane == t) mine = x;
+            }
+            if (lane < NB) s_uslot[lane] = mine;
+        }
     }
     lds_barrier();
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -1225,15 +1298,17 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         // unused ones skipped by uniform branches; rows with more take a loop.
         constexpr int SB = 8;
         constexpr int TW = NB / 4;                      // words of a row of s_tcol
-        // U_sb as the B operand of row t: from LDS when kept there; past 512
-        // nodes a block more than UW rows back is re-read from this lane's
-        // own fp32 stores of it (rows 4q .. 4q+3 of column c0 + n, past L1),
-        // rounded as LDS keeps it, and positions past the tree read as zero
+        // U_sb as the B operand of row t (sb = t: an unused entry): from LDS
+        // when kept there; past 512 nodes a row without a slot is re-read
+        // from this lane's own fp32 stores of it (rows 4q .. 4q+3 of column
+        // c0 + n, past L1), rounded as LDS keeps it, and positions past the
+        // tree read as zero
         auto uget = [&](int sb, int t) __attribute__((always_inline)) {
             if constexpr (NB <= 32) {
                 return __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
             } else {
-                if (sb + UW > t) return __builtin_bit_cast(s16x4, s_u[sb % UW][g][lane]);
+                const int us = __builtin_amdgcn_readfirstlane(s_uslot[sb]);
+                if (us >= 0 || sb == t) return __builtin_bit_cast(s16x4, s_u[max(us, 0)][g][lane]);
                 f32x4 x;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -1347,7 +1422,12 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             split4(acc, hi, lo);
             const f32x4 uf = mfma16(dt, lo, mfma16(dt, hi, z));
             const s16x4 ut = to_bf16x4(uf);
-            s_u[NB <= 32 ? t : t % UW][g][lane] = __builtin_bit_cast(uint2, ut);
+            if constexpr (NB <= 32) {
+                s_u[t][g][lane] = __builtin_bit_cast(uint2, ut);
+            } else {
+                const int x = __builtin_amdgcn_readfirstlane(s_uslot[t]);
+                if (x >= 0) s_u[x][g][lane] = __builtin_bit_cast(uint2, ut);
+            }
             // the cache row: lane (n, q) holds rows 4q .. 4q+3 of column n;
             // positions past the tree store outside the buffer and are dropped
 #pragma unroll
