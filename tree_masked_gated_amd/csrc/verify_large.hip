@@ -1303,11 +1303,12 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         // from this lane's own fp32 stores of it (rows 4q .. 4q+3 of column
         // c0 + n, past L1), rounded as LDS keeps it, and positions past the
         // tree read as zero
+        const int slotv = NB > 32 && lane < NB ? s_uslot[min(lane, NB - 1)] : -1;   // lane t: row t's slot
         auto uget = [&](int sb, int t) __attribute__((always_inline)) {
             if constexpr (NB <= 32) {
                 return __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
             } else {
-                const int us = __builtin_amdgcn_readfirstlane(s_uslot[sb]);
+                const int us = __builtin_amdgcn_readlane(slotv, sb);
                 if (us >= 0 || sb == t) return __builtin_bit_cast(s16x4, s_u[max(us, 0)][g][lane]);
                 f32x4 x;
 #pragma unroll
@@ -1425,7 +1426,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             if constexpr (NB <= 32) {
                 s_u[t][g][lane] = __builtin_bit_cast(uint2, ut);
             } else {
-                const int x = __builtin_amdgcn_readfirstlane(s_uslot[t]);
+                const int x = __builtin_amdgcn_readlane(slotv, t);
                 if (x >= 0) s_u[x][g][lane] = __builtin_bit_cast(uint2, ut);
             }
             // the cache row: lane (n, q) holds rows 4q .. 4q+3 of column n;
