@@ -109,11 +109,11 @@ struct LargeShape {
     static constexpr int HDR = KLDS ? 0 : 17;
     static constexpr int NFIX = 1;                      // items of a row before its occupied blocks'
 
-    static constexpr int RING = NB <= 16 ? 84 : NB <= 32 ? 112 : 156;   // 512-byte tile slots
+    static constexpr int RING = NB <= 16 ? 84 : NB <= 32 ? 112 : 184;   // 512-byte tile slots
     // block rows of U kept in LDS by each solve wave: all of them up to 512
     // nodes; past that UW slots, each held from its row until the last row
-    // that reads it
-    static constexpr int UW = NB <= 32 ? NB : 15;
+    // that reads it (so that the ring takes the rest)
+    static constexpr int UW = NB <= 32 ? NB : 8;
     static constexpr int BIG = RING * 512 > SCRATCH ? RING * 512 : SCRATCH;
     // items: per row one for the diagonal block, without k in LDS one for the
     // right-hand sides, and one per C occupied blocks
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     __shared__ __attribute__((aligned(16))) uint2 s_big[BIG / 8];
     __shared__ __attribute__((aligned(16))) uint16_t s_k[KLDS ? NP * kD : 8];   // k rows, node order
     __shared__ __attribute__((aligned(16))) uint2 s_u[UW][kSolveWaves][64];   // U_t, bf16 B operands
-    __shared__ int s_uslot[NB > 32 ? NB : 1];           // (past 512 nodes) row t's slot of s_u, -1: none
+    __shared__ int s_uslot[UW < NB ? NB : 1];          // (with slots) row t's slot of s_u, -1: none
     __shared__ __attribute__((aligned(16))) uint2 s_d[KLDS ? NB : 1][64];    // D_t, bf16 A operands (else in the ring)
     __shared__ __attribute__((aligned(16))) uint16_t s_s0[KLDS ? 8 : 64 * kD];   // the slice's S0 rows, bf16
     __shared__ __attribute__((aligned(16))) float s_xd[kProducers][256];     // each producer's X_tt, fp32 [col][row]
@@ -905,7 +905,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         for (int j = 0; j < ni; ++j) s_items[ib + j] = (uint16_t)(lane | (j << 8));
         if (lane == NB - 1) s_nitems = ib + ni;
     }
-    if constexpr (NB > 32) {
+    if constexpr (UW < NB) {
         // (meanwhile, past 512 nodes) the slots of s_u: block row t is read
         // by the rows up to the one holding its last descendant; rows take
         // slots in order, each the lowest one whose holder's last reader has
@@ -1020,9 +1020,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
     if (nt == 0) {
         constexpr int CR = 4;                           // ring rows; row t uses entry t % CR
         // D_t (A operand) and Y_tt (B operand) at slot t, past 512 nodes at
-        // slot t % CR (written once the entry is free)
-        constexpr int DT = NB <= 32 ? NB : CR;
-        auto dslot = [&](int t) __attribute__((always_inline)) { return NB <= 32 ? t : t % CR; };
+        // slot t % DT (written once the solve waves are done with row t - DT)
+        constexpr int DT = UW == NB ? NB : 2 * CR;
+        auto dslot = [&](int t) __attribute__((always_inline)) { return UW == NB ? t : t % DT; };
         uint2* const dtab = s_big;
         uint2* const ytab = s_big + 64 * DT;
         // entry r: v of the slice's 64 columns ([node][column], 2 KB), then
@@ -1036,11 +1036,11 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         constexpr int KNE = 2 * 16 * kD;                // halfwords of an entry's K^T tiles
         constexpr int QE = KNE + (KLDS ? 0 : 2 * 16 * kD);   // halfwords per entry in s_u
         // (past 512 nodes in the ring area, after the v entries)
-        uint16_t* const qring = NB <= 32 ? reinterpret_cast<uint16_t*>(&s_u[0][0][0]) : vring + CR * VE;
+        uint16_t* const qring = UW == NB ? reinterpret_cast<uint16_t*>(&s_u[0][0][0]) : vring + CR * VE;
         uint16_t* const qring2 = vring + CR * VE;       // (with k in LDS)
-        static_assert(2 * DT * 512 + CR * VE * 2 + (KLDS ? CR * 16 * kD * 2 : 0) + (NB <= 32 ? 0 : CR * QE * 2) <= BIG,
+        static_assert(2 * DT * 512 + CR * VE * 2 + (KLDS ? CR * 16 * kD * 2 : 0) + (UW == NB ? 0 : CR * QE * 2) <= BIG,
                       "chain tables and ring entries fit the ring area");
-        static_assert(NB > 32 || UW * kSolveWaves * 512 >= CR * QE * 2, "ring entries fit s_u");
+        static_assert(UW < NB || UW * kSolveWaves * 512 >= CR * QE * 2, "ring entries fit s_u");
         auto vent = [&](int r) __attribute__((always_inline)) { return vring + r * VE; };
         auto fent = [&](int r) __attribute__((always_inline)) { return reinterpret_cast<float*>(vring + r * VE + 16 * 64); };
         auto knent = [&](int r) __attribute__((always_inline)) { return qring + r * QE; };
@@ -1084,7 +1084,12 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                     for (int e = 0; e < 4; ++e) dd[a16_pos(4 * qd + e, c)] = bf16_rne(accd[e]);
                     ytab[64 * dslot(t) + lane] = __builtin_bit_cast(uint2, yb);
                 };
-                if constexpr (NB <= 32) put_dy();
+                if constexpr (UW < NB) {
+                    if (t >= DT)
+#pragma unroll
+                        for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_oready[gg], t - DT + 1);
+                }
+                put_dy();
                 // K_t^T tiles (tile 2 w + hh: its keys by the row's nodes), exact products
                 s16x4 kn[8];
 #pragma unroll
@@ -1104,7 +1109,6 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
                 if (t >= CR)
 #pragma unroll
                     for (int gg = 0; gg < kSolveWaves; ++gg) wait_flag_ge(&s_oready[gg], t - CR + 1);
-                if constexpr (NB > 32) put_dy();
 #pragma unroll
                 for (int cs = 0; cs < 4; ++cs) {
                     *reinterpret_cast<u32x4*>(qent(r) + row_chunk(ln, 4 * cs + lq)) = __builtin_bit_cast(u32x4, o.qt[cs]);
@@ -1303,9 +1307,9 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
         // from this lane's own fp32 stores of it (rows 4q .. 4q+3 of column
         // c0 + n, past L1), rounded as LDS keeps it, and positions past the
         // tree read as zero
-        const int slotv = NB > 32 && lane < NB ? s_uslot[min(lane, NB - 1)] : -1;   // lane t: row t's slot
+        const int slotv = UW < NB && lane < NB ? s_uslot[min(lane, NB - 1)] : -1;   // lane t: row t's slot
         auto uget = [&](int sb, int t) __attribute__((always_inline)) {
-            if constexpr (NB <= 32) {
+            if constexpr (UW == NB) {
                 return __builtin_bit_cast(s16x4, s_u[sb][g][lane]);
             } else {
                 const int us = __builtin_amdgcn_readlane(slotv, sb);
@@ -1423,7 +1427,7 @@ __global__ __launch_bounds__(kLargeThreads, 1) void verify_large_kernel(VerifyAr
             split4(acc, hi, lo);
             const f32x4 uf = mfma16(dt, lo, mfma16(dt, hi, z));
             const s16x4 ut = to_bf16x4(uf);
-            if constexpr (NB <= 32) {
+            if constexpr (UW == NB) {
                 s_u[t][g][lane] = __builtin_bit_cast(uint2, ut);
             } else {
                 const int x = __builtin_amdgcn_readlane(slotv, t);
