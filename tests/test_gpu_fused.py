@@ -205,11 +205,11 @@ def test_fused_other_sizes(N, d, io):
     run_case(f"other N={N} d={d}", steps, io, 1, 2)
 
 
-@pytest.mark.parametrize("N", [200, 256, 300, 512])
+@pytest.mark.parametrize("N", [200, 256, 300, 512, 1000, 1024])
 def test_fused_large_trees(N):
-    """Trees of 129 .. 512 nodes: the commit runs inside the larger-tree
+    """Trees of 129 .. 1024 nodes: the commit runs inside the larger-tree
     launch.  Chains whose every node is accepted (paths of N nodes, several
-    rounds of 256 path nodes at N = 300 and 512), random recursive trees with
+    rounds of 256 path nodes from N = 300), random recursive trees with
     a leaf accepted, a sequence with nothing accepted and one whose previous
     tree is invalid; then the same loop in place."""
     rng = np.random.default_rng(110 + N)
